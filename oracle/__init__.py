@@ -1,0 +1,180 @@
+"""Python access to the fp64 C oracle (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, the smoke check and the benchmark's CPU-baseline leg import this
+package.  The HIP library and its binding never do.
+
+All arrays are numpy float64, C-contiguous, in the oracle's own layouts
+(documented in oracle.h): the cache is [B][n_kv][cap][d_head] with one row per
+absolute position, for both K and V.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("n_heads", ctypes.c_int), ("n_kv_heads", ctypes.c_int),
+                ("d_head", ctypes.c_int), ("d_ff", ctypes.c_int),
+                ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_double)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [(n, _dp) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm",
+                                   "w_gate", "w_up", "w_down")]
+
+
+STAGES = ("n1", "q", "k", "v", "o", "h", "n2", "z")
+
+
+class _Stages(ctypes.Structure):
+    _fields_ = [(n, _dp) for n in STAGES]
+
+
+def lib():
+    """Load liboracle.so, compiling it first if it is not there."""
+    global _lib
+    if _lib is None:
+        path = os.path.join(_HERE, "liboracle.so")
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.orc_rms_norm.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_double, _dp]
+        L.orc_linear.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_int, _dp]
+        L.orc_rope.argtypes = [_dp, ctypes.c_int, ctypes.c_long, ctypes.c_double]
+        L.orc_silu.argtypes = [ctypes.c_double]
+        L.orc_silu.restype = ctypes.c_double
+        L.orc_attend.argtypes = [_dp, _dp, _dp, ctypes.c_long, ctypes.c_int, _dp, _dp]
+        L.orc_block_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_long, ctypes.c_long, _dp,
+                                        ctypes.POINTER(_Weights), _dp, _dp, _dp,
+                                        ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                        ctypes.POINTER(_Stages)]
+        L.orc_block_forward.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"], (a.dtype, a.flags)
+    return a.ctypes.data_as(_dp)
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+# ---- single steps -------------------------------------------------------------------
+
+def rms_norm(v, g, eps: float) -> np.ndarray:
+    v, g = _f64(v), _f64(g)
+    out = np.empty_like(v)
+    lib().orc_rms_norm(_p(v), _p(g), v.shape[-1], eps, _p(out))
+    return out
+
+
+def linear(inp, w) -> np.ndarray:
+    inp, w = _f64(inp), _f64(w)
+    out = np.empty(w.shape[0], dtype=np.float64)
+    lib().orc_linear(_p(inp), _p(w), w.shape[0], w.shape[1], _p(out))
+    return out
+
+
+def rope(v, pos: int, theta: float) -> np.ndarray:
+    out = _f64(v).copy()
+    lib().orc_rope(_p(out), out.shape[-1], int(pos), float(theta))
+    return out
+
+
+def silu(a: float) -> float:
+    return lib().orc_silu(float(a))
+
+
+def attend(q, k_rows, v_rows) -> np.ndarray:
+    q, k_rows, v_rows = _f64(q), _f64(k_rows), _f64(v_rows)
+    n, dh = k_rows.shape
+    scr = np.empty(max(n, 1), dtype=np.float64)
+    out = np.empty(dh, dtype=np.float64)
+    lib().orc_attend(_p(q), _p(k_rows), _p(v_rows), n, dh, _p(scr), _p(out))
+    return out
+
+
+# ---- whole block ----------------------------------------------------------------------
+
+WEIGHT_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+def block_forward(cfg: Dict, x, weights: Dict, start_pos: int, k_cache: np.ndarray,
+                  v_cache: np.ndarray, rows: Optional[Sequence[int]] = None,
+                  stages: bool = False):
+    """Run the block.  cfg keys: d, H, n_kv, d_head, d_ff, theta, eps.
+
+    x: [B][S][d].  k_cache / v_cache: float64 [B][n_kv][cap][d_head], updated in
+    place (rows [start_pos, start_pos+S) written).  Returns (y, stages_dict);
+    with `rows`, only those flat rows of y (and of the stages) are meaningful.
+    """
+    x = _f64(x)
+    B, S, d = x.shape
+    assert d == cfg["d"]
+    cap = k_cache.shape[2]
+    c = _Cfg(cfg["d"], cfg["H"], cfg["n_kv"], cfg["d_head"], cfg["d_ff"],
+             float(cfg["theta"]), float(cfg["eps"]))
+    ws = {n: _f64(weights[n]) for n in WEIGHT_NAMES}
+    wstruct = _Weights(*[_p(ws[n]) for n in WEIGHT_NAMES])
+    y = np.zeros((B, S, d), dtype=np.float64)
+    M = B * S
+    widths = {"n1": d, "q": cfg["H"] * cfg["d_head"], "k": cfg["n_kv"] * cfg["d_head"],
+              "v": cfg["n_kv"] * cfg["d_head"], "o": cfg["H"] * cfg["d_head"], "h": d,
+              "n2": d, "z": cfg["d_ff"]}
+    st_arrays = {}
+    st_ptr = None
+    if stages:
+        st_arrays = {n: np.zeros((M, widths[n]), dtype=np.float64) for n in STAGES}
+        st_ptr = ctypes.pointer(_Stages(*[_p(st_arrays[n]) for n in STAGES]))
+    if rows is not None:
+        rarr = (ctypes.c_int * len(rows))(*[int(r) for r in rows])
+        nrows = len(rows)
+    else:
+        rarr, nrows = None, 0
+    rc = lib().orc_block_forward(ctypes.byref(c), B, S, int(start_pos), int(cap), _p(x),
+                                 ctypes.byref(wstruct), _p(k_cache), _p(v_cache), _p(y),
+                                 rarr, nrows, st_ptr)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return y, st_arrays
+
+
+def cfg_of(w) -> Dict:
+    """Oracle config dict from a workloads.BlockWorkload."""
+    return {"d": w.d, "H": w.H, "n_kv": w.n_kv, "d_head": w.d_head, "d_ff": w.d_ff,
+            "theta": w.theta, "eps": w.eps}
+
+
+def empty_cache(w, cap: Optional[int] = None):
+    cap = cap or w.capacity
+    shape = (w.B, w.n_kv, cap, w.d_head)
+    return np.zeros(shape, dtype=np.float64), np.zeros(shape, dtype=np.float64)
+
+
+def run_workload(w, tensors: Dict, rows: Optional[Sequence[int]] = None, stages: bool = False):
+    """Oracle forward of a generated workload: fills the pre-filled prefix, runs
+    the block and returns (y, k_cache, v_cache, stages)."""
+    kc, vc = empty_cache(w)
+    if w.start_pos > 0:
+        kc[:, :, : w.start_pos, :] = _f64(tensors["k_prefix"])
+        vc[:, :, : w.start_pos, :] = _f64(tensors["v_prefix"])
+    y, st = block_forward(cfg_of(w), tensors["x"], tensors, w.start_pos, kc, vc, rows=rows,
+                          stages=stages)
+    return y, kc, vc, st

@@ -1,0 +1,62 @@
+/*
+ * fp64 CPU oracle for the forward pass of one Llama pre-norm decoder block.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it.  The HIP library neither links
+ * nor calls it, and the two share no source, header, table or helper.
+ *
+ * Every value is double precision; inputs are the exact (already quantised)
+ * workload values widened to double.  All arrays are host memory, row-major.
+ *
+ * Layouts used by this oracle (its own choice, independent of the library):
+ *   x, y            [B][S][d]
+ *   wq              [H*d_head][d]      wk, wv [n_kv*d_head][d]
+ *   wo              [d][H*d_head]
+ *   w_gate, w_up    [d_ff][d]          w_down [d][d_ff]
+ *   attn_norm, ffn_norm [d]
+ *   k_cache, v_cache [B][n_kv][cap][d_head]  (one row per absolute position)
+ */
+#ifndef LLAMA_BLOCK_ORACLE_H
+#define LLAMA_BLOCK_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int d, n_heads, n_kv_heads, d_head, d_ff;
+    double rope_theta, norm_eps;
+} orc_cfg;
+
+typedef struct {
+    const double *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} orc_weights;
+
+/* Optional per-row intermediates (any pointer may be NULL), all [B*S][...]:
+ * n1 [d], q [H*d_head] (after RoPE), k, v [n_kv*d_head] (k after RoPE),
+ * o [H*d_head] (concatenated heads), h [d], n2 [d], z [d_ff]. */
+typedef struct {
+    double *n1, *q, *k, *v, *o, *h, *n2, *z;
+} orc_stages;
+
+/* Single steps, exposed so tests can pin each one on its own. */
+void orc_rms_norm(const double* v, const double* g, int d, double eps, double* out);
+void orc_linear(const double* in, const double* w, int n_out, int n_in, double* out);
+void orc_rope(double* v, int d_head, long pos, double theta);
+double orc_silu(double a);
+void orc_attend(const double* q, const double* k_rows, const double* v_rows, long n_keys,
+                int d_head, double* scratch, double* out);
+
+/* Whole block.  Reads cache rows [0, start_pos) of every sequence, writes rows
+ * [start_pos, start_pos+S).  rows/n_rows (optional): compute y (and stages)
+ * only for these flat row indices b*S+s; the cache is still written for every
+ * position up to the last requested one of each sequence.  rows == NULL
+ * computes every row.  Returns 0, or a negative code for an invalid argument. */
+int orc_block_forward(const orc_cfg* cfg, int B, int S, long start_pos, long cap,
+                      const double* x, const orc_weights* w, double* k_cache, double* v_cache,
+                      double* y, const int* rows, int n_rows, orc_stages* stages);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

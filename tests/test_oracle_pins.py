@@ -1,0 +1,446 @@
+"""Pins for the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: figures the
+pages print (tests/golden/page_figures.json), closed forms, invariants, special
+cases that reduce to a library routine, or brute force on tiny inputs.  The
+planted-mistake check at the end shows that a plausible slip in the oracle's
+arithmetic is caught.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+
+
+def g(key):
+    return GOLD[key]["value"]
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- RMSNorm ----
+
+def test_rmsnorm_unit_gain_closed_form():
+    """Unit gain: rms(out) = sqrt(ms / (ms + eps)); with eps = 0 exactly 1."""
+    r = rng(1)
+    for d, scale in [(64, 1.0), (576, 3.0), (4096, 0.01)]:
+        v = r.normal(0, scale, d)
+        ms = np.mean(v * v)
+        for eps in (1e-5, 1e-6, 0.0):
+            out = oracle.rms_norm(v, np.ones(d), eps)
+            got = math.sqrt(np.mean(out * out))
+            want = math.sqrt(ms / (ms + eps))
+            assert abs(got - want) <= 1e-14 * want, (d, eps, got, want)
+            # no centring: the output is a positive multiple of the input
+            assert np.all(np.sign(out) == np.sign(v))
+
+
+def test_rmsnorm_matches_torch_rms_norm():
+    """Library special case: torch's F.rms_norm (named on the page "From GPT-2 to
+    Llama", The norm stops centring) in fp64, with a learned gain."""
+    r = rng(2)
+    for d in (64, 576, 1000):
+        v = r.normal(0, 1.7, (5, d))
+        gain = r.normal(1, 0.1, d)
+        want = F.rms_norm(torch.from_numpy(v), (d,), torch.from_numpy(gain), eps=1e-5).numpy()
+        for i in range(5):
+            got = oracle.rms_norm(v[i], gain, 1e-5)
+            np.testing.assert_allclose(got, want[i], rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------- projections ----
+
+def test_linear_matches_numpy_matmul():
+    r = rng(3)
+    for n_out, n_in in [(128, 64), (7, 176), (960, 576)]:
+        w = r.normal(0, 0.02, (n_out, n_in))
+        v = r.normal(0, 1, n_in)
+        np.testing.assert_allclose(oracle.linear(v, w), w @ v, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------- RoPE ----
+
+def _score(q, k, m, n, theta):
+    return float(oracle.rope(q, m, theta) @ oracle.rope(k, n, theta))
+
+
+def test_rope_relative_position_invariance():
+    """"From GPT-2 to Llama", Positions become a rotation: the rotated score
+    depends only on m - n (-13.4724 at (10,3) vs -13.4723 at (1010,1003)), and
+    moving one step closer changes it (-10.786 at (10,4))."""
+    figs = g("rope_score_invariance")
+    assert abs(figs["m10_n3"] - figs["m1010_n1003"]) < 2e-4
+    assert abs(figs["m10_n3"] - figs["m10_n4"]) > 1.0
+    r = rng(4)
+    for theta, dh in [(1e5, 64), (5e5, 128), (1e4, 16)]:
+        for trial in range(3):
+            q, k = r.normal(0, 1, dh), r.normal(0, 1, dh)
+            base = _score(q, k, 10, 3, theta)
+            for delta in (1, 1000, 5000, 100000):
+                assert abs(_score(q, k, 10 + delta, 3 + delta, theta) - base) <= 1e-11 * (1 + abs(base))
+            # one step closer is a different score
+            assert abs(_score(q, k, 10, 4, theta) - base) > 1e-6
+
+
+def _omegas(dh, theta):
+    """Read each pair's angular speed back from the oracle: the turn of a unit
+    vector in pair i over one position."""
+    om = []
+    for i in range(dh // 2):
+        e = np.zeros(dh)
+        e[2 * i] = 1.0
+        r = oracle.rope(e, 1, theta)
+        om.append(math.atan2(r[2 * i + 1], r[2 * i]))
+    return np.array(om)
+
+
+def test_rope_pair_periods_match_page():
+    """"From GPT-2 to Llama", Positions become a rotation: with base 100 000 and
+    heads of 64, the fastest pair turns once every 6.3 positions and the slowest
+    once every ~438 000."""
+    om = _omegas(64, 1e5)
+    periods = 2 * math.pi / om
+    assert round(periods[0], 1) == g("smollm2_rope_fastest_period_positions")
+    assert abs(periods[-1] - g("smollm2_rope_slowest_period_positions")) / 438000 < 0.005
+    # speeds fall monotonically from the first pair to the last (geometric schedule)
+    assert np.all(np.diff(periods) > 0)
+    ratios = om[1:] / om[:-1]
+    np.testing.assert_allclose(ratios, ratios[0], rtol=1e-12)
+
+
+def test_rope_is_complex_rotation_of_adjacent_pairs():
+    """"Mini Llama 2 Implementation", Rotary positional embeddings: adjacent
+    dimensions (2i, 2i+1) are the real and imaginary parts of one complex number,
+    turned by e^(i m w_i).  Also: position 0 is the identity and each pair keeps
+    its length."""
+    dh, theta = 128, 5e5
+    om = _omegas(dh, theta)
+    r = rng(5)
+    v = r.normal(0, 1, dh)
+    np.testing.assert_array_equal(oracle.rope(v, 0, theta), v)
+    for m in (1, 7, 2047, 8191):
+        got = oracle.rope(v, m, theta)
+        z = (v[0::2] + 1j * v[1::2]) * np.exp(1j * m * om)
+        np.testing.assert_allclose(got[0::2], z.real, rtol=0, atol=1e-9)
+        np.testing.assert_allclose(got[1::2], z.imag, rtol=0, atol=1e-9)
+        np.testing.assert_allclose(np.hypot(got[0::2], got[1::2]), np.hypot(v[0::2], v[1::2]),
+                                   rtol=1e-13)
+
+
+# --------------------------------------------------------------------- SiLU ----
+
+def test_silu_special_values_and_library():
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12
+    assert abs(oracle.silu(-40.0)) < 1e-15
+    for a in np.linspace(-12, 12, 97):
+        assert abs(oracle.silu(a) - a * scipy.special.expit(a)) <= 1e-15 * (1 + abs(a))
+    assert abs(oracle.silu(1.0) - F.silu(torch.tensor(1.0, dtype=torch.float64)).item()) < 1e-16
+
+
+# ---------------------------------------------------------------- attention ----
+
+def test_attention_uniform_cases():
+    """Equal keys (or a zero query) give equal weights: the output is the mean
+    of the value rows."""
+    r = rng(6)
+    dh = 16
+    v = r.normal(0, 1, (9, dh))
+    k = np.tile(r.normal(0, 1, dh), (9, 1))
+    q = r.normal(0, 1, dh)
+    np.testing.assert_allclose(oracle.attend(q, k, v), v.mean(0), rtol=1e-13, atol=1e-15)
+    k2 = r.normal(0, 1, (9, dh))
+    np.testing.assert_allclose(oracle.attend(np.zeros(dh), k2, v), v.mean(0), rtol=1e-13,
+                               atol=1e-15)
+
+
+def test_attention_two_key_closed_form_pins_scale():
+    """Two keys whose scores differ by s/sqrt(dh): the first weight is
+    sigmoid(s / sqrt(dh)) -- pins the 1/sqrt(d_head) scale of the equation in
+    "The Evolving Transformer 04 LLaMA", 05 GQA."""
+    for dh in (16, 64, 128):
+        s = 3.0
+        q = np.zeros(dh)
+        q[0] = s
+        k = np.zeros((2, dh))
+        k[0, 0] = 1.0
+        v = np.zeros((2, dh))
+        v[0, 1] = 1.0
+        v[1, 2] = 1.0
+        out = oracle.attend(q, k, v)
+        p = scipy.special.expit(s / math.sqrt(dh))
+        assert abs(out[1] - p) < 1e-15 and abs(out[2] - (1 - p)) < 1e-15
+
+
+def test_attention_matches_torch_sdpa():
+    """Library special case: torch's scaled_dot_product_attention in fp64."""
+    r = rng(7)
+    for n, dh in [(1, 16), (37, 64), (300, 128)]:
+        q = r.normal(0, 1.5, dh)
+        k = r.normal(0, 1.5, (n, dh))
+        v = r.normal(0, 1, (n, dh))
+        want = F.scaled_dot_product_attention(torch.from_numpy(q)[None, None, None],
+                                              torch.from_numpy(k)[None, None],
+                                              torch.from_numpy(v)[None, None])[0, 0, 0].numpy()
+        np.testing.assert_allclose(oracle.attend(q, k, v), want, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ the block ----
+
+def _small(name="tiny_f32", **kw):
+    return workloads.with_overrides(workloads.get(name), **kw)
+
+
+def _library_block(w, t, start_pos=0, k_prefix=None, v_prefix=None):
+    """The block composed from torch library routines in fp64: F.rms_norm,
+    F.linear, complex multiplication for the rotation (speeds read back from
+    the oracle's own single-position rotation, pinned separately above), and
+    F.scaled_dot_product_attention with grouped heads (enable_gqa repeats each
+    KV head over consecutive query heads)."""
+    d, H, G, dh = w.d, w.H, w.n_kv, w.d_head
+    T = {k: v.double() for k, v in t.items()}
+    x = T["x"]
+    B, S, _ = x.shape
+    n1 = F.rms_norm(x, (d,), T["attn_norm"], eps=w.eps)
+    q = F.linear(n1, T["wq"]).view(B, S, H, dh)
+    k = F.linear(n1, T["wk"]).view(B, S, G, dh)
+    v = F.linear(n1, T["wv"]).view(B, S, G, dh)
+    om = torch.from_numpy(_omegas(dh, w.theta))
+    pos = torch.arange(start_pos, start_pos + S, dtype=torch.float64)
+    rot = torch.polar(torch.ones(S, dh // 2, dtype=torch.float64), pos[:, None] * om[None, :])
+
+    def turn(a):
+        c = torch.view_as_complex(a.reshape(*a.shape[:-1], dh // 2, 2).contiguous())
+        return torch.view_as_real(c * rot[None, :, None, :]).reshape(a.shape)
+
+    q, k = turn(q), turn(k)
+    q, k, v = q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2)
+    if start_pos > 0:
+        k = torch.cat([k_prefix.double(), k], dim=2)
+        v = torch.cat([v_prefix.double(), v], dim=2)
+    Tn = start_pos + S
+    mask = torch.arange(Tn)[None, :] <= (start_pos + torch.arange(S))[:, None]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, enable_gqa=True)
+    o = o.transpose(1, 2).reshape(B, S, H * dh)
+    h = x + F.linear(o, T["wo"])
+    n2 = F.rms_norm(h, (d,), T["ffn_norm"], eps=w.eps)
+    y = h + F.linear(F.silu(F.linear(n2, T["w_gate"])) * F.linear(n2, T["w_up"]), T["w_down"])
+    return y.numpy()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", {}),
+    ("tiny_f32", {"B": 3, "S": 9, "seed": 5}),
+    ("smollm2_135m_prefill", {"B": 2, "S": 33, "dtype": "f32"}),
+])
+def test_block_matches_library_composition(name, kw):
+    w = _small(name, **kw)
+    t = workloads.generate(w)
+    y, _, _, _ = oracle.run_workload(w, t)
+    want = _library_block(w, t)
+    err = np.abs(y - want).max() / np.sqrt((want ** 2).mean())
+    assert err < 1e-12, err
+
+
+def test_block_with_cache_offset_matches_library_composition():
+    """Chunked call at start_pos > 0 reads the cached prefix ("Full Llama 3
+    transformer block", How it works: start_pos and the cache offset)."""
+    w = _small("tiny_f32", B=2, S=5, start_pos=11, seed=3)
+    t = workloads.generate(w)
+    y, _, _, _ = oracle.run_workload(w, t)
+    want = _library_block(w, t, 11, t["k_prefix"], t["v_prefix"])
+    err = np.abs(y - want).max() / np.sqrt((want ** 2).mean())
+    assert err < 1e-12, err
+
+
+def test_gqa_with_duplicated_heads_equals_mha_bitwise():
+    """"From GPT-2 to Llama", Keys and values get shared: a copy with full
+    key/value heads, each a duplicate of its group's, gives identical outputs."""
+    w = _small("tiny_f32", B=2, S=7, seed=9)
+    t = workloads.generate(w)
+    y_gqa, _, _, _ = oracle.run_workload(w, t)
+    rep = w.H // w.n_kv
+    t2 = dict(t)
+    for n in ("wk", "wv"):
+        heads = t[n].view(w.n_kv, w.d_head, w.d)
+        t2[n] = heads.repeat_interleave(rep, dim=0).reshape(w.H * w.d_head, w.d)
+    w2 = workloads.with_overrides(w, n_kv=w.H)
+    y_mha, _, _, _ = oracle.run_workload(w2, t2)
+    np.testing.assert_array_equal(y_gqa, y_mha)
+    # tiling the shared heads instead (the page's silent port mistake) differs
+    t3 = dict(t)
+    for n in ("wk", "wv"):
+        heads = t[n].view(w.n_kv, w.d_head, w.d)
+        t3[n] = heads.repeat(rep, 1, 1).reshape(w.H * w.d_head, w.d)
+    y_tiled, _, _, _ = oracle.run_workload(w2, t3)
+    assert np.abs(y_tiled - y_gqa).max() > 1e-6
+
+
+def test_decode_token_by_token_equals_prefill():
+    """"Full Llama 3 transformer block", How it works: incremental decoding with
+    the cache offset gives the rows of one full causal prefill."""
+    w = _small("tiny_f32", B=2, S=12, seed=11)
+    t = workloads.generate(w)
+    y_full, kc_full, vc_full, _ = oracle.run_workload(w, t)
+    cfg = oracle.cfg_of(w)
+    kc, vc = oracle.empty_cache(w)
+    x = t["x"].double().numpy()
+    for s in range(w.S):
+        y_s, _ = oracle.block_forward(cfg, x[:, s:s + 1, :].copy(), t, s, kc, vc)
+        np.testing.assert_allclose(y_s[:, 0, :], y_full[:, s, :], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(kc, kc_full, rtol=0, atol=0)
+    np.testing.assert_allclose(vc, vc_full, rtol=0, atol=0)
+
+
+def test_residual_wiring_zero_weights():
+    """"Full Llama 3 transformer block", How it works: h = x + Attn(...),
+    y = h + FFN(...).  With Wo = 0 and W_down = 0, y = x exactly; with
+    W_down = 0 alone, y = h."""
+    w = _small("tiny_f32", B=1, S=6, seed=2)
+    t = workloads.generate(w)
+    t0 = dict(t, wo=torch.zeros_like(t["wo"]), w_down=torch.zeros_like(t["w_down"]))
+    y, _, _, _ = oracle.run_workload(w, t0)
+    np.testing.assert_array_equal(y, t["x"].double().numpy())
+    t1 = dict(t, w_down=torch.zeros_like(t["w_down"]))
+    y1, _, _, st = oracle.run_workload(w, t1, stages=True)
+    np.testing.assert_array_equal(y1.reshape(-1, w.d), st["h"])
+
+
+def test_kv_cache_values_written_per_token():
+    """"Llama 4 From Scratch", Worked example: 2 x 8 x 128 = 2048 values per
+    token per layer for the 8B heads (8192 with full heads); the call writes
+    exactly those cache entries and nothing else."""
+    for H, G, want_key in [(32, 8, "kv_values_per_token_per_layer_llama3_8b"),
+                           (32, 32, "kv_values_per_token_per_layer_llama3_8b_full_heads")]:
+        w = workloads.BlockWorkload("kvcount", "f32", B=1, S=3, start_pos=5, d=64, H=H, n_kv=G,
+                                    d_head=128, d_ff=32, theta=5e5, eps=1e-5, w_std=0.02,
+                                    max_seq=12)
+        t = workloads.generate(w)
+        kc = np.full((1, G, 12, 128), np.nan)
+        vc = np.full((1, G, 12, 128), np.nan)
+        kc[:, :, :5] = t["k_prefix"].double().numpy()
+        vc[:, :, :5] = t["v_prefix"].double().numpy()
+        oracle.block_forward(oracle.cfg_of(w), t["x"], t, 5, kc, vc)
+        written = int(np.sum(~np.isnan(kc[:, :, 5:])) + np.sum(~np.isnan(vc[:, :, 5:])))
+        assert written == w.S * g(want_key)
+        assert np.all(np.isnan(kc[:, :, 8:])) and np.all(np.isnan(vc[:, :, 8:]))
+    # all-layer totals quoted on the pages
+    assert 32 * g("kv_values_per_token_per_layer_llama3_8b") == g("kv_values_per_token_llama3_8b_32_layers")
+    assert 2 * g("kv_values_per_token_llama3_8b_32_layers") == g("kv_bytes_per_token_llama3_8b_16bit")
+    assert 30 * 2 * 3 * 64 == g("kv_values_per_token_smollm2_30_layers")
+    assert 30 * 2 * 9 * 64 == g("kv_values_per_token_smollm2_full_heads")
+    assert 12 * 2 * 12 * 64 == g("kv_values_per_token_gpt2_small")
+    gb = g("kv_bytes_per_token_llama3_8b_16bit") * 131072 / 1e9
+    assert round(gb, 1) == g("llama31_8b_kv_gb_at_131072")
+    assert round(4 * gb, 1) == g("llama31_8b_kv_gb_full_heads_at_131072")
+
+
+def test_workload_shapes_match_pages():
+    w8 = workloads.get("llama3_8b_prefill")
+    s8 = g("llama3_8b_shape")
+    assert (w8.d, w8.H, w8.n_kv, w8.d_head, w8.d_ff, w8.eps) == (
+        s8["d"], s8["H"], s8["n_kv"], s8["d_head"], s8["d_ff"], s8["eps"])
+    assert w8.theta == g("llama3_rope_base")
+    pc = workloads.param_count(w8)
+    assert round(pc["total_linear"] / 1e6) == g("llama3_8b_block_params_millions")
+    assert round(pc["ffn"] / 1e6) == g("llama3_8b_block_ffn_params_millions")
+    assert round(100 * pc["ffn"] / pc["total_linear"]) == g("llama3_8b_ffn_share_percent")
+    mha = workloads.param_count(workloads.with_overrides(w8, n_kv=32))
+    assert round(100 * mha["ffn"] / mha["total_linear"]) == g("llama3_8b_ffn_share_full_heads_percent")
+    w70 = workloads.get("llama3_70b_prefill")
+    wd = g("llama3_widths")
+    assert w70.d == wd["d"][1] and w70.d_ff == wd["ffn"][1]
+    assert w70.d_head == wd["head_dim"] and w70.n_kv == wd["n_kv"]
+    ws = workloads.get("smollm2_135m_prefill")
+    ss = g("smollm2_shape")
+    assert (ws.d, ws.H, ws.n_kv, ws.d_head, ws.theta) == (ss["d"], ss["H"], ss["n_kv"], ss["d_head"],
+                                                           ss["rope_base"])
+    assert ws.d_ff == g("smollm2_ffn_width")
+    ps = workloads.param_count(ws)
+    assert round(100 * ps["ffn"] / ps["total_linear"]) == g("smollm2_ffn_share_percent")
+    # full-head copy of all 30 layers adds 30 * 2 * 576 * 384 weights
+    lo, hi = g("smollm2_full_head_copy_params_millions")
+    full = workloads.param_count(workloads.with_overrides(ws, n_kv=9))
+    assert abs(30 * (full["attn"] - ps["attn"]) / 1e6 - (hi - lo)) < 0.05
+    # tiny block: d_ff is 8/3 * 64 rounded up to a multiple of 16
+    wt = workloads.get("tiny_f32")
+    assert wt.d_ff == 16 * math.ceil(8 * wt.d / 3 / 16)
+
+
+# ------------------------------------------------- planted mistakes are caught ----
+
+MUTANTS = [
+    # (what is planted, text in oracle.c, replacement, pins that must fail)
+    ("RoPE exponent -i/dh", "-2.0 * (double)i / (double)d_head", "-1.0 * (double)i / (double)d_head",
+     ["test_rope_pair_periods_match_page"]),
+    ("RoPE rotation sign", "v[2 * i + 1] = u * s + w * c;", "v[2 * i + 1] = -u * s + w * c;",
+     ["test_rope_is_complex_rotation_of_adjacent_pairs", "test_rope_relative_position_invariance"]),
+    ("attention scale 1/dh", "1.0 / sqrt((double)d_head)", "1.0 / (double)d_head",
+     ["test_attention_two_key_closed_form_pins_scale", "test_attention_matches_torch_sdpa"]),
+    ("causal bound t < m", "const long n_keys = pos + 1;", "const long n_keys = pos > 0 ? pos : 1;",
+     ["test_block_matches_library_composition"]),
+    ("GQA tiling h % n_kv", "const int g = hh / n_rep;", "const int g = hh % G;",
+     ["test_block_matches_library_composition"]),
+    ("RMSNorm sum not mean", "sqrt(ss / (double)d + eps)", "sqrt(ss + eps)",
+     ["test_rmsnorm_unit_gain_closed_form", "test_rmsnorm_matches_torch_rms_norm"]),
+    ("missing attention residual", "h[i] = xr[i] + h[i];", "h[i] = h[i];",
+     ["test_residual_wiring_zero_weights", "test_block_matches_library_composition"]),
+    ("sigmoid instead of SiLU", "return a / (1.0 + exp(-a));", "return 1.0 / (1.0 + exp(-a));",
+     ["test_silu_special_values_and_library", "test_block_matches_library_composition"]),
+    ("transposed projection", "const double* row = w + (size_t)j * (size_t)n_in;",
+     "const double* row = w + (size_t)j;",
+     ["test_linear_matches_numpy_matmul"]),
+]
+
+
+def _build_mutant(tmp_path, old, new):
+    import ctypes
+    import subprocess
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    assert src.count(old) == 1, old
+    d = tmp_path / "mut"
+    d.mkdir(exist_ok=True)
+    (d / "oracle.c").write_text(src.replace(old, new))
+    (d / "oracle.h").write_text(open(os.path.join(os.path.dirname(oracle.__file__), "oracle.h")).read())
+    so = d / "libmut.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", str(so), str(d / "oracle.c"), "-lm"], check=True)
+    return so
+
+
+@pytest.mark.parametrize("label,old,new,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, label, old, new, pins):
+    so = _build_mutant(tmp_path, old, new)
+    saved = oracle._lib
+    try:
+        oracle._lib = None
+        real = oracle.lib()  # argtypes set on the real library object
+        import ctypes
+        mut = ctypes.CDLL(str(so))
+        for name in ("orc_rms_norm", "orc_linear", "orc_rope", "orc_silu", "orc_attend",
+                     "orc_block_forward"):
+            getattr(mut, name).argtypes = getattr(real, name).argtypes
+            getattr(mut, name).restype = getattr(real, name).restype
+        oracle._lib = mut
+        for pin in pins:
+            fn = globals()[pin]
+            args = {"test_block_matches_library_composition": ("tiny_f32", {"B": 3, "S": 9, "seed": 5})}
+            with pytest.raises(AssertionError):
+                if pin in args:
+                    fn(*args[pin])
+                else:
+                    fn()
+    finally:
+        oracle._lib = saved
