@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the Llama-block library on one MI355X.
+
+One step = one llama_block_forward over one batch of synthetic input (every
+stage of the block: RMSNorm, q/k/v + RoPE + cache append, causal GQA
+attention, o projection + residual, RMSNorm, gate/up + SiLU*up, down +
+residual).
+
+Default run (N = 1):
+  * prefill: Llama-3-8B-width block, B=2 x S=2048 from position 0 -> the
+    headline `value` in tokens/s;
+  * decode:  Llama-3-8B-width block, 32 sequences x 1 new token at position
+    8191 over 8191 cached positions -> reported under "decode" (us/step);
+  * cpu_baseline: the fp64 oracle on the host cores over a bounded sample of
+    the prefill workload (the first tokens of one sequence).
+Per-stage GPU times come from the library's HIP-event profiler recorded on the
+forward's stream during the timed steps; the dominant stage gives `roofline`.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 matrix peak
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+METRIC = "block prefill tokens/s + decode µs/step; % bf16 MFMA peak / % HBM BW"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_work(w):
+    """Algorithmic work per forward, per profiled stage: flops (matrix products,
+    causal attention over visible (query, key) pairs only) and HBM bytes (each
+    operand read once, each result written once)."""
+    M, d, dh, H, G, dff = w.M, w.d, w.d_head, w.H, w.n_kv, w.d_ff
+    qd, kvd = H * dh, G * dh
+    e = 2  # bytes per bf16/fp16 element
+    vis = sum(w.start_pos + s + 1 for s in range(w.S)) * w.B       # visible pairs per head
+    kv_read = w.B * G * (w.start_pos + w.S) * dh * 2 * e            # K and V, every visible row
+    return {
+        "rmsnorm_1": {"flops": 0, "bytes": M * d * (e + e)},
+        "qkv_rope_append": {"flops": 2 * M * (qd + 2 * kvd) * d,
+                            "bytes": (qd + 2 * kvd) * d * e + M * d * e + M * (qd + 4 * kvd) * e},
+        "attention": {"flops": 4 * dh * vis * H,
+                      "bytes": kv_read + 2 * M * qd * e},
+        "o_proj_residual": {"flops": 2 * M * d * qd,
+                            "bytes": d * qd * e + M * qd * e + M * d * (e + 4)},
+        "rmsnorm_2": {"flops": 0, "bytes": M * d * (4 + e)},
+        "gate_up_swiglu": {"flops": 2 * M * 2 * dff * d,
+                           "bytes": 2 * dff * d * e + M * d * e + M * dff * e},
+        "down_residual": {"flops": 2 * M * d * dff,
+                          "bytes": d * dff * e + M * dff * e + M * d * (4 + e)},
+    }
+
+
+def run_gpu(w, steps, warmup):
+    import torch
+
+    import decoder_only_transformer_amd as lbmod
+    import workloads
+
+    t = workloads.generate(w)
+    cap = (w.capacity + 7) // 8 * 8
+    cfg = lbmod.make_config(w.d, w.H, w.n_kv, w.d_head, w.d_ff, w.M, cap, w.theta, w.eps, w.dtype)
+    blk = lbmod.LlamaBlock(cfg, {n: t[n].to("cuda") for n in lbmod.WEIGHT_NAMES})
+    k, v = lbmod.new_kv_cache(w.B, w.n_kv, cap, w.d_head, w.torch_dtype)
+    if w.start_pos > 0:
+        k[:, :, : w.start_pos, :] = t["k_prefix"].to("cuda")
+        v[:, :, :, : w.start_pos] = t["v_prefix"].to("cuda").transpose(-1, -2)
+    x = t["x"].to("cuda")
+    out = torch.empty_like(x)
+    del t
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        blk.forward(x, w.start_pos, (k, v), out)
+    torch.cuda.synchronize()
+    lbmod.llama_block_profile(blk.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        blk.forward(x, w.start_pos, (k, v), out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms, calls = lbmod.llama_block_profile_read(blk.handle)
+    lbmod.llama_block_profile(blk.handle, False)
+    blk.close()
+    del k, v, x, out
+    torch.cuda.empty_cache()
+    ms = (t1 - t0) * 1e3 / steps
+    avg = {n: stage_ms[n] / max(calls, 1) for n in stage_ms}
+    return ms, avg, stream
+
+
+def roofline(w, avg_ms, bound):
+    work = stage_work(w)
+    stages = {}
+    for n, ms in avg_ms.items():
+        s = ms * 1e-3
+        stages[n] = {"ms": round(ms, 4),
+                     "tflops": round(work[n]["flops"] / s / 1e12, 2) if s > 0 else None,
+                     "gbs": round(work[n]["bytes"] / s / 1e9, 1) if s > 0 else None}
+    dom = max(avg_ms, key=lambda n: avg_ms[n])
+    s = avg_ms[dom] * 1e-3
+    if bound == "mfma":
+        a = work[dom]["flops"] / s / 1e12
+        r = {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(a / MFMA_PEAK_TFLOPS, 4), "traffic": None, "kernel": dom}
+    else:
+        a = work[dom]["bytes"] / s / 1e9
+        r = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+    return r, stages
+
+
+def cpu_baseline(w, tokens):
+    """The fp64 oracle, as it stands, on the host: the first `tokens` tokens of
+    one sequence of workload w (full block weights)."""
+    import workloads
+    import oracle
+    ws = workloads.with_overrides(w, B=1, S=tokens)
+    t = workloads.generate(ws)
+    cfg = oracle.cfg_of(ws)
+    xs = t["x"]
+    wts = {n: oracle._f64(t[n]) for n in oracle.WEIGHT_NAMES}
+    kc, vc = oracle.empty_cache(ws)
+    t0 = time.perf_counter()
+    oracle.block_forward(cfg, xs, wts, 0, kc, vc)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{w.name} weights, first {tokens} tokens of one sequence (B=1, S={tokens}), "
+                      f"fp64 naive loops"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_prefill")
+    ap.add_argument("--decode-workload", default="llama3_8b_decode")
+    ap.add_argument("--decode-steps", type=int, default=0, help="default: 5 x --steps")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the block's hot path is single-GPU "
+              "(no collectives); multi-GPU runs are not supported.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    w = workloads.get(args.workload)
+    log(f"[bench] prefill {w.name}: warmup {args.warmup}, steps {args.steps}")
+    ms, avg, _ = run_gpu(w, args.steps, args.warmup)
+    roof, stages = roofline(w, avg, "mfma")
+    total_flops = sum(v["flops"] for v in stage_work(w).values())
+    result = {
+        "metric": METRIC,
+        "value": round(w.M / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "io_dtype": w.dtype,
+        "accumulate": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "start_pos": w.start_pos, "d": w.d,
+                   "H": w.H, "n_kv": w.n_kv, "d_head": w.d_head, "d_ff": w.d_ff,
+                   "theta": w.theta, "parallelism": "single-gpu"},
+        "block_tflops": round(total_flops / (ms * 1e-3) / 1e12, 2),
+        "block_mfma_frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+        "roofline": roof,
+        "stages": stages,
+    }
+    log(f"[bench] prefill {ms:.3f} ms/step, {result['value']:.0f} tokens/s")
+
+    if not args.no_decode:
+        wd = workloads.get(args.decode_workload)
+        dsteps = args.decode_steps or 5 * args.steps
+        log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {dsteps}")
+        dms, davg, _ = run_gpu(wd, dsteps, args.warmup)
+        droof, dstages = roofline(wd, davg, "hbm")
+        total_bytes = sum(v["bytes"] for v in stage_work(wd).values())
+        result["decode"] = {
+            "workload": wd.name, "B": wd.B, "start_pos": wd.start_pos, "steps": dsteps,
+            "us_per_step": round(dms * 1e3, 2),
+            "tokens_per_s": round(wd.M / (dms * 1e-3), 1),
+            "block_gbs": round(total_bytes / (dms * 1e-3) / 1e9, 1),
+            "block_hbm_frac": round(total_bytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": droof, "stages": dstages,
+        }
+        log(f"[bench] decode {dms * 1e3:.1f} us/step")
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        log(f"[bench] cpu baseline {result['cpu_baseline']['seconds']} s")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

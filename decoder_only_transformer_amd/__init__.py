@@ -1,0 +1,228 @@
+"""Python binding of libllama_block.so (the gfx950 Llama-block library).
+
+Argument marshalling only: every step of the block runs in the library's HIP
+kernels.  The names match the C ABI in include/llama_block.h.  Tensors are
+torch tensors on the GPU; their data pointers and the current HIP stream are
+handed to the library.  There is no fallback: if the library is missing, the
+import of the entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libllama_block.so")
+
+LB_F32, LB_BF16 = 0, 1
+LB_OPERANDS_AUTO, LB_OPERANDS_F16, LB_OPERANDS_BF16 = 0, 1, 2
+LB_OK, LB_ERR_INVALID_ARG, LB_ERR_UNSUPPORTED, LB_ERR_OOM, LB_ERR_HIP = 0, 1, 2, 3, 4
+STAGES = {"n1": 0, "q": 1, "o": 2, "h": 3, "n2": 4, "z": 5}
+ELEM_NAMES = {0: "f32", 1: "bf16", 2: "f16"}
+
+EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_destroy",
+           "llama_block_status_string", "llama_block_last_error", "llama_block_stage_info",
+           "llama_block_copy_stage", "llama_block_profile", "llama_block_profile_read")
+STAGE_NAMES = ("rmsnorm_1", "qkv_rope_append", "attention", "o_proj_residual", "rmsnorm_2",
+               "gate_up_swiglu", "down_residual")
+
+
+class LbConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+                ("norm_eps", ctypes.c_double), ("dtype", ctypes.c_int),
+                ("operands", ctypes.c_int)]
+
+
+class LbWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm",
+                                               "w_gate", "w_up", "w_down")]
+
+
+class LbKVCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("batch", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32)]
+
+
+WEIGHT_NAMES = [f[0] for f in LbWeights._fields_]
+
+
+class LlamaBlockError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.llama_block_init.argtypes = [ctypes.POINTER(LbConfig), ctypes.POINTER(LbWeights),
+                                       ctypes.POINTER(vp)]
+        L.llama_block_init.restype = ctypes.c_int
+        L.llama_block_forward.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(LbKVCache), vp, vp]
+        L.llama_block_forward.restype = ctypes.c_int
+        L.llama_block_destroy.argtypes = [vp]
+        L.llama_block_destroy.restype = None
+        L.llama_block_status_string.argtypes = [ctypes.c_int]
+        L.llama_block_status_string.restype = ctypes.c_char_p
+        L.llama_block_last_error.argtypes = [vp]
+        L.llama_block_last_error.restype = ctypes.c_char_p
+        L.llama_block_stage_info.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                             ctypes.POINTER(ctypes.c_int64)]
+        L.llama_block_stage_info.restype = ctypes.c_int
+        L.llama_block_copy_stage.argtypes = [vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.llama_block_copy_stage.restype = ctypes.c_int
+        L.llama_block_profile.argtypes = [vp, ctypes.c_int]
+        L.llama_block_profile.restype = ctypes.c_int
+        L.llama_block_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int64)]
+        L.llama_block_profile_read.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _check(handle, status: int, what: str):
+    if status != LB_OK:
+        L = lib()
+        msg = L.llama_block_last_error(handle).decode() or L.llama_block_status_string(status).decode()
+        raise LlamaBlockError(status, f"{what}: {msg}")
+
+
+# ---- the C entry points, same names -------------------------------------------------
+
+def llama_block_status_string(status: int) -> str:
+    return lib().llama_block_status_string(status).decode()
+
+
+def llama_block_last_error(handle=None) -> str:
+    return lib().llama_block_last_error(handle).decode()
+
+
+def llama_block_init(cfg: LbConfig, weights: Dict[str, "object"]) -> int:
+    """cfg: LbConfig; weights: dict of device tensors named as LbWeights fields.
+    Returns the opaque handle (an int).  Synchronous."""
+    w = LbWeights(*[_ptr(weights[n]) for n in WEIGHT_NAMES])
+    h = ctypes.c_void_p()
+    st = lib().llama_block_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
+    _check(None, st, "llama_block_init")
+    return h.value
+
+
+def llama_block_forward(handle: int, x, start_pos: int, kv: Tuple, out, stream=None) -> None:
+    """x, out: device tensors [B][S][d]; kv: (k_cache, v_cache) device tensors
+    in the library's layout (see new_kv_cache).  Enqueued on `stream` (default:
+    torch's current stream)."""
+    k, v = kv
+    B, S = int(x.shape[0]), int(x.shape[1])
+    c = LbKVCache(_ptr(k), _ptr(v), int(k.shape[0]), int(k.shape[2]))
+    st = lib().llama_block_forward(handle, _ptr(x), B, S, int(start_pos), ctypes.byref(c),
+                                   _ptr(out), _stream(stream))
+    _check(handle, st, "llama_block_forward")
+
+
+def llama_block_destroy(handle: int) -> None:
+    if handle:
+        lib().llama_block_destroy(handle)
+
+
+def llama_block_stage_info(handle: int, stage: str) -> Tuple[str, int]:
+    e, cols = ctypes.c_int(), ctypes.c_int64()
+    st = lib().llama_block_stage_info(handle, STAGES[stage], ctypes.byref(e), ctypes.byref(cols))
+    _check(handle, st, "llama_block_stage_info")
+    return ELEM_NAMES[e.value], cols.value
+
+
+def llama_block_copy_stage(handle: int, stage: str, dst, stream=None) -> None:
+    nbytes = dst.numel() * dst.element_size()
+    st = lib().llama_block_copy_stage(handle, STAGES[stage], _ptr(dst), nbytes, _stream(stream))
+    _check(handle, st, "llama_block_copy_stage")
+
+
+def llama_block_profile(handle: int, enable: bool) -> None:
+    _check(handle, lib().llama_block_profile(handle, int(bool(enable))), "llama_block_profile")
+
+
+def llama_block_profile_read(handle: int) -> Tuple[Dict[str, float], int]:
+    """Summed milliseconds per stage since profiling was enabled, and the number
+    of profiled forwards."""
+    arr = (ctypes.c_double * len(STAGE_NAMES))()
+    calls = ctypes.c_int64()
+    st = lib().llama_block_profile_read(handle, arr, len(STAGE_NAMES), ctypes.byref(calls))
+    _check(handle, st, "llama_block_profile_read")
+    return {n: arr[i] for i, n in enumerate(STAGE_NAMES)}, calls.value
+
+
+# ---- small conveniences (allocation / argument packing only) ----------------------------
+
+def make_config(d_model, n_heads, n_kv_heads, d_head, d_ff, max_tokens, max_seq_len, rope_theta,
+                norm_eps, dtype: str, operands: str = "auto") -> LbConfig:
+    return LbConfig(d_model, n_heads, n_kv_heads, d_head, d_ff, max_tokens, max_seq_len,
+                    float(rope_theta), float(norm_eps), {"f32": LB_F32, "bf16": LB_BF16}[dtype],
+                    {"auto": LB_OPERANDS_AUTO, "f16": LB_OPERANDS_F16,
+                     "bf16": LB_OPERANDS_BF16}[operands])
+
+
+def new_kv_cache(batch: int, n_kv: int, max_seq_len: int, d_head: int, dtype, device="cuda",
+                 fill: Optional[float] = 0.0):
+    """Allocate (k, v) in the library's cache layout: k [B][n_kv][max_seq][d_head],
+    v [B][n_kv][d_head][max_seq] (transposed)."""
+    import torch
+    k = torch.empty((batch, n_kv, max_seq_len, d_head), dtype=dtype, device=device)
+    v = torch.empty((batch, n_kv, d_head, max_seq_len), dtype=dtype, device=device)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return k, v
+
+
+class LlamaBlock:
+    """Owns one library handle."""
+
+    def __init__(self, cfg: LbConfig, weights: Dict[str, "object"]):
+        self.cfg = cfg
+        self.handle = llama_block_init(cfg, weights)
+
+    def forward(self, x, start_pos: int, kv, out, stream=None):
+        llama_block_forward(self.handle, x, start_pos, kv, out, stream)
+        return out
+
+    def stage(self, name: str, rows: int):
+        import torch
+        elem, cols = llama_block_stage_info(self.handle, name)
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[elem]
+        dst = torch.empty((rows, cols), dtype=dt, device="cuda")
+        llama_block_copy_stage(self.handle, name, dst)
+        return dst
+
+    def close(self):
+        if self.handle:
+            llama_block_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

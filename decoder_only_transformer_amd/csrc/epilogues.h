@@ -1,0 +1,116 @@
+// GEMM epilogues of the block.  Every GEMM kernel hands its fp32 results to
+// an epilogue in chunks of 8 consecutive output columns of one token row:
+// row8(m, n, v) with n % 8 == 0.  The epilogue owns the fusion that follows
+// the product and the stores.
+#pragma once
+
+#include "lb_device.h"
+
+namespace lb {
+
+// q/k/v projection epilogue: RoPE on q and k, KV-cache append, q (and, for a
+// prefill from position 0, a k/v copy in the operand type) to the workspace.
+//
+// RoPE ("The Evolving Transformer 04 LLaMA", 02 RoPE; "Mini Llama 2
+// Implementation", Rotary positional embeddings): the pair (2i, 2i+1) of a
+// head is turned by the angle pos * theta^(-2i/d_head) with
+// pos = start_pos + s ("Full Llama 3 transformer block", How it works).  The
+// (cos, sin) table is built in fp64 on the host and stored as fp32 pairs.
+//
+// Column ranges of the packed projection: [0, qd) q heads, [qd, qd+kvd) k
+// heads, [qd+kvd, qd+2kvd) v heads, each head d_head wide.
+template <typename TO, typename TC>
+struct EpiQKV {
+    TO* q;              // [M][qd]
+    TO* kws;            // [B][nkv][s_stride][dh] or nullptr
+    TO* vws;            // [B][nkv][dh][s_stride] or nullptr
+    TC* kc;             // [B][nkv][cap][dh]
+    TC* vc;             // [B][nkv][dh][cap]
+    const float2* rope; // [max_seq][dh/2] (cos, sin)
+    int S, start_pos, cap, s_stride, nkv, dh, qd;
+
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+        const int b = m / S, s = m - b * S, pos = start_pos + s;
+        const int kvd = nkv * dh;
+        if (n < qd + kvd) {
+            const int j = (n < qd ? n : n - qd) % dh;
+            const float2* cs = rope + (size_t)pos * (dh / 2) + (j >> 1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float2 t = cs[e];
+                const float u = v[2 * e], w = v[2 * e + 1];
+                v[2 * e] = u * t.x - w * t.y;
+                v[2 * e + 1] = u * t.y + w * t.x;
+            }
+            if (n < qd) {
+                store8(q + (size_t)m * qd + n, v);
+            } else {
+                const int g = (n - qd) / dh;
+                const size_t bg = (size_t)b * nkv + g;
+                store8(kc + (bg * cap + pos) * dh + j, v);
+                if (kws) store8(kws + (bg * s_stride + s) * dh + j, v);
+            }
+        } else {
+            const int nn = n - qd - kvd;
+            const int g = nn / dh, j = nn % dh;
+            const size_t bg = (size_t)b * nkv + g;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vc[(bg * dh + j + e) * cap + pos] = from_f32<TC>(v[e]);
+            if (vws) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vws[(bg * dh + j + e) * s_stride + s] = from_f32<TO>(v[e]);
+            }
+        }
+    }
+};
+
+// h = x + o Wo^T, kept in fp32 ("Full Llama 3 transformer block", How it works).
+template <typename TR>
+struct EpiResid {
+    const TR* resid;  // [M][N]
+    float* out;       // [M][N]
+    int N;
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+        float r[8];
+        load8(resid + (size_t)m * N + n, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = r[e] + v[e];
+        store8(out + (size_t)m * N + n, v);
+    }
+};
+
+// z = SiLU(gate) * up ("The Evolving Transformer 04 LLaMA", 04 SWIGLU), with
+// SiLU(a) = a / (1 + e^-a).  The packed weight interleaves groups of four rows:
+// packed columns [8c, 8c+4) are gate features [4c, 4c+4), [8c+4, 8c+8) the
+// up features of the same four.
+template <typename TO>
+struct EpiSwiGLU {
+    TO* z;    // [M][dff]
+    int dff;
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a = v[e];
+            r[e] = a / (1.0f + expf(-a)) * v[4 + e];
+        }
+        store4(z + (size_t)m * dff + (n >> 1), r);
+    }
+};
+
+// y = h + z W_down^T, stored in the block's dtype.
+template <typename TY>
+struct EpiOut {
+    const float* h;  // [M][N]
+    TY* y;           // [M][N]
+    int N;
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+        float r[8];
+        load8(h + (size_t)m * N + n, r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = r[e] + v[e];
+        store8(y + (size_t)m * N + n, v);
+    }
+};
+
+}  // namespace lb

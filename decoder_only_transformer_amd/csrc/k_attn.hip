@@ -1,0 +1,554 @@
+// Causal grouped-query attention ("The Evolving Transformer 04 LLaMA", 05 GQA:
+// softmax(Q K^T / sqrt(d_head)) V with a lower-triangular mask; query head h
+// reads key/value head floor(h / n_rep); "Full Llama 3 transformer block",
+// How it works: queries sit at absolute positions start_pos + s and see every
+// cached key at a position <= their own).
+//
+// All three kernels evaluate the softmax online (running maximum, rescaled
+// running sum and output) in base 2: scores are multiplied by
+// log2(e)/sqrt(d_head) and exponentiated with exp2.
+#include <math.h>
+
+#include "launch.h"
+#include "lb_device.h"
+
+namespace lb {
+
+template <typename T, typename S> __device__ __forceinline__ u32x4 to_operand(const u32x4& raw);
+template <> __device__ __forceinline__ u32x4 to_operand<f16, f16>(const u32x4& raw) { return raw; }
+template <> __device__ __forceinline__ u32x4 to_operand<bf16, bf16>(const u32x4& raw) { return raw; }
+template <> __device__ __forceinline__ u32x4 to_operand<f16, bf16>(const u32x4& raw) {
+    bf16x8 s;
+    __builtin_memcpy(&s, &raw, 16);
+    f16x8 d;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = (f16)(float)s[e];
+    u32x4 r;
+    __builtin_memcpy(&r, &d, 16);
+    return r;
+}
+
+// Row order of the key tile fed to the S^T = K Q^T product: MFMA row i holds
+// key pi(i) (bits 2 and 3 of i swapped), so that after the product each lane
+// holds 8 consecutive keys per 16-key step -- the order the P V product needs
+// for its operand, with V^T read as contiguous 16-byte runs.
+__device__ __forceinline__ int key_perm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+// LDS chunk swizzle of the key tile, conflict-free for the permuted read.
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+// ------------------------------------------------------------------------------------
+// Prefill.  Grid (ceil(S/32), B*n_kv*n_hb), NW wavefronts per block: the
+// block owns 32 consecutive queries of one sequence and NW query heads of one
+// KV group; every wavefront is one head and all of them share each K / V^T
+// tile staged in LDS.  Per 64-key tile a wavefront computes S^T (64 keys x
+// 32 queries) with 32x32x16 MFMAs, masks, updates the softmax state of its
+// lane's query (lane = query, so rescaling is lane-local) and accumulates
+// O^T += V^T P^T.  Tiles are prefetched into registers during the MFMAs.
+// Heavier (later) query blocks are launched first.
+// ------------------------------------------------------------------------------------
+template <typename T, typename KVT, int DH, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
+    const T* __restrict__ q, const KVT* __restrict__ kbase, const KVT* __restrict__ vbase,
+    T* __restrict__ o, long k_bg, long v_bg, int t_stride, int S, int start_pos, int H, int nkv,
+    int n_rep, int n_hb, float c) {
+    typedef typename vec8<T>::type V8;
+    constexpr int KT = 64;
+    constexpr int NT = NW * 64;
+    constexpr int KCH = DH / 8;
+    constexpr int KCHUNKS = KT * KCH;
+    constexpr int VCHUNKS = DH * (KT / 8);
+    constexpr int KPT = (KCHUNKS + NT - 1) / NT;
+    constexpr int VPT = (VCHUNKS + NT - 1) / NT;
+    __shared__ __attribute__((aligned(16))) T ks[KT * DH];
+    __shared__ __attribute__((aligned(16))) T vs[DH * KT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int qb = gridDim.x - 1 - blockIdx.x;
+    const int hb = blockIdx.y % n_hb;
+    const int bg = blockIdx.y / n_hb;
+    const int g = bg % nkv, b = bg / nkv;
+    const int hl = hb * NW + wave;
+    const bool head_ok = hl < n_rep;
+    const int h = g * n_rep + (head_ok ? hl : n_rep - 1);
+    const int q0 = qb * 32;
+    const int qi = q0 + (lane & 31);
+    const int qrow = min(qi, S - 1);
+    const int qpos = start_pos + qrow;
+    const int qd = H * DH;
+
+    V8 qf[DH / 16];
+    {
+        const T* qp = q + (size_t)(b * S + qrow) * qd + h * DH + 8 * (lane >> 5);
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qp + 16 * kk);
+    }
+    const int kv_len = start_pos + min(q0 + 32, S);
+    const int ntiles = (kv_len + KT - 1) / KT;
+    const KVT* kp = kbase + (size_t)bg * k_bg;
+    const KVT* vp = vbase + (size_t)bg * v_bg;
+
+    u32x4 kreg[KPT], vreg[VPT];
+    auto gload = [&](int tile) {
+        const int t0 = tile * KT;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int cidx = tid + i * NT;
+            if (cidx < KCHUNKS) {
+                const int row = cidx / KCH, ch = cidx % KCH, key = t0 + row;
+                if (key < kv_len)
+                    kreg[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)key * DH + ch * 8);
+                else
+                    kreg[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int cidx = tid + i * NT;
+            if (cidx < VCHUNKS) {
+                const int d = cidx / (KT / 8), ch = cidx % (KT / 8), key8 = t0 + ch * 8;
+                const KVT* p = vp + (size_t)d * t_stride + key8;
+                if (key8 + 8 <= kv_len) {
+                    vreg[i] = *reinterpret_cast<const u32x4*>(p);
+                } else {
+                    KVT tmp[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) tmp[e] = (key8 + e < kv_len) ? p[e] : from_f32<KVT>(0.0f);
+                    __builtin_memcpy(&vreg[i], tmp, 16);
+                }
+            }
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int cidx = tid + i * NT;
+            if (cidx < KCHUNKS) {
+                const int row = cidx / KCH, ch = cidx % KCH;
+                *reinterpret_cast<u32x4*>(ks + row * DH + ((ch ^ kswz(row)) << 3)) = to_operand<T, KVT>(kreg[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int cidx = tid + i * NT;
+            if (cidx < VCHUNKS) {
+                const int d = cidx / (KT / 8), ch = cidx % (KT / 8);
+                *reinterpret_cast<u32x4*>(vs + d * KT + ((ch ^ (d & 7)) << 3)) = to_operand<T, KVT>(vreg[i]);
+            }
+        }
+    };
+
+    f32x16 oacc[DH / 32];
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    const int prow = key_perm(lane & 31);
+
+    gload(0);
+    for (int tile = 0; tile < ntiles; ++tile) {
+        __syncthreads();
+        lstore();
+        __syncthreads();
+        if (tile + 1 < ntiles) gload(tile + 1);
+
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+            const int row = kb * 32 + prow;
+#pragma unroll
+            for (int kk = 0; kk < DH / 16; ++kk) {
+                const int ch = 2 * kk + (lane >> 5);
+                const V8 kf = *reinterpret_cast<const V8*>(ks + row * DH + ((ch ^ kswz(row)) << 3));
+                sacc[kb] = mfma32(kf, qf[kk], sacc[kb]);
+            }
+        }
+        const int t0 = tile * KT;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = t0 + kb * 32 + 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7);
+                float sv = sacc[kb][r] * c;
+                if (key > qpos) sv = -INFINITY;
+                sacc[kb][r] = sv;
+                mx = fmaxf(mx, sv);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        float ls = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2f(sacc[kb][r] - m_new);
+                sacc[kb][r] = p;
+                ls += p;
+            }
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        V8 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[kb][cc][e] = from_f32<T>(sacc[kb][8 * cc + e]);
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) {
+            const int d = dt * 32 + (lane & 31);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    const int ch = 4 * kb + 2 * cc + (lane >> 5);
+                    const V8 vf = *reinterpret_cast<const V8*>(vs + d * KT + ((ch ^ (d & 7)) << 3));
+                    oacc[dt] = mfma32(vf, pf[kb][cc], oacc[dt]);
+                }
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l_tot;
+    if (head_ok && qi < S) {
+        T* op = o + (size_t)(b * S + qi) * qd + h * DH;
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float vv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vv[e] = oacc[dt][4 * a + e] * inv;
+                store4(op + dt * 32 + 8 * a + 4 * (lane >> 5), vv);
+            }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Decode (one new token per sequence).  Grid (nsplit, B*n_kv), 4 wavefronts
+// per block; the block owns 4*CH consecutive keys of one (sequence, KV group)
+// and all n_rep query heads of the group (heads are the 16 columns of a
+// 16x16x32 MFMA; columns >= n_rep are zero).  K rows and V^T rows go straight
+// from HBM into MFMA operand registers with 16-byte loads -- no LDS.  The
+// cache is bf16; q and the probabilities enter the bf16 MFMAs as a hi + lo
+// pair of bf16 values (16 mantissa bits), so only the cache itself is bf16.
+// The block merges its wavefronts in LDS and writes one partial (unnormalised
+// output, running max, running sum) per head; attn_combine_kernel merges the
+// splits.
+// ------------------------------------------------------------------------------------
+template <typename T, int DH, int CH>
+__global__ void __launch_bounds__(256) attn_decode_kernel(
+    const T* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    float* __restrict__ part, long k_bg, long v_bg, int t_stride, int H, int nkv, int n_rep,
+    int kv_len, int nsplit, float c) {
+    constexpr int NW = 4;
+    __shared__ float sm[NW][16], sl[NW][16];
+    __shared__ float so[NW][16][DH];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int split = blockIdx.x, bg = blockIdx.y;
+    const int b = bg / nkv, g = bg % nkv;
+    const int hl = lane & 15, grp = lane >> 4;
+
+    bf16x8 qh[DH / 32], ql[DH / 32];
+#pragma unroll
+    for (int kk = 0; kk < DH / 32; ++kk) {
+        float v[8];
+        if (hl < n_rep) {
+            load8(q + (size_t)b * H * DH + (size_t)(g * n_rep + hl) * DH + 32 * kk + 8 * grp, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bf16 hi = (bf16)v[e];
+            qh[kk][e] = hi;
+            ql[kk][e] = (bf16)(v[e] - (float)hi);
+        }
+    }
+
+    const bf16* kp = kc + (size_t)bg * k_bg;
+    const bf16* vp = vc + (size_t)bg * v_bg;
+    const int k_begin = (split * NW + wave) * CH;
+    f32x4 oacc[DH / 16];
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    for (int st = 0; st < CH / 32; ++st) {
+        const int kb0 = k_begin + 32 * st;
+        if (kb0 >= kv_len) break;
+        bf16x8 kf[2][DH / 32];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int key = kb0 + 8 * ((lane & 15) >> 2) + 4 * t + (lane & 3);
+            const bf16* p = kp + (size_t)min(key, kv_len - 1) * DH + 8 * grp;
+#pragma unroll
+            for (int kk = 0; kk < DH / 32; ++kk) kf[t][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
+        }
+        bf16x8 vf[DH / 16];
+        const int key8 = kb0 + 8 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) {
+            const bf16* p = vp + (size_t)(16 * dt + (lane & 15)) * t_stride + key8;
+            if (key8 + 8 <= kv_len) {
+                vf[dt] = *reinterpret_cast<const bf16x8*>(p);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vf[dt][e] = (key8 + e < kv_len) ? p[e] : (bf16)0.0f;
+            }
+        }
+        f32x4 sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DH / 32; ++kk) {
+                sc[t] = mfma16(kf[t][kk], qh[kk], sc[t]);
+                sc[t] = mfma16(kf[t][kk], ql[kk], sc[t]);
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kb0 + 8 * grp + 4 * t + r;
+                float sv = sc[t][r] * c;
+                if (key >= kv_len) sv = -INFINITY;
+                sc[t][r] = sv;
+                mx = fmaxf(mx, sv);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        float pv[8], ls = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2f(sc[t][r] - m_new);
+                pv[4 * t + r] = p;
+                ls += p;
+            }
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bf16 hi = (bf16)pv[e];
+            ph[e] = hi;
+            pl[e] = (bf16)(pv[e] - (float)hi);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[dt][r] *= alpha;
+            oacc[dt] = mfma16(vf[dt], ph, oacc[dt]);
+            oacc[dt] = mfma16(vf[dt], pl, oacc[dt]);
+        }
+    }
+
+    float lt = l_run + __shfl_xor(l_run, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    if (grp == 0) {
+        sm[wave][hl] = m_run;
+        sl[wave][hl] = lt;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) so[wave][hl][16 * dt + 4 * grp + r] = oacc[dt][r];
+    __syncthreads();
+    for (int idx = tid; idx < n_rep * DH; idx += NW * 64) {
+        const int hh = idx / DH, d = idx % DH;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][hh]);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            if (sm[w][hh] != -INFINITY) {
+                const float f = exp2f(sm[w][hh] - M);
+                L += sl[w][hh] * f;
+                O += so[w][hh][d] * f;
+            }
+        }
+        float* pp = part + (((size_t)b * H + g * n_rep + hh) * nsplit + split) * (DH + 2);
+        pp[d] = O;
+        if (d == 0) {
+            pp[DH] = M;
+            pp[DH + 1] = L;
+        }
+    }
+}
+
+// Merge the decode splits of one (sequence, head): grid B*H, DH threads.
+template <typename T, int DH>
+__global__ void __launch_bounds__(DH) attn_combine_kernel(const float* __restrict__ part,
+                                                          T* __restrict__ o, int nsplit) {
+    const int bh = blockIdx.x, d = threadIdx.x;
+    const float* pp = part + (size_t)bh * nsplit * (DH + 2);
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (DH + 2) + DH]);
+    float L = 0.0f, O = 0.0f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float f = exp2f(pp[s * (DH + 2) + DH] - M);
+        L += pp[s * (DH + 2) + DH + 1] * f;
+        O += pp[s * (DH + 2) + d] * f;
+    }
+    o[(size_t)bh * DH + d] = from_f32<T>(O / L);
+}
+
+// ------------------------------------------------------------------------------------
+// fp32 attention for fp32 blocks.  Grid (S, H, B), one wavefront per query:
+// lanes score 64 keys at a time (fp32 dot products), the block of
+// probabilities goes through LDS and each lane accumulates up to 4 output
+// dimensions.  Any d_head <= 256, any length.
+// ------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) attn_simple_kernel(const float* __restrict__ q,
+                                                         const float* __restrict__ kc,
+                                                         const float* __restrict__ vc,
+                                                         float* __restrict__ o, long k_bg,
+                                                         long v_bg, int t_stride, int S,
+                                                         int start_pos, int H, int nkv, int dh,
+                                                         float c) {
+    __shared__ float qs[256];
+    __shared__ float ps[64];
+    const int lane = threadIdx.x;
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int g = h / (H / nkv);
+    const int n = start_pos + s + 1;
+    const size_t bg = (size_t)b * nkv + g;
+    const float* qp = q + ((size_t)b * S + s) * H * dh + (size_t)h * dh;
+    for (int d = lane; d < dh; d += 64) qs[d] = qp[d];
+    __syncthreads();
+    float oa[4] = {0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+    for (int t0 = 0; t0 < n; t0 += 64) {
+        const int t = t0 + lane;
+        float sv = -INFINITY;
+        if (t < n) {
+            const float* kr = kc + bg * k_bg + (size_t)t * dh;
+            float acc = 0.0f;
+            for (int d = 0; d < dh; ++d) acc = fmaf(qs[d], kr[d], acc);
+            sv = acc * c;
+        }
+        const float m_new = fmaxf(m_run, wave_max(sv));
+        const float alpha = exp2f(m_run - m_new);
+        const float p = (t < n) ? exp2f(sv - m_new) : 0.0f;
+        l_run = l_run * alpha + wave_sum(p);
+        m_run = m_new;
+        ps[lane] = p;
+        __syncthreads();
+        const int cnt = min(64, n - t0);
+        for (int j = 0; j < 4; ++j) {
+            const int d = lane + 64 * j;
+            if (d < dh) {
+                float a = oa[j] * alpha;
+                const float* vr = vc + bg * v_bg + (size_t)d * t_stride + t0;
+                for (int u = 0; u < cnt; ++u) a = fmaf(ps[u], vr[u], a);
+                oa[j] = a;
+            }
+        }
+        __syncthreads();
+    }
+    float* op = o + ((size_t)b * S + s) * H * dh + (size_t)h * dh;
+    for (int j = 0; j < 4; ++j) {
+        const int d = lane + 64 * j;
+        if (d < dh) op[d] = oa[j] / l_run;
+    }
+}
+
+// ---- dispatch ---------------------------------------------------------------------------
+
+template <typename T, typename KVT, int DH, int NW>
+static hipError_t prefill_t(const AttnArgs& a, hipStream_t s) {
+    const int n_rep = a.H / a.nkv;
+    const int n_hb = n_rep / NW;
+    const dim3 grid((a.S + 31) / 32, a.B * a.nkv * n_hb);
+    const float c = kLog2e / sqrtf((float)DH);
+    attn_prefill_kernel<T, KVT, DH, NW><<<grid, NW * 64, 0, s>>>(
+        (const T*)a.q, (const KVT*)a.k, (const KVT*)a.v, (T*)a.o, a.k_bg, a.v_bg, a.t_stride, a.S,
+        a.start_pos, a.H, a.nkv, n_rep, n_hb, c);
+    return hipGetLastError();
+}
+
+template <typename T, typename KVT, int DH>
+static hipError_t prefill_nw(const AttnArgs& a, hipStream_t s) {
+    const int n_rep = a.H / a.nkv;
+    if (n_rep % 8 == 0) return prefill_t<T, KVT, DH, 8>(a, s);
+    if (n_rep % 4 == 0) return prefill_t<T, KVT, DH, 4>(a, s);
+    if (n_rep % 3 == 0) return prefill_t<T, KVT, DH, 3>(a, s);
+    if (n_rep % 2 == 0) return prefill_t<T, KVT, DH, 2>(a, s);
+    return prefill_t<T, KVT, DH, 1>(a, s);
+}
+
+template <typename T, typename KVT>
+static hipError_t prefill_dh(const AttnArgs& a, hipStream_t s) {
+    if (a.dh == 128) return prefill_nw<T, KVT, 128>(a, s);
+    if (a.dh == 64) return prefill_nw<T, KVT, 64>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t attn_prefill(Elem op, Elem kv_t, const AttnArgs& a, hipStream_t s) {
+    if (a.B <= 0 || a.S <= 0) return hipSuccess;
+    if (op == Elem::F16 && kv_t == Elem::F16) return prefill_dh<f16, f16>(a, s);
+    if (op == Elem::F16 && kv_t == Elem::BF16) return prefill_dh<f16, bf16>(a, s);
+    if (op == Elem::BF16 && kv_t == Elem::BF16) return prefill_dh<bf16, bf16>(a, s);
+    return hipErrorInvalidValue;
+}
+
+constexpr int kDecodeCH = 128;                    // keys per wavefront
+constexpr int kDecodeKeysPerBlock = 4 * kDecodeCH;
+
+size_t decode_partials_floats(int max_batch, int H, int dh, int max_kv) {
+    const size_t nsplit = (size_t)(max_kv + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
+    return (size_t)max_batch * H * nsplit * (dh + 2);
+}
+
+template <typename T, int DH>
+static hipError_t decode_t(const AttnArgs& a, float* part, hipStream_t s) {
+    const int n_rep = a.H / a.nkv;
+    const int kv_len = a.start_pos + 1;
+    const int nsplit = (kv_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
+    const float c = kLog2e / sqrtf((float)DH);
+    attn_decode_kernel<T, DH, kDecodeCH><<<dim3(nsplit, a.B * a.nkv), 256, 0, s>>>(
+        (const T*)a.q, (const bf16*)a.k, (const bf16*)a.v, part, a.k_bg, a.v_bg, a.t_stride, a.H,
+        a.nkv, n_rep, kv_len, nsplit, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_combine_kernel<T, DH><<<a.B * a.H, DH, 0, s>>>(part, (T*)a.o, nsplit);
+    return hipGetLastError();
+}
+
+hipError_t attn_decode(Elem op, Elem kv_t, const AttnArgs& a, float* part, hipStream_t s) {
+    if (a.B <= 0) return hipSuccess;
+    if (kv_t != Elem::BF16 || a.S != 1 || a.H / a.nkv > 16) return hipErrorInvalidValue;
+    if (op == Elem::F16 && a.dh == 128) return decode_t<f16, 128>(a, part, s);
+    if (op == Elem::F16 && a.dh == 64) return decode_t<f16, 64>(a, part, s);
+    if (op == Elem::BF16 && a.dh == 128) return decode_t<bf16, 128>(a, part, s);
+    if (op == Elem::BF16 && a.dh == 64) return decode_t<bf16, 64>(a, part, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t attn_simple(const AttnArgs& a, hipStream_t s) {
+    if (a.B <= 0 || a.S <= 0) return hipSuccess;
+    if (a.dh > 256) return hipErrorInvalidValue;
+    const float c = kLog2e / sqrtf((float)a.dh);
+    attn_simple_kernel<<<dim3(a.S, a.H, a.B), 64, 0, s>>>(
+        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.k_bg, a.v_bg,
+        a.t_stride, a.S, a.start_pos, a.H, a.nkv, a.dh, c);
+    return hipGetLastError();
+}
+
+}  // namespace lb

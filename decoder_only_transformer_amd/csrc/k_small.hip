@@ -1,0 +1,119 @@
+// RMSNorm, dtype conversion and weight packing kernels.
+#include "launch.h"
+#include "lb_device.h"
+
+namespace lb {
+
+// RMSNorm ("The Evolving Transformer 04 LLaMA", 03 RMSNORM; "Full Llama 3
+// transformer block", How it works): out = x / sqrt(mean(x^2) + eps) * g.
+// One wavefront per token row; the sum of squares is accumulated in fp32 per
+// lane (8 elements per 16-byte load) and reduced across the wavefront in a
+// fixed butterfly order, so results are deterministic.
+template <typename TI, typename TO>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const TI* __restrict__ x,
+                                                      const float* __restrict__ g,
+                                                      TO* __restrict__ out, int M, int d, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const TI* xr = x + (size_t)row * d;
+    TO* orow = out + (size_t)row * d;
+    float ss = 0.0f;
+    for (int c = lane * 8; c < d; c += 512) {
+        float v[8];
+        load8(xr + c, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int c = lane * 8; c < d; c += 512) {
+        float v[8], gg[8];
+        load8(xr + c, v);
+        load8(g + c, gg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] * r * gg[e];
+        store8(orow + c, v);
+    }
+}
+
+template <typename TI, typename TO>
+__global__ void convert_kernel(const TI* __restrict__ src, TO* __restrict__ dst, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = from_f32<TO>(to_f32(src[i]));
+}
+
+// Packed row p: group c = p / 8; rows 8c..8c+3 = gate rows 4c..4c+3,
+// rows 8c+4..8c+7 = up rows 4c..4c+3.
+template <typename TI, typename TO>
+__global__ void pack_gate_up_kernel(const TI* __restrict__ gate, const TI* __restrict__ up,
+                                    TO* __restrict__ dst, int dff, int d) {
+    const int p = blockIdx.x;
+    const int c = p >> 3, e = p & 7;
+    const TI* src = (e < 4) ? gate + (size_t)(4 * c + e) * d : up + (size_t)(4 * c + e - 4) * d;
+    TO* out = dst + (size_t)p * d;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) out[k] = from_f32<TO>(to_f32(src[k]));
+}
+
+template <typename TI, typename TO>
+static hipError_t rmsnorm_t(const void* x, const float* g, void* out, int M, int d, float eps,
+                            hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    rmsnorm_kernel<TI, TO><<<(M + 3) / 4, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(Elem in_t, Elem out_t, const void* x, const float* g, void* out, int M,
+                          int d, float eps, hipStream_t s) {
+#define RN(TI, TO) return rmsnorm_t<TI, TO>(x, g, out, M, d, eps, s)
+    if (in_t == Elem::F32 && out_t == Elem::F32) RN(float, float);
+    if (in_t == Elem::F32 && out_t == Elem::F16) RN(float, f16);
+    if (in_t == Elem::F32 && out_t == Elem::BF16) RN(float, bf16);
+    if (in_t == Elem::BF16 && out_t == Elem::F16) RN(bf16, f16);
+    if (in_t == Elem::BF16 && out_t == Elem::BF16) RN(bf16, bf16);
+#undef RN
+    return hipErrorInvalidValue;
+}
+
+template <typename TI, typename TO>
+static hipError_t convert_t(const void* src, void* dst, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    convert_kernel<TI, TO><<<(unsigned)blocks, 256, 0, s>>>((const TI*)src, (TO*)dst, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_convert(Elem src_t, Elem dst_t, const void* src, void* dst, size_t n,
+                          hipStream_t s) {
+#define CV(TI, TO) return convert_t<TI, TO>(src, dst, n, s)
+    if (src_t == Elem::F32 && dst_t == Elem::F32) CV(float, float);
+    if (src_t == Elem::BF16 && dst_t == Elem::F32) CV(bf16, float);
+    if (src_t == Elem::BF16 && dst_t == Elem::F16) CV(bf16, f16);
+    if (src_t == Elem::BF16 && dst_t == Elem::BF16) CV(bf16, bf16);
+    if (src_t == Elem::F32 && dst_t == Elem::BF16) CV(float, bf16);
+    if (src_t == Elem::F32 && dst_t == Elem::F16) CV(float, f16);
+#undef CV
+    return hipErrorInvalidValue;
+}
+
+template <typename TI, typename TO>
+static hipError_t pack_t(const void* gate, const void* up, void* dst, int dff, int d,
+                         hipStream_t s) {
+    pack_gate_up_kernel<TI, TO><<<2 * dff, 256, 0, s>>>((const TI*)gate, (const TI*)up, (TO*)dst,
+                                                        dff, d);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const void* up, void* dst,
+                               int dff, int d, hipStream_t s) {
+#define PK(TI, TO) return pack_t<TI, TO>(gate, up, dst, dff, d, s)
+    if (src_t == Elem::F32 && dst_t == Elem::F32) PK(float, float);
+    if (src_t == Elem::BF16 && dst_t == Elem::F16) PK(bf16, f16);
+    if (src_t == Elem::BF16 && dst_t == Elem::BF16) PK(bf16, bf16);
+#undef PK
+    return hipErrorInvalidValue;
+}
+
+}  // namespace lb

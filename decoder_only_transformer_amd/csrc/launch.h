@@ -1,0 +1,70 @@
+// Host-side launch interface between the block executor and the kernel
+// translation units.  All pointers are device pointers; every launcher only
+// enqueues work on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lb {
+
+enum class Elem : int { F32 = 0, BF16 = 1, F16 = 2 };
+
+inline size_t elem_bytes(Elem e) { return e == Elem::F32 ? 4 : 2; }
+
+// ---- small kernels ------------------------------------------------------------
+// out[m][:] = x[m][:] / sqrt(mean(x[m]^2) + eps) * g  (fp32 arithmetic, one rounding)
+hipError_t launch_rmsnorm(Elem in_t, Elem out_t, const void* x, const float* g, void* out, int M,
+                          int d, float eps, hipStream_t s);
+// dst[i] = src[i] converted (round to nearest even)
+hipError_t launch_convert(Elem src_t, Elem dst_t, const void* src, void* dst, size_t n,
+                          hipStream_t s);
+// dst [2*dff][d]: row groups of 8 = four gate rows then the same four up rows
+hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const void* up, void* dst,
+                               int dff, int d, hipStream_t s);
+
+// ---- GEMMs: C[M][N] = A[M][K] . W[N][K]^T, fp32 accumulation ---------------------
+struct QkvEpi {
+    void* q;          // [M][qd]           operand type
+    void* kws;        // [B][nkv][s_stride][dh] operand type, or nullptr
+    void* vws;        // [B][nkv][dh][s_stride] operand type, or nullptr
+    void* kc;         // [Bc][nkv][cap][dh] cache type
+    void* vc;         // [Bc][nkv][dh][cap] cache type
+    const float2* rope;
+    int S, start_pos, cap, s_stride, nkv, dh, qd;
+};
+// op: operand type of A and W (F32 selects the plain fp32 kernels); cache: cache type.
+hipError_t gemm_qkv(Elem op, Elem cache, const void* A, const void* W, int M, int N, int K,
+                    const QkvEpi& e, hipStream_t s);
+// out(fp32) = resid + A W^T
+hipError_t gemm_resid(Elem op, Elem resid_t, const void* A, const void* W, int M, int N, int K,
+                      const void* resid, float* out, hipStream_t s);
+// z[M][dff] = SiLU(gate) * up from the interleaved gate/up product (N = 2*dff)
+hipError_t gemm_swiglu(Elem op, const void* A, const void* W, int M, int N, int K, void* z,
+                       hipStream_t s);
+// y = h + A W^T, y in out_t
+hipError_t gemm_out(Elem op, Elem out_t, const void* A, const void* W, int M, int N, int K,
+                    const float* h, void* y, hipStream_t s);
+
+// ---- attention --------------------------------------------------------------------
+struct AttnArgs {
+    const void* q;   // [B*S][H*dh] operand type (fp32 for fp32 blocks)
+    const void* k;   // K rows: element (bg, t, d) at k[bg*k_bg + t*dh + d]
+    const void* v;   // V^T rows: element (bg, d, t) at v[bg*v_bg + d*t_stride + t]
+    void* o;         // [B*S][H*dh] operand type
+    long k_bg, v_bg;
+    int t_stride;
+    int B, S, start_pos, H, nkv, dh;
+};
+// Causal prefill attention (seq_len > 1).  op: q/o type; kv_t: K/V storage type.
+hipError_t attn_prefill(Elem op, Elem kv_t, const AttnArgs& a, hipStream_t s);
+
+// Split-K decode attention (seq_len == 1) over a bf16/fp16 cache, then the
+// merge of the splits into o.  part: workspace of decode_partials_floats().
+size_t decode_partials_floats(int max_batch, int H, int dh, int max_kv);
+hipError_t attn_decode(Elem op, Elem kv_t, const AttnArgs& a, float* part, hipStream_t s);
+
+// Plain fp32 attention (fp32 blocks, any seq_len).
+hipError_t attn_simple(const AttnArgs& a, hipStream_t s);
+
+}  // namespace lb

@@ -1,0 +1,471 @@
+// Block executor and C ABI (include/llama_block.h).
+//
+// init: validate the config, pack the weights into library-owned device
+// memory (fused [Wq;Wk;Wv], gate/up interleaved in groups of four rows,
+// bf16 -> fp16 widening for fp16 operands), build the RoPE table and size the
+// workspace.  forward: validate, then enqueue
+//   RMSNorm_1 -> QKV GEMM (+RoPE, KV append) -> attention -> o GEMM (+x)
+//   -> RMSNorm_2 -> gate/up GEMM (+SiLU*up) -> down GEMM (+h)
+// on the caller's stream ("Full Llama 3 transformer block", How it works).
+#include "llama_block.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+using lb::Elem;
+
+struct lb_block {
+    lb_config cfg;
+    Elem dt = Elem::F32;  // dtype of x, out, cache
+    Elem op = Elem::F32;  // matrix-product operand type
+    int dev = 0;
+    int qd = 0, kvd = 0, nqkv = 0;
+    // packed weights
+    void* w_qkv = nullptr;
+    void* w_o = nullptr;
+    void* w_gu = nullptr;
+    void* w_down = nullptr;
+    float* g1 = nullptr;
+    float* g2 = nullptr;
+    float2* rope = nullptr;
+    // workspace
+    void* n1 = nullptr;
+    void* n2 = nullptr;
+    void* q = nullptr;
+    void* o = nullptr;
+    void* z = nullptr;
+    float* h = nullptr;
+    void* kws = nullptr;
+    void* vws = nullptr;
+    size_t ws_rows = 0;  // token rows the k/v workspace copies hold
+    float* part = nullptr;
+    std::vector<void*> allocs;
+    std::string err;
+    // per-stage timing: a ring of event sets, LB_NUM_STAGES + 1 events each
+    bool profiling = false;
+    std::vector<hipEvent_t> events;
+    std::vector<int> pending;      // ring slots recorded but not yet summed
+    int next_slot = 0;
+    double stage_ms[LB_NUM_STAGES] = {};
+    int64_t profiled_calls = 0;
+};
+
+static constexpr int kProfileSlots = 256;
+
+static void profile_release(lb_block* blk) {
+    for (hipEvent_t e : blk->events) hipEventDestroy(e);
+    blk->events.clear();
+    blk->pending.clear();
+    blk->profiling = false;
+}
+
+// Sum one recorded slot into the per-stage totals (waits for its events).
+static hipError_t profile_collect(lb_block* blk, int slot) {
+    hipEvent_t* ev = &blk->events[(size_t)slot * (LB_NUM_STAGES + 1)];
+    hipError_t e = hipEventSynchronize(ev[LB_NUM_STAGES]);
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < LB_NUM_STAGES; ++i) {
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+        if (e != hipSuccess) return e;
+        blk->stage_ms[i] += ms;
+    }
+    blk->profiled_calls += 1;
+    return hipSuccess;
+}
+
+static thread_local std::string g_init_error;
+
+static lb_status fail(lb_block* blk, lb_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    if (blk) blk->err = buf;
+    else g_init_error = buf;
+    return st;
+}
+
+static void free_all(lb_block* blk) {
+    for (void* p : blk->allocs) hipFree(p);
+    blk->allocs.clear();
+}
+
+template <typename P>
+static bool dalloc(lb_block* blk, P** out, size_t bytes) {
+    void* p = nullptr;
+    if (bytes == 0) bytes = 256;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    blk->allocs.push_back(p);
+    *out = static_cast<P*>(p);
+    return true;
+}
+
+static size_t esz(Elem e) { return lb::elem_bytes(e); }
+
+extern "C" const char* llama_block_status_string(lb_status s) {
+    switch (s) {
+        case LB_OK: return "ok";
+        case LB_ERR_INVALID_ARG: return "invalid argument";
+        case LB_ERR_UNSUPPORTED: return "unsupported configuration";
+        case LB_ERR_OOM: return "device out of memory";
+        case LB_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+extern "C" const char* llama_block_last_error(const lb_block* blk) {
+    return blk ? blk->err.c_str() : g_init_error.c_str();
+}
+
+static lb_status validate_config(const lb_config* c) {
+    if (c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->d_head <= 0 || c->d_ff <= 0)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "d_model, n_heads, n_kv_heads, d_head and d_ff must be > 0");
+    if ((long)c->n_heads * c->d_head != c->d_model)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "d_model (%d) != n_heads (%d) * d_head (%d)", c->d_model,
+                    c->n_heads, c->d_head);
+    if (c->n_heads % c->n_kv_heads != 0)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "n_heads (%d) is not a multiple of n_kv_heads (%d)",
+                    c->n_heads, c->n_kv_heads);
+    if (c->d_head % 2 != 0) return fail(nullptr, LB_ERR_INVALID_ARG, "d_head (%d) must be even", c->d_head);
+    if (c->max_tokens <= 0 || c->max_seq_len <= 0)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "max_tokens and max_seq_len must be > 0");
+    if (!(c->rope_theta > 0.0) || !std::isfinite(c->rope_theta) || !(c->norm_eps > 0.0) ||
+        !std::isfinite(c->norm_eps))
+        return fail(nullptr, LB_ERR_INVALID_ARG, "rope_theta and norm_eps must be finite and > 0");
+    if (c->dtype != LB_F32 && c->dtype != LB_BF16)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
+    if (c->operands != LB_OPERANDS_AUTO && c->operands != LB_OPERANDS_F16 && c->operands != LB_OPERANDS_BF16)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "unknown operands %d", (int)c->operands);
+    if (c->dtype == LB_BF16) {
+        if (c->d_head != 64 && c->d_head != 128)
+            return fail(nullptr, LB_ERR_UNSUPPORTED, "bf16 blocks need d_head 64 or 128 (got %d)", c->d_head);
+        if (c->d_model % 64 != 0 || c->d_ff % 64 != 0)
+            return fail(nullptr, LB_ERR_UNSUPPORTED, "bf16 blocks need d_model and d_ff multiples of 64");
+        if (c->n_heads / c->n_kv_heads > 16)
+            return fail(nullptr, LB_ERR_UNSUPPORTED, "bf16 blocks need n_heads / n_kv_heads <= 16");
+    } else {
+        if (c->d_head % 8 != 0 || c->d_head > 256)
+            return fail(nullptr, LB_ERR_UNSUPPORTED, "fp32 blocks need d_head a multiple of 8 and <= 256");
+        if (c->d_model % 8 != 0 || c->d_ff % 4 != 0)
+            return fail(nullptr, LB_ERR_UNSUPPORTED, "fp32 blocks need d_model % 8 == 0 and d_ff % 4 == 0");
+    }
+    return LB_OK;
+}
+
+extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w, lb_block** out) {
+    g_init_error.clear();
+    if (!out) return fail(nullptr, LB_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg || !w) return fail(nullptr, LB_ERR_INVALID_ARG, "cfg or weights is NULL");
+    const void* wp[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
+    for (const void* p : wp)
+        if (!p) return fail(nullptr, LB_ERR_INVALID_ARG, "a weight pointer is NULL");
+    lb_status st = validate_config(cfg);
+    if (st != LB_OK) return st;
+
+    lb_block* blk = new lb_block();
+    blk->cfg = *cfg;
+    const lb_config& c = blk->cfg;
+    blk->dt = c.dtype == LB_BF16 ? Elem::BF16 : Elem::F32;
+    blk->op = c.dtype == LB_F32 ? Elem::F32 : (c.operands == LB_OPERANDS_BF16 ? Elem::BF16 : Elem::F16);
+    if (hipGetDevice(&blk->dev) != hipSuccess) {
+        delete blk;
+        return fail(nullptr, LB_ERR_HIP, "hipGetDevice failed");
+    }
+    const int d = c.d_model, dh = c.d_head, nkv = c.n_kv_heads, dff = c.d_ff;
+    blk->qd = c.n_heads * dh;
+    blk->kvd = nkv * dh;
+    blk->nqkv = blk->qd + 2 * blk->kvd;
+    const size_t T = (size_t)c.max_tokens;
+    const Elem op = blk->op, dt = blk->dt;
+    const size_t eo = esz(op);
+
+    bool ok = dalloc(blk, &blk->w_qkv, (size_t)blk->nqkv * d * eo) &&
+              dalloc(blk, &blk->w_o, (size_t)d * blk->qd * eo) &&
+              dalloc(blk, &blk->w_gu, (size_t)2 * dff * d * eo) &&
+              dalloc(blk, &blk->w_down, (size_t)d * dff * eo) && dalloc(blk, &blk->g1, (size_t)d * 4) &&
+              dalloc(blk, &blk->g2, (size_t)d * 4) &&
+              dalloc(blk, &blk->rope, (size_t)c.max_seq_len * (dh / 2) * sizeof(float2)) &&
+              dalloc(blk, &blk->n1, T * d * eo) && dalloc(blk, &blk->n2, T * d * eo) &&
+              dalloc(blk, &blk->q, T * blk->qd * eo) && dalloc(blk, &blk->o, T * blk->qd * eo) &&
+              dalloc(blk, &blk->z, T * dff * eo) && dalloc(blk, &blk->h, T * d * 4);
+    if (ok && dt == Elem::BF16) {
+        // prefill from position 0 keeps k and v^T in the operand type with the
+        // sequence stride rounded up to 8: B * round8(S) <= T + 7 * T / 2 rows.
+        blk->ws_rows = T + 7 * (T / 2) + 8;
+        ok = dalloc(blk, &blk->kws, blk->ws_rows * blk->kvd * eo) &&
+             dalloc(blk, &blk->vws, blk->ws_rows * blk->kvd * eo) &&
+             dalloc(blk, &blk->part,
+                    lb::decode_partials_floats(c.max_tokens, c.n_heads, dh, c.max_seq_len) * sizeof(float));
+    }
+    if (!ok) {
+        free_all(blk);
+        delete blk;
+        return fail(nullptr, LB_ERR_OOM, "device allocation failed");
+    }
+
+    // RoPE table: (cos, sin) of pos * theta^(-2i/d_head), angles in fp64
+    // ("The Evolving Transformer 04 LLaMA", 02 RoPE).
+    std::vector<float2> table((size_t)c.max_seq_len * (dh / 2));
+    for (int i = 0; i < dh / 2; ++i) {
+        const double freq = std::pow(c.rope_theta, -2.0 * (double)i / (double)dh);
+        for (long pos = 0; pos < c.max_seq_len; ++pos) {
+            const double a = (double)pos * freq;
+            table[(size_t)pos * (dh / 2) + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+        }
+    }
+
+    hipStream_t s = nullptr;
+    hipError_t e = hipStreamCreate(&s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(blk->rope, table.data(), table.size() * sizeof(float2), hipMemcpyHostToDevice, s);
+    const size_t eo_row = (size_t)d * eo;
+    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wq, blk->w_qkv, (size_t)blk->qd * d, s);
+    if (e == hipSuccess)
+        e = lb::launch_convert(dt, op, w->wk, (char*)blk->w_qkv + (size_t)blk->qd * eo_row, (size_t)blk->kvd * d, s);
+    if (e == hipSuccess)
+        e = lb::launch_convert(dt, op, w->wv, (char*)blk->w_qkv + (size_t)(blk->qd + blk->kvd) * eo_row,
+                               (size_t)blk->kvd * d, s);
+    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wo, blk->w_o, (size_t)d * blk->qd, s);
+    if (e == hipSuccess) e = lb::launch_pack_gate_up(dt, op, w->w_gate, w->w_up, blk->w_gu, dff, d, s);
+    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->w_down, blk->w_down, (size_t)d * dff, s);
+    if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->attn_norm, blk->g1, (size_t)d, s);
+    if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->ffn_norm, blk->g2, (size_t)d, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (s) hipStreamDestroy(s);
+    if (e != hipSuccess) {
+        const char* msg = hipGetErrorString(e);
+        free_all(blk);
+        delete blk;
+        return fail(nullptr, LB_ERR_HIP, "weight packing failed: %s", msg);
+    }
+    *out = blk;
+    return LB_OK;
+}
+
+extern "C" void llama_block_destroy(lb_block* blk) {
+    if (!blk) return;
+    int cur = 0;
+    hipGetDevice(&cur);
+    hipSetDevice(blk->dev);
+    hipDeviceSynchronize();
+    profile_release(blk);
+    free_all(blk);
+    hipSetDevice(cur);
+    delete blk;
+}
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = (const char*)a;
+    const char* pb = (const char*)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int start_pos,
+                             const lb_kv_cache* kv, void* out, hipStream_t s) {
+    const lb_config& c = blk->cfg;
+    const int M = B * S, d = c.d_model, dh = c.d_head, nkv = c.n_kv_heads, dff = c.d_ff;
+    const int cap = kv->max_seq_len;
+    const Elem op = blk->op, dt = blk->dt;
+    hipError_t e;
+    hipEvent_t* ev = nullptr;
+    if (blk->profiling) {
+        const int slot = blk->next_slot;
+        for (size_t i = 0; i < blk->pending.size(); ++i) {
+            if (blk->pending[i] == slot) {  // ring full: fold the oldest use of this slot in first
+                e = profile_collect(blk, slot);
+                if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "profiling: %s", hipGetErrorString(e));
+                blk->pending.erase(blk->pending.begin() + i);
+                break;
+            }
+        }
+        ev = &blk->events[(size_t)slot * (LB_NUM_STAGES + 1)];
+        blk->pending.push_back(slot);
+        blk->next_slot = (slot + 1) % kProfileSlots;
+    }
+    auto mark = [&](int i) { if (ev) hipEventRecord(ev[i], s); };
+
+    mark(0);
+    e = lb::launch_rmsnorm(dt, op, x, blk->g1, blk->n1, M, d, (float)c.norm_eps, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_1: %s", hipGetErrorString(e));
+
+    const bool ws_kv = (dt == Elem::BF16) && S > 1 && start_pos == 0;
+    const int s_stride = (S + 7) & ~7;
+    lb::QkvEpi qe;
+    qe.q = blk->q;
+    qe.kws = ws_kv ? blk->kws : nullptr;
+    qe.vws = ws_kv ? blk->vws : nullptr;
+    qe.kc = kv->k;
+    qe.vc = kv->v;
+    qe.rope = blk->rope;
+    qe.S = S;
+    qe.start_pos = start_pos;
+    qe.cap = cap;
+    qe.s_stride = s_stride;
+    qe.nkv = nkv;
+    qe.dh = dh;
+    qe.qd = blk->qd;
+    mark(1);
+    e = lb::gemm_qkv(op, dt, blk->n1, blk->w_qkv, M, blk->nqkv, d, qe, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "qkv projection: %s", hipGetErrorString(e));
+
+    lb::AttnArgs a;
+    a.q = blk->q;
+    a.o = blk->o;
+    a.B = B;
+    a.S = S;
+    a.start_pos = start_pos;
+    a.H = c.n_heads;
+    a.nkv = nkv;
+    a.dh = dh;
+    if (ws_kv) {
+        a.k = blk->kws;
+        a.v = blk->vws;
+        a.k_bg = (long)s_stride * dh;
+        a.v_bg = (long)dh * s_stride;
+        a.t_stride = s_stride;
+    } else {
+        a.k = kv->k;
+        a.v = kv->v;
+        a.k_bg = (long)cap * dh;
+        a.v_bg = (long)dh * cap;
+        a.t_stride = cap;
+    }
+    mark(2);
+    if (dt == Elem::F32) e = lb::attn_simple(a, s);
+    else if (S == 1) e = lb::attn_decode(op, dt, a, blk->part, s);
+    else e = lb::attn_prefill(op, ws_kv ? op : dt, a, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "attention: %s", hipGetErrorString(e));
+
+    mark(3);
+    e = lb::gemm_resid(op, dt, blk->o, blk->w_o, M, d, blk->qd, x, blk->h, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "o projection: %s", hipGetErrorString(e));
+    mark(4);
+    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, blk->g2, blk->n2, M, d, (float)c.norm_eps, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_2: %s", hipGetErrorString(e));
+    mark(5);
+    e = lb::gemm_swiglu(op, blk->n2, blk->w_gu, M, 2 * dff, d, blk->z, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "gate/up projection: %s", hipGetErrorString(e));
+    mark(6);
+    e = lb::gemm_out(op, dt, blk->z, blk->w_down, M, d, dff, blk->h, out, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "down projection: %s", hipGetErrorString(e));
+    mark(7);
+    return LB_OK;
+}
+
+extern "C" lb_status llama_block_forward(lb_block* blk, const void* x, int32_t batch, int32_t seq_len,
+                                         int32_t start_pos, const lb_kv_cache* kv, void* out,
+                                         void* stream) {
+    if (!blk) return LB_ERR_INVALID_ARG;
+    blk->err.clear();
+    const lb_config& c = blk->cfg;
+    if (!x || !out || !kv || !kv->k || !kv->v)
+        return fail(blk, LB_ERR_INVALID_ARG, "x, out, kv, kv->k and kv->v must be non-NULL");
+    if (batch < 1 || seq_len < 1)
+        return fail(blk, LB_ERR_INVALID_ARG, "batch (%d) and seq_len (%d) must be >= 1", batch, seq_len);
+    if ((long)batch * seq_len > c.max_tokens)
+        return fail(blk, LB_ERR_INVALID_ARG, "batch*seq_len (%ld) exceeds max_tokens (%d)",
+                    (long)batch * seq_len, c.max_tokens);
+    if (start_pos < 0) return fail(blk, LB_ERR_INVALID_ARG, "start_pos (%d) < 0", start_pos);
+    if ((long)start_pos + seq_len > c.max_seq_len || (long)start_pos + seq_len > kv->max_seq_len)
+        return fail(blk, LB_ERR_INVALID_ARG,
+                    "start_pos+seq_len (%ld) exceeds max_seq_len (config %d, cache %d)",
+                    (long)start_pos + seq_len, c.max_seq_len, kv->max_seq_len);
+    if (batch > kv->batch)
+        return fail(blk, LB_ERR_INVALID_ARG, "batch (%d) exceeds the cache's batch (%d)", batch, kv->batch);
+    if (blk->dt == Elem::BF16 && kv->max_seq_len % 8 != 0)
+        return fail(blk, LB_ERR_UNSUPPORTED, "bf16 caches need max_seq_len % 8 == 0 (got %d)", kv->max_seq_len);
+    const size_t act = (size_t)batch * seq_len * c.d_model * esz(blk->dt);
+    if (overlap(x, act, out, act)) return fail(blk, LB_ERR_INVALID_ARG, "out overlaps x");
+
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(blk, LB_ERR_HIP, "hipGetDevice failed");
+    if (cur != blk->dev) hipSetDevice(blk->dev);
+    lb_status st = run_forward(blk, x, batch, seq_len, start_pos, kv, out, (hipStream_t)stream);
+    if (cur != blk->dev) hipSetDevice(cur);
+    return st;
+}
+
+static bool stage_buffer(const lb_block* blk, lb_stage which, const void** ptr, Elem* elem, int64_t* cols) {
+    const lb_config& c = blk->cfg;
+    switch (which) {
+        case LB_STAGE_N1: *ptr = blk->n1; *elem = blk->op; *cols = c.d_model; return true;
+        case LB_STAGE_Q: *ptr = blk->q; *elem = blk->op; *cols = blk->qd; return true;
+        case LB_STAGE_O: *ptr = blk->o; *elem = blk->op; *cols = blk->qd; return true;
+        case LB_STAGE_H: *ptr = blk->h; *elem = Elem::F32; *cols = c.d_model; return true;
+        case LB_STAGE_N2: *ptr = blk->n2; *elem = blk->op; *cols = c.d_model; return true;
+        case LB_STAGE_Z: *ptr = blk->z; *elem = blk->op; *cols = c.d_ff; return true;
+    }
+    return false;
+}
+
+static lb_elem to_abi(Elem e) {
+    return e == Elem::F32 ? LB_ELEM_F32 : (e == Elem::BF16 ? LB_ELEM_BF16 : LB_ELEM_F16);
+}
+
+extern "C" lb_status llama_block_stage_info(const lb_block* blk, lb_stage which, lb_elem* elem, int64_t* cols) {
+    if (!blk || !elem || !cols) return LB_ERR_INVALID_ARG;
+    const void* p;
+    Elem e;
+    if (!stage_buffer(blk, which, &p, &e, cols)) return LB_ERR_INVALID_ARG;
+    *elem = to_abi(e);
+    return LB_OK;
+}
+
+extern "C" lb_status llama_block_copy_stage(lb_block* blk, lb_stage which, void* dst, size_t bytes, void* stream) {
+    if (!blk) return LB_ERR_INVALID_ARG;
+    const void* p;
+    Elem e;
+    int64_t cols;
+    if (!dst || !stage_buffer(blk, which, &p, &e, &cols))
+        return fail(blk, LB_ERR_INVALID_ARG, "bad stage or NULL destination");
+    const size_t cap = (size_t)blk->cfg.max_tokens * (size_t)cols * esz(e);
+    if (bytes > cap) return fail(blk, LB_ERR_INVALID_ARG, "%zu bytes exceed the stage buffer (%zu)", bytes, cap);
+    hipError_t err = hipMemcpyAsync(dst, p, bytes, hipMemcpyDefault, (hipStream_t)stream);
+    if (err != hipSuccess) return fail(blk, LB_ERR_HIP, "copy_stage: %s", hipGetErrorString(err));
+    return LB_OK;
+}
+
+extern "C" lb_status llama_block_profile(lb_block* blk, int enable) {
+    if (!blk) return LB_ERR_INVALID_ARG;
+    profile_release(blk);
+    for (double& v : blk->stage_ms) v = 0.0;
+    blk->profiled_calls = 0;
+    blk->next_slot = 0;
+    if (!enable) return LB_OK;
+    blk->events.resize((size_t)kProfileSlots * (LB_NUM_STAGES + 1));
+    for (size_t i = 0; i < blk->events.size(); ++i) {
+        if (hipEventCreate(&blk->events[i]) != hipSuccess) {
+            blk->events.resize(i);
+            profile_release(blk);
+            return fail(blk, LB_ERR_HIP, "hipEventCreate failed");
+        }
+    }
+    blk->profiling = true;
+    return LB_OK;
+}
+
+extern "C" lb_status llama_block_profile_read(lb_block* blk, double* stage_ms, int n, int64_t* calls) {
+    if (!blk || !stage_ms || !calls || n < 0 || n > LB_NUM_STAGES) return LB_ERR_INVALID_ARG;
+    for (int slot : blk->pending) {
+        hipError_t e = profile_collect(blk, slot);
+        if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "profiling: %s", hipGetErrorString(e));
+    }
+    blk->pending.clear();
+    for (int i = 0; i < n; ++i) stage_ms[i] = blk->stage_ms[i];
+    *calls = blk->profiled_calls;
+    return LB_OK;
+}

@@ -1,0 +1,167 @@
+/*
+ * llama_block.h -- C ABI of a gfx950 (MI355X) library that runs the forward
+ * pass of one Llama pre-norm decoder block:
+ *
+ *     h = x + Attn(RMSNorm_1(x)),     y = h + FFN(RMSNorm_2(h))
+ *
+ * ("Full Llama 3 transformer block", How it works; "The Evolving Transformer
+ *  04 LLaMA", 06 BLOCK).  Attn = bias-free q/k/v projections, RoPE on q and k
+ * (interleaved pairs (2i, 2i+1) turned by (start_pos+s) * theta^(-2i/d_head),
+ * "The Evolving Transformer 04 LLaMA", 02 RoPE), a KV-cache write at start_pos
+ * ("Full Llama 3 transformer block", How it works), causal grouped-query
+ * attention in which query head h reads KV head floor(h / (n_heads/n_kv_heads))
+ * ("The Evolving Transformer 04 LLaMA", 05 GQA), and the output projection.
+ * FFN = down(SiLU(gate n) * up n) ("The Evolving Transformer 04 LLaMA",
+ * 04 SWIGLU).  RMSNorm: v / sqrt(mean(v^2) + eps) * g (same page, 03 RMSNORM).
+ *
+ * Conventions
+ *  - Every tensor pointer passed to init/forward is a DEVICE pointer (HIP
+ *    device memory of the current device), row-major and densely packed.
+ *  - Weights use the nn.Linear convention, weight[out][in]:
+ *      wq [n_heads*d_head][d_model]   wk, wv [n_kv_heads*d_head][d_model]
+ *      wo [d_model][n_heads*d_head]   w_gate, w_up [d_ff][d_model]
+ *      w_down [d_model][d_ff]         attn_norm, ffn_norm [d_model]
+ *    Head h owns rows/columns [h*d_head, (h+1)*d_head).
+ *  - Activations x and out: [batch][seq_len][d_model].
+ *  - Element type of x, out, the weights and the cache: cfg.dtype (fp32 or
+ *    bf16).  Internally bf16 blocks run their matrix products with fp16 (or,
+ *    on request, bf16) MFMA operands and fp32 accumulation; the residual
+ *    stream h is kept in fp32.
+ *  - Errors: every function validates its arguments before touching device
+ *    memory; on any error nothing is launched and nothing is written.  The
+ *    text of the last error of a handle is available from
+ *    llama_block_last_error().
+ */
+#ifndef LLAMA_BLOCK_H
+#define LLAMA_BLOCK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LB_F32 = 0, LB_BF16 = 1 } lb_dtype;
+
+/* Operand type of the matrix-core products for bf16 blocks (ignored for fp32
+ * blocks, which run in fp32 throughout).  AUTO = F16: bf16 weights are widened
+ * to fp16 at init and activations are rounded to fp16, three more mantissa
+ * bits than bf16 at the same MFMA rate.  BF16 keeps every operand in bf16. */
+typedef enum { LB_OPERANDS_AUTO = 0, LB_OPERANDS_F16 = 1, LB_OPERANDS_BF16 = 2 } lb_operands;
+
+typedef enum {
+    LB_OK = 0,
+    LB_ERR_INVALID_ARG = 1,  /* a pointer, size or config value is invalid */
+    LB_ERR_UNSUPPORTED = 2,  /* valid, but a shape this build does not run */
+    LB_ERR_OOM = 3,          /* device allocation failed */
+    LB_ERR_HIP = 4           /* a HIP runtime call failed */
+} lb_status;
+
+typedef struct {
+    int32_t d_model;      /* model width; must equal n_heads * d_head */
+    int32_t n_heads;      /* query heads H */
+    int32_t n_kv_heads;   /* key/value heads; must divide n_heads */
+    int32_t d_head;       /* head width; even */
+    int32_t d_ff;         /* SwiGLU inner width */
+    int32_t max_tokens;   /* largest batch*seq_len of one forward (sizes the workspace) */
+    int32_t max_seq_len;  /* RoPE table rows: every start_pos+seq_len must be <= this */
+    double rope_theta;    /* rotation base theta (> 0) */
+    double norm_eps;      /* RMSNorm epsilon (> 0), added to mean(v^2) inside the root */
+    lb_dtype dtype;
+    lb_operands operands;
+} lb_config;
+
+/* Device pointers in cfg.dtype, layouts as above.  init copies (and repacks)
+ * them into library-owned memory: the caller may free them once init returns. */
+typedef struct {
+    const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} lb_weights;
+
+/* KV cache, caller-owned device memory in cfg.dtype:
+ *   k: [batch][n_kv_heads][max_seq_len][d_head]   one row per position
+ *   v: [batch][n_kv_heads][d_head][max_seq_len]   TRANSPOSED: one row per
+ *      head dimension, so that the decode kernels read V along positions
+ *      with full-width loads.
+ * A forward with start_pos p and seq_len S reads positions [0, p) of
+ * sequences 0..B-1 and writes positions [p, p+S); no other entry changes.
+ * The "Llama 4 From Scratch" worked example counts 2*n_kv*d_head values per
+ * token per layer: exactly what one token adds here. */
+typedef struct {
+    void* k;
+    void* v;
+    int32_t batch;        /* sequences the cache holds (>= forward batch) */
+    int32_t max_seq_len;  /* positions per sequence */
+} lb_kv_cache;
+
+typedef struct lb_block lb_block;
+
+/* Create a block on the current HIP device.  Validates cfg: d_model ==
+ * n_heads*d_head, n_heads % n_kv_heads == 0, d_head even, d_ff, max_tokens,
+ * max_seq_len, rope_theta, norm_eps > 0 (LB_ERR_INVALID_ARG); bf16 blocks
+ * need d_head in {64, 128}, d_model % 64 == 0 and d_ff % 64 == 0, fp32
+ * blocks d_head <= 256 (else LB_ERR_UNSUPPORTED).  Packs the weights, builds
+ * the RoPE cos/sin table (angles in fp64, stored as fp32) and allocates the
+ * workspace.  Synchronous.  *out receives the handle (NULL on error). */
+lb_status llama_block_init(const lb_config* cfg, const lb_weights* weights, lb_block** out);
+
+/* One forward pass, enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and asynchronous to the host.
+ *   x   [batch][seq_len][d_model], device, cfg.dtype
+ *   out [batch][seq_len][d_model], device, cfg.dtype; must not overlap x
+ * seq_len == 1 runs the decode kernels, seq_len > 1 the prefill kernels; one
+ * start_pos applies to every sequence.  Checks: batch, seq_len >= 1,
+ * batch*seq_len <= max_tokens, start_pos >= 0, start_pos+seq_len <=
+ * min(cfg.max_seq_len, kv->max_seq_len), batch <= kv->batch, non-null
+ * pointers (LB_ERR_INVALID_ARG).  One call per handle may be in flight: the
+ * workspace is shared by every call on the handle. */
+lb_status llama_block_forward(lb_block* blk, const void* x, int32_t batch, int32_t seq_len,
+                              int32_t start_pos, const lb_kv_cache* kv, void* out,
+                              void* stream);
+
+/* Free the handle and everything it owns (synchronises the device first). */
+void llama_block_destroy(lb_block* blk);
+
+/* Static text for a status code. */
+const char* llama_block_status_string(lb_status s);
+
+/* Text of the last error recorded on this handle ("" if none); with a NULL
+ * handle, the last error of a failed llama_block_init on this thread. */
+const char* llama_block_last_error(const lb_block* blk);
+
+/* Intermediates of the last forward, for stage-by-stage checks.  They live in
+ * the workspace, are valid until the next forward on the handle, and are
+ * [batch*seq_len][cols] row-major:
+ *   N1 RMSNorm_1(x) [d_model]     Q q after RoPE [n_heads*d_head]
+ *   O attention output [n_heads*d_head]   H residual h, always fp32 [d_model]
+ *   N2 RMSNorm_2(h) [d_model]     Z SiLU(gate)*up [d_ff]
+ * Element type: fp32 for fp32 blocks and for H; otherwise the operand type. */
+typedef enum { LB_STAGE_N1 = 0, LB_STAGE_Q = 1, LB_STAGE_O = 2, LB_STAGE_H = 3,
+               LB_STAGE_N2 = 4, LB_STAGE_Z = 5 } lb_stage;
+typedef enum { LB_ELEM_F32 = 0, LB_ELEM_BF16 = 1, LB_ELEM_F16 = 2 } lb_elem;
+
+/* Describe a stage buffer: element type and columns per token row. */
+lb_status llama_block_stage_info(const lb_block* blk, lb_stage which, lb_elem* elem,
+                                 int64_t* cols);
+
+/* Copy `bytes` bytes from the start of a stage buffer to dst (device or host
+ * memory), ordered on `stream`.  bytes must not exceed the buffer. */
+lb_status llama_block_copy_stage(lb_block* blk, lb_stage which, void* dst, size_t bytes,
+                                 void* stream);
+
+/* Per-stage GPU timing.  While enabled, each forward records HIP events on
+ * its stream between its stages:
+ *   0 RMSNorm_1   1 q/k/v projection (+RoPE, cache append)   2 attention
+ *   3 o projection (+x)   4 RMSNorm_2   5 gate/up (+SiLU*up)   6 down (+h)
+ * llama_block_profile(blk, 1) resets the sums and starts recording; 0 stops.
+ * llama_block_profile_read waits for the recorded events and returns the
+ * summed milliseconds per stage in stage_ms[0..n) (n <= LB_NUM_STAGES) and
+ * the number of profiled forwards in *calls. */
+#define LB_NUM_STAGES 7
+lb_status llama_block_profile(lb_block* blk, int enable);
+lb_status llama_block_profile_read(lb_block* blk, double* stage_ms, int n, int64_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLAMA_BLOCK_H */

@@ -61,6 +61,8 @@ def lib():
                                         ctypes.POINTER(ctypes.c_int), ctypes.c_int,
                                         ctypes.POINTER(_Stages)]
         L.orc_block_forward.restype = ctypes.c_int
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -74,6 +76,10 @@ def _f64(a) -> np.ndarray:
     if hasattr(a, "detach"):  # torch tensor
         a = a.detach().to("cpu").double().numpy()
     return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
 
 
 # ---- single steps -------------------------------------------------------------------

@@ -32,8 +32,15 @@
 #include "oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Host threads the oracle's parallel loops use (reported with its timings). */
+int orc_num_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* [LL 03 RMSNORM; L3 How it works; ML RMS normalization]:
  * out_k = v_k / sqrt(mean_j v_j^2 + eps) * g_k  -- no centring, no bias,

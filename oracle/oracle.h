@@ -39,6 +39,8 @@ typedef struct {
     double *n1, *q, *k, *v, *o, *h, *n2, *z;
 } orc_stages;
 
+int orc_num_threads(void);
+
 /* Single steps, exposed so tests can pin each one on its own. */
 void orc_rms_norm(const double* v, const double* g, int d, double eps, double* out);
 void orc_linear(const double* in, const double* w, int n_out, int n_in, double* out);
