@@ -1,9 +1,11 @@
 // GEMM kernels: C[M][N] = A[M][K] . W[N][K]^T with fp32 accumulation, results
 // handed to an epilogue (epilogues.h) in 8-column chunks.
 //
-//  gemm_mfma_kernel   prefill: 32x32x16 MFMA tiles, LDS double buffering
-//  gemm_skinny_kernel decode (M <= 64): 16x16x32 MFMA, split-K over waves,
-//                     weights streamed from HBM straight into MFMA operands
+//  gemm_mfma_kernel   prefill: 32x32x16 MFMA tiles, direct-to-LDS loads,
+//                     LDS double buffering
+//  gemm_skinny_kernel decode (M <= 64): 16x16x32 MFMA, split-K over waves
+//                     and blocks, weights streamed from HBM straight into
+//                     MFMA operands (+ reduce_epilogue_kernel)
 //  gemm_simple_kernel fp32 blocks: plain LDS-tiled fp32 FMA
 #pragma once
 
@@ -12,27 +14,34 @@
 namespace lb {
 
 // ------------------------------------------------------------------------------------
-// Prefill GEMM.  Block tile BM x BN x 64, 256 threads = 4 wavefronts in a
-// (BM/WM) x (BN/WN) grid, each computing WM x WN with (WM/32)*(WN/32)
-// accumulator tiles.  A and W tiles live in LDS as [rows][64] with the 16-byte
-// chunk index XORed by (row & 7): the 8 lanes of one ds_read_b128 phase read
-// 8 different rows at one logical chunk and hit 8 different bank groups.
-// One barrier per K step: global loads for step k+1 are issued before the
-// MFMAs of step k and written to the other LDS buffer after them.
-// Rows of A beyond M and of W beyond N are clamped to the last valid row (they
-// only feed outputs that the epilogue discards).  K % 64 == 0.
+// Prefill GEMM.  Block tile BM x BN x 64, NW wavefronts in a (BM/WM) x (BN/WN)
+// grid, each computing WM x WN with (WM/32)*(WN/32) accumulator tiles.
+// A and W tiles live in LDS as [rows][64] with the 16-byte chunk index XORed
+// by (row & 7): the 8 lanes of one ds_read_b128 phase read 8 different rows
+// at one logical chunk and hit 8 different bank groups.  Tiles are fetched
+// straight from global memory into LDS (global_load_lds_dwordx4, no VGPR
+// staging): instruction i of wavefront w fills the 64 consecutive 16-byte
+// LDS slots starting at (i*NW + w)*64, lane l the slot l, so every lane loads
+// the global chunk whose swizzled home is that slot.  Two LDS stages: the
+// loads for step k+1 are issued before the MFMAs of step k; one barrier per
+// step.  Rows of A beyond M and of W beyond N are clamped to the last valid
+// row (they only feed outputs that the epilogue discards).  K % 64 == 0.
 // ------------------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WM, int WN, class Epi>
-__global__ void __launch_bounds__(256) gemm_mfma_kernel(const T* __restrict__ A,
-                                                        const T* __restrict__ W, int M, int N,
-                                                        int K, Epi epi) {
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi>
+__global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict__ A,
+                                                            const T* __restrict__ W, int M, int N,
+                                                            int K, Epi epi) {
     typedef typename vec8<T>::type V8;
+    constexpr int NT = NW * 64;
     constexpr int BK = 64;
     constexpr int NWN = BN / WN;
-    static_assert((BM / WM) * NWN == 4, "4 wavefronts per block");
+    static_assert((BM / WM) * NWN == NW, "wavefront grid covers the tile");
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int ACH = BM * BK / 8 / 256;  // 16-byte chunks per thread and stage
-    constexpr int BCH = BN * BK / 8 / 256;
+    constexpr int ACH = BM * BK / 8 / NT;   // direct-load instructions per thread and stage
+    constexpr int BCH = BN * BK / 8 / NT;
+    static_assert(ACH * NT * 8 == BM * BK && BCH * NT * 8 == BN * BK, "whole instructions");
     constexpr int EPR = 64;                 // epilogue rows per pass
     constexpr int CPAD = BN + 8;            // fp32 row pitch of the epilogue stage
     static_assert(EPR * CPAD * 4 <= 2 * (BM + BN) * BK * (int)sizeof(T), "epilogue stage fits");
@@ -57,38 +66,29 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const T* __restrict__ A,
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
 
-    u32x4 ra[ACH], rb[BCH];
     const T* abase[ACH];
     const T* bbase[BCH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int c = tid + i * 256, row = c >> 3, kc = c & 7;
-        abase[i] = A + (size_t)min(m0 + row, M - 1) * K + kc * 8;
+        const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ (row & 7);
+        abase[i] = A + (size_t)min(m0 + row, M - 1) * K + c * 8;
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-        const int c = tid + i * 256, row = c >> 3, kc = c & 7;
-        bbase[i] = W + (size_t)min(n0 + row, N - 1) * K + kc * 8;
+        const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ (row & 7);
+        bbase[i] = W + (size_t)min(n0 + row, N - 1) * K + c * 8;
     }
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(abase[i] + k0);
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bbase[i] + k0);
-    };
-    auto lstore = [&](int buf) {
+    auto gload = [&](int k0, int buf) {
         T* la = lds + buf * (BM + BN) * BK;
         T* lb = la + BM * BK;
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int c = tid + i * 256, row = c >> 3, kc = c & 7;
-            *reinterpret_cast<u32x4*>(la + row * BK + ((kc ^ (row & 7)) << 3)) = ra[i];
-        }
+        for (int i = 0; i < ACH; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(abase[i] + k0),
+                                             (lds_ptr_t)(la + (i * NW + wave) * 64 * 8), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + i * 256, row = c >> 3, kc = c & 7;
-            *reinterpret_cast<u32x4*>(lb + row * BK + ((kc ^ (row & 7)) << 3)) = rb[i];
-        }
+        for (int i = 0; i < BCH; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + k0),
+                                             (lds_ptr_t)(lb + (i * NW + wave) * 64 * 8), 16, 0, 0);
     };
 
     f32x16 acc[TM][TN];
@@ -100,12 +100,11 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const T* __restrict__ A,
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const int nk = K / BK;
-    gload(0);
-    lstore(0);
+    gload(0, 0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+        if (kt + 1 < nk) gload((kt + 1) * BK, buf ^ 1);
         const T* la = lds + buf * (BM + BN) * BK;
         const T* lb = la + BM * BK;
 #pragma unroll
@@ -127,7 +126,8 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const T* __restrict__ A,
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
-        if (kt + 1 < nk) lstore(buf ^ 1);
+        // the barrier waits for this wavefront's loads of step k+1 (vmcnt) and
+        // for every wavefront to finish reading stage k
         __syncthreads();
     }
 
@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const T* __restrict__ A,
             }
         }
         __syncthreads();
-        for (int c = tid; c < EPR * (BN / 8); c += 256) {
+        for (int c = tid; c < EPR * (BN / 8); c += NT) {
             const int row = c / (BN / 8), c8 = c % (BN / 8);
             const int m = m0 + p * EPR + row, n = n0 + c8 * 8;
             if (m < M && n < N) {
@@ -169,71 +169,124 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const T* __restrict__ A,
 }
 
 // ------------------------------------------------------------------------------------
-// Decode GEMM for M <= 16*MT token rows.  One block owns 16 output columns;
-// its KW wavefronts split K (k-steps of 32 dealt round-robin), each keeping
-// U k-steps of weight loads in flight.  Per k-step a lane loads 16 bytes of
-// one weight row (the MFMA B operand) and 16 bytes of each token tile (A, hot
-// in L2).  Partial sums meet in LDS in a fixed order (deterministic).
+// Decode GEMM for M <= 16*MT token rows: a weight-streaming kernel.  Grid
+// (N / (16*CT), KS), KW wavefronts per block.  Every wavefront owns the block's
+// 16*CT output columns (CT 16x16x32 MFMA column tiles) and a share of K: k-steps
+// of 32 are dealt round-robin over the KS blocks and their wavefronts, U steps
+// per chunk, two chunks in flight (register double buffering).  Per k-step a
+// lane loads 16 bytes of each of its CT weight rows (MFMA B operands) straight
+// from HBM and 16 bytes of each token tile (A, hot in L2); CT column tiles per
+// A load keep the activation re-reads at 2*MT/CT of the weight traffic.  The
+// block sums its wavefronts in LDS in a fixed order; with KS == 1 it runs the
+// epilogue, otherwise it stores an fp32 partial [ks][M][N] and
+// reduce_epilogue_kernel adds the KS partials in order (deterministic).
 // K % 32 == 0.
 // ------------------------------------------------------------------------------------
-template <typename T, int MT, int KW, class Epi>
+template <typename T, int MT, int KW, int U, int CT, bool PARTIAL, class Epi>
 __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restrict__ A,
                                                               const T* __restrict__ W, int M,
-                                                              int N, int K, Epi epi) {
+                                                              int N, int K, int KS,
+                                                              float* __restrict__ part, Epi epi) {
     typedef typename vec8<T>::type V8;
-    constexpr int U = 8;
-    __shared__ float red[KW][MT][16][17];
+    constexpr int COLS = 16 * CT;
+    __shared__ float red[KW][MT * 16][COLS + 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * COLS, ks = blockIdx.y;
     const int nks = K / 32;
-    const T* wp = W + (size_t)min(n0 + (lane & 15), N - 1) * K + 8 * (lane >> 4);
+    const int stride = KS * KW;
+    const int first = ks + KS * wave;
+    const int n_my = first < nks ? (nks - first + stride - 1) / stride : 0;
+    const int nchunk = (n_my + U - 1) / U;
+    const T* wp[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+        wp[c] = W + (size_t)min(n0 + 16 * c + (lane & 15), N - 1) * K + 8 * (lane >> 4);
     const T* ap[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) ap[t] = A + (size_t)min(t * 16 + (lane & 15), M - 1) * K + 8 * (lane >> 4);
-
-    f32x4 acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int ks0 = wave; ks0 < nks; ks0 += KW * U) {
-        V8 bw[U], aa[U][MT];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ks = ks0 + u * KW;
-            if (ks < nks) {
-                bw[u] = *reinterpret_cast<const V8*>(wp + ks * 32);
-#pragma unroll
-                for (int t = 0; t < MT; ++t) aa[u][t] = *reinterpret_cast<const V8*>(ap[t] + ks * 32);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ks = ks0 + u * KW;
-            if (ks < nks) {
-#pragma unroll
-                for (int t = 0; t < MT; ++t) acc[t] = mfma16(aa[u][t], bw[u], acc[t]);
-            }
-        }
-    }
+    f32x4 acc[MT][CT];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][t][4 * (lane >> 4) + r][lane & 15] = acc[t][r];
+        for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    V8 bw[2][U][CT], aa[2][U][MT];
+    // steps past this wavefront's share load a clamped (valid) address and
+    // contribute nothing: their A operand is zeroed
+    auto load = [&](int chunk, int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kstep = min(first + (chunk * U + u) * stride, nks - 1);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) bw[s][u][c] = *reinterpret_cast<const V8*>(wp[c] + kstep * 32);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) aa[s][u][t] = *reinterpret_cast<const V8*>(ap[t] + kstep * 32);
+        }
+    };
+    auto compute = [&](int chunk, int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = chunk * U + u < n_my;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                V8 a = aa[s][u][t];
+                if (!ok) a = V8{};
+#pragma unroll
+                for (int c = 0; c < CT; ++c) acc[t][c] = mfma16(a, bw[s][u][c], acc[t][c]);
+            }
+        }
+    };
+    if (nchunk > 0) load(0, 0);
+    int c = 0;
+    for (; c + 1 < nchunk; c += 2) {
+        load(c + 1, 1);
+        compute(c, 0);
+        if (c + 2 < nchunk) load(c + 2, 0);
+        compute(c + 1, 1);
+    }
+    if (c < nchunk) compute(c, 0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[wave][t * 16 + 4 * (lane >> 4) + r][cc * 16 + (lane & 15)] = acc[t][cc][r];
     __syncthreads();
-    for (int c = threadIdx.x; c < MT * 16 * 2; c += KW * 64) {
-        const int row = c >> 1, half = c & 1;
-        const int n = n0 + half * 8;
+    for (int q = threadIdx.x; q < MT * 16 * (COLS / 8); q += KW * 64) {
+        const int row = q / (COLS / 8), c8 = q % (COLS / 8);
+        const int n = n0 + c8 * 8;
         if (row < M && n < N) {
             float v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float s = 0.0f;
-                for (int w = 0; w < KW; ++w) s += red[w][row >> 4][row & 15][half * 8 + e];
-                v[e] = s;
+                float sacc = 0.0f;
+                for (int w = 0; w < KW; ++w) sacc += red[w][row][c8 * 8 + e];
+                v[e] = sacc;
             }
-            epi.row8(row, n, v);
+            if (PARTIAL) store8(part + ((size_t)ks * M + row) * N + n, v);
+            else epi.row8(row, n, v);
         }
     }
+}
+
+// Sum the KS fp32 partials of a split-K decode GEMM (in split order) and run
+// the epilogue: one thread per 8-column chunk.
+template <class Epi>
+__global__ void __launch_bounds__(256) reduce_epilogue_kernel(const float* __restrict__ part, int M,
+                                                              int N, int KS, Epi epi) {
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    const int n8 = N / 8;
+    if (q >= M * n8) return;
+    const int row = q / n8, n = (q % n8) * 8;
+    float v[8];
+    load8(part + (size_t)row * N + n, v);
+    for (int k = 1; k < KS; ++k) {
+        float w[8];
+        load8(part + ((size_t)k * M + row) * N + n, w);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += w[e];
+    }
+    epi.row8(row, n, v);
 }
 
 // ------------------------------------------------------------------------------------

@@ -14,6 +14,8 @@
 
 namespace lb {
 
+constexpr int kDecodeMaxSplit = 256;  // decode blocks per (sequence, KV group)
+
 template <typename T, typename S> __device__ __forceinline__ u32x4 to_operand(const u32x4& raw);
 template <> __device__ __forceinline__ u32x4 to_operand<f16, f16>(const u32x4& raw) { return raw; }
 template <> __device__ __forceinline__ u32x4 to_operand<bf16, bf16>(const u32x4& raw) { return raw; }
@@ -234,7 +236,8 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
 
 // ------------------------------------------------------------------------------------
 // Decode (one new token per sequence).  Grid (nsplit, B*n_kv), 4 wavefronts
-// per block; the block owns 4*CH consecutive keys of one (sequence, KV group)
+// per block; the block owns 4*CH consecutive keys of one (sequence, KV group),
+// each wavefront CH of them in steps of 32,
 // and all n_rep query heads of the group (heads are the 16 columns of a
 // 16x16x32 MFMA; columns >= n_rep are zero).  K rows and V^T rows go straight
 // from HBM into MFMA operand registers with 16-byte loads -- no LDS.  The
@@ -244,11 +247,11 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
 // output, running max, running sum) per head; attn_combine_kernel merges the
 // splits.
 // ------------------------------------------------------------------------------------
-template <typename T, int DH, int CH>
+template <typename T, int DH>
 __global__ void __launch_bounds__(256) attn_decode_kernel(
     const T* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     float* __restrict__ part, long k_bg, long v_bg, int t_stride, int H, int nkv, int n_rep,
-    int kv_len, int nsplit, float c) {
+    int kv_len, int CH, int nsplit, float c) {
     constexpr int NW = 4;
     __shared__ float sm[NW][16], sl[NW][16];
     __shared__ float so[NW][16][DH];
@@ -283,37 +286,43 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
     for (int dt = 0; dt < DH / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    for (int st = 0; st < CH / 32; ++st) {
+    // Steps of 32 keys.  One register buffer: at two wavefronts per SIMD the
+    // other wavefront's loads cover this one's compute (a second buffer would
+    // cost that occupancy).
+    int nsteps = (kv_len - k_begin + 31) / 32;
+    nsteps = nsteps < 0 ? 0 : (nsteps > CH / 32 ? CH / 32 : nsteps);
+    bf16x8 kf[1][2][DH / 32], vf[1][DH / 16];
+    auto load = [&](int st, int buf) {
         const int kb0 = k_begin + 32 * st;
-        if (kb0 >= kv_len) break;
-        bf16x8 kf[2][DH / 32];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int key = kb0 + 8 * ((lane & 15) >> 2) + 4 * t + (lane & 3);
             const bf16* p = kp + (size_t)min(key, kv_len - 1) * DH + 8 * grp;
 #pragma unroll
-            for (int kk = 0; kk < DH / 32; ++kk) kf[t][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
+            for (int kk = 0; kk < DH / 32; ++kk) kf[buf][t][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
         }
-        bf16x8 vf[DH / 16];
         const int key8 = kb0 + 8 * grp;
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) {
             const bf16* p = vp + (size_t)(16 * dt + (lane & 15)) * t_stride + key8;
             if (key8 + 8 <= kv_len) {
-                vf[dt] = *reinterpret_cast<const bf16x8*>(p);
+                vf[buf][dt] = *reinterpret_cast<const bf16x8*>(p);
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vf[dt][e] = (key8 + e < kv_len) ? p[e] : (bf16)0.0f;
+                for (int e = 0; e < 8; ++e) vf[buf][dt][e] = (key8 + e < kv_len) ? p[e] : (bf16)0.0f;
             }
         }
+    };
+    auto compute = [&](int st, int buf) {
+        const int kb0 = k_begin + 32 * st;
         f32x4 sc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < DH / 32; ++kk) {
-                sc[t] = mfma16(kf[t][kk], qh[kk], sc[t]);
-                sc[t] = mfma16(kf[t][kk], ql[kk], sc[t]);
+                sc[t] = mfma16(kf[buf][t][kk], qh[kk], sc[t]);
+                sc[t] = mfma16(kf[buf][t][kk], ql[kk], sc[t]);
             }
         }
         float mx = -INFINITY;
@@ -353,9 +362,13 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
         for (int dt = 0; dt < DH / 16; ++dt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) oacc[dt][r] *= alpha;
-            oacc[dt] = mfma16(vf[dt], ph, oacc[dt]);
-            oacc[dt] = mfma16(vf[dt], pl, oacc[dt]);
+            oacc[dt] = mfma16(vf[buf][dt], ph, oacc[dt]);
+            oacc[dt] = mfma16(vf[buf][dt], pl, oacc[dt]);
         }
+    };
+    for (int st = 0; st < nsteps; ++st) {
+        load(st, 0);
+        compute(st, 0);
     }
 
     float lt = l_run + __shfl_xor(l_run, 16, 64);
@@ -392,21 +405,48 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
     }
 }
 
-// Merge the decode splits of one (sequence, head): grid B*H, DH threads.
+// Merge the decode splits of one (sequence, KV group): grid B*n_kv, 256
+// threads.  A wavefront per head reduces the running maxima and sums over the
+// splits (lanes across splits) and leaves the per-split weights
+// exp2(m_s - M) / L in LDS; then every thread accumulates output elements over
+// the splits, four independent partial sums in flight.  nsplit <= 256.
 template <typename T, int DH>
-__global__ void __launch_bounds__(DH) attn_combine_kernel(const float* __restrict__ part,
-                                                          T* __restrict__ o, int nsplit) {
-    const int bh = blockIdx.x, d = threadIdx.x;
-    const float* pp = part + (size_t)bh * nsplit * (DH + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[s * (DH + 2) + DH]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float f = exp2f(pp[s * (DH + 2) + DH] - M);
-        L += pp[s * (DH + 2) + DH + 1] * f;
-        O += pp[s * (DH + 2) + d] * f;
+__global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ part,
+                                                           T* __restrict__ o, int H, int nkv,
+                                                           int n_rep, int nsplit) {
+    __shared__ float wt[16][kDecodeMaxSplit];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int bg = blockIdx.x, b = bg / nkv, g = bg % nkv;
+    const size_t head0 = (size_t)b * H + (size_t)g * n_rep;
+    for (int hh = wave; hh < n_rep; hh += 4) {
+        const float* pp = part + (head0 + hh) * nsplit * (DH + 2);
+        float m = -INFINITY;
+        for (int s = lane; s < nsplit; s += 64) m = fmaxf(m, pp[(size_t)s * (DH + 2) + DH]);
+        const float M = wave_max(m);
+        float l = 0.0f;
+        for (int s = lane; s < nsplit; s += 64) {
+            const float f = exp2f(pp[(size_t)s * (DH + 2) + DH] - M);
+            wt[hh][s] = f;
+            l += pp[(size_t)s * (DH + 2) + DH + 1] * f;
+        }
+        const float inv = 1.0f / wave_sum(l);
+        for (int s = lane; s < nsplit; s += 64) wt[hh][s] *= inv;
     }
-    o[(size_t)bh * DH + d] = from_f32<T>(O / L);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < n_rep * DH; idx += 256) {
+        const int hh = idx / DH, d = idx % DH;
+        const float* pp = part + (head0 + hh) * nsplit * (DH + 2) + d;
+        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+        int s = 0;
+        for (; s + 4 <= nsplit; s += 4) {
+            o0 += pp[(size_t)s * (DH + 2)] * wt[hh][s];
+            o1 += pp[(size_t)(s + 1) * (DH + 2)] * wt[hh][s + 1];
+            o2 += pp[(size_t)(s + 2) * (DH + 2)] * wt[hh][s + 2];
+            o3 += pp[(size_t)(s + 3) * (DH + 2)] * wt[hh][s + 3];
+        }
+        for (; s < nsplit; ++s) o0 += pp[(size_t)s * (DH + 2)] * wt[hh][s];
+        o[(head0 + hh) * DH + d] = from_f32<T>((o0 + o1) + (o2 + o3));
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -508,11 +548,19 @@ hipError_t attn_prefill(Elem op, Elem kv_t, const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-constexpr int kDecodeCH = 128;                    // keys per wavefront
-constexpr int kDecodeKeysPerBlock = 4 * kDecodeCH;
+// Keys per wavefront: 128, or more (a multiple of 32) when that would need
+// more than kDecodeMaxSplit blocks per (sequence, KV group).
+static int decode_keys_per_wave(int kv_len) {
+    int ch = 128;
+    while ((kv_len + 4 * ch - 1) / (4 * ch) > kDecodeMaxSplit) ch += 128;
+    return ch;
+}
 
+// Any kv_len <= max_kv uses at most min(kDecodeMaxSplit, ceil(max_kv / 512))
+// splits (keys per wavefront never drop below 128).
 size_t decode_partials_floats(int max_batch, int H, int dh, int max_kv) {
-    const size_t nsplit = (size_t)(max_kv + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
+    size_t nsplit = (size_t)(max_kv + 511) / 512;
+    if (nsplit > (size_t)kDecodeMaxSplit) nsplit = kDecodeMaxSplit;
     return (size_t)max_batch * H * nsplit * (dh + 2);
 }
 
@@ -520,14 +568,15 @@ template <typename T, int DH>
 static hipError_t decode_t(const AttnArgs& a, float* part, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
     const int kv_len = a.start_pos + 1;
-    const int nsplit = (kv_len + kDecodeKeysPerBlock - 1) / kDecodeKeysPerBlock;
+    const int ch = decode_keys_per_wave(kv_len);
+    const int nsplit = (kv_len + 4 * ch - 1) / (4 * ch);
     const float c = kLog2e / sqrtf((float)DH);
-    attn_decode_kernel<T, DH, kDecodeCH><<<dim3(nsplit, a.B * a.nkv), 256, 0, s>>>(
+    attn_decode_kernel<T, DH><<<dim3(nsplit, a.B * a.nkv), 256, 0, s>>>(
         (const T*)a.q, (const bf16*)a.k, (const bf16*)a.v, part, a.k_bg, a.v_bg, a.t_stride, a.H,
-        a.nkv, n_rep, kv_len, nsplit, c);
+        a.nkv, n_rep, kv_len, ch, nsplit, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attn_combine_kernel<T, DH><<<a.B * a.H, DH, 0, s>>>(part, (T*)a.o, nsplit);
+    attn_combine_kernel<T, DH><<<a.B * a.nkv, 256, 0, s>>>(part, (T*)a.o, a.H, a.nkv, n_rep, nsplit);
     return hipGetLastError();
 }
 

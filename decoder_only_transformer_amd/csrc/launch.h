@@ -34,17 +34,26 @@ struct QkvEpi {
     int S, start_pos, cap, s_stride, nkv, dh, qd;
 };
 // op: operand type of A and W (F32 selects the plain fp32 kernels); cache: cache type.
+// part: fp32 workspace for the split-K decode GEMMs (M <= 64), cap floats;
+// skinny_partials_floats(max M, max N) is enough for any split the launcher
+// picks, and the launcher lowers the split until [split][M][N] fits cap.
+constexpr int kSkinnyMaxSplit = 8;
+size_t skinny_partials_floats(int max_m, int max_n);
+struct SplitWs {
+    float* part;
+    size_t cap;
+};
 hipError_t gemm_qkv(Elem op, Elem cache, const void* A, const void* W, int M, int N, int K,
-                    const QkvEpi& e, hipStream_t s);
+                    const QkvEpi& e, const SplitWs& part, hipStream_t s);
 // out(fp32) = resid + A W^T
 hipError_t gemm_resid(Elem op, Elem resid_t, const void* A, const void* W, int M, int N, int K,
-                      const void* resid, float* out, hipStream_t s);
+                      const void* resid, float* out, const SplitWs& part, hipStream_t s);
 // z[M][dff] = SiLU(gate) * up from the interleaved gate/up product (N = 2*dff)
 hipError_t gemm_swiglu(Elem op, const void* A, const void* W, int M, int N, int K, void* z,
-                       hipStream_t s);
+                       const SplitWs& part, hipStream_t s);
 // y = h + A W^T, y in out_t
 hipError_t gemm_out(Elem op, Elem out_t, const void* A, const void* W, int M, int N, int K,
-                    const float* h, void* y, hipStream_t s);
+                    const float* h, void* y, const SplitWs& part, hipStream_t s);
 
 // ---- attention --------------------------------------------------------------------
 struct AttnArgs {

@@ -11,6 +11,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -46,7 +47,9 @@ struct lb_block {
     void* kws = nullptr;
     void* vws = nullptr;
     size_t ws_rows = 0;  // token rows the k/v workspace copies hold
-    float* part = nullptr;
+    float* part = nullptr;       // decode attention partials
+    float* gpart = nullptr;      // split-K decode GEMM partials
+    size_t gpart_cap = 0;        // floats
     std::vector<void*> allocs;
     std::string err;
     // per-stage timing: a ring of event sets, LB_NUM_STAGES + 1 events each
@@ -209,7 +212,10 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
         ok = dalloc(blk, &blk->kws, blk->ws_rows * blk->kvd * eo) &&
              dalloc(blk, &blk->vws, blk->ws_rows * blk->kvd * eo) &&
              dalloc(blk, &blk->part,
-                    lb::decode_partials_floats(c.max_tokens, c.n_heads, dh, c.max_seq_len) * sizeof(float));
+                    lb::decode_partials_floats(c.max_tokens, c.n_heads, dh, c.max_seq_len) * sizeof(float)) &&
+             dalloc(blk, &blk->gpart, (blk->gpart_cap = lb::skinny_partials_floats(
+                                           c.max_tokens < 64 ? c.max_tokens : 64,
+                                           std::max(std::max(blk->nqkv, d), 2 * dff))) * sizeof(float));
     }
     if (!ok) {
         free_all(blk);
@@ -319,7 +325,7 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     qe.dh = dh;
     qe.qd = blk->qd;
     mark(1);
-    e = lb::gemm_qkv(op, dt, blk->n1, blk->w_qkv, M, blk->nqkv, d, qe, s);
+    e = lb::gemm_qkv(op, dt, blk->n1, blk->w_qkv, M, blk->nqkv, d, qe, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "qkv projection: %s", hipGetErrorString(e));
 
     lb::AttnArgs a;
@@ -351,16 +357,16 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "attention: %s", hipGetErrorString(e));
 
     mark(3);
-    e = lb::gemm_resid(op, dt, blk->o, blk->w_o, M, d, blk->qd, x, blk->h, s);
+    e = lb::gemm_resid(op, dt, blk->o, blk->w_o, M, d, blk->qd, x, blk->h, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "o projection: %s", hipGetErrorString(e));
     mark(4);
     e = lb::launch_rmsnorm(Elem::F32, op, blk->h, blk->g2, blk->n2, M, d, (float)c.norm_eps, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_2: %s", hipGetErrorString(e));
     mark(5);
-    e = lb::gemm_swiglu(op, blk->n2, blk->w_gu, M, 2 * dff, d, blk->z, s);
+    e = lb::gemm_swiglu(op, blk->n2, blk->w_gu, M, 2 * dff, d, blk->z, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "gate/up projection: %s", hipGetErrorString(e));
     mark(6);
-    e = lb::gemm_out(op, dt, blk->z, blk->w_down, M, d, dff, blk->h, out, s);
+    e = lb::gemm_out(op, dt, blk->z, blk->w_down, M, d, dff, blk->h, out, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "down projection: %s", hipGetErrorString(e));
     mark(7);
     return LB_OK;
