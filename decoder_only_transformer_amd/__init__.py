@@ -186,11 +186,10 @@ def make_config(d_model, n_heads, n_kv_heads, d_head, d_ff, max_tokens, max_seq_
 
 def new_kv_cache(batch: int, n_kv: int, max_seq_len: int, d_head: int, dtype, device="cuda",
                  fill: Optional[float] = 0.0):
-    """Allocate (k, v) in the library's cache layout: k [B][n_kv][max_seq][d_head],
-    v [B][n_kv][d_head][max_seq] (transposed)."""
+    """Allocate (k, v) in the library's cache layout: [B][n_kv][max_seq][d_head] each."""
     import torch
     k = torch.empty((batch, n_kv, max_seq_len, d_head), dtype=dtype, device=device)
-    v = torch.empty((batch, n_kv, d_head, max_seq_len), dtype=dtype, device=device)
+    v = torch.empty((batch, n_kv, max_seq_len, d_head), dtype=dtype, device=device)
     if fill is not None:
         k.fill_(fill)
         v.fill_(fill)

@@ -23,9 +23,9 @@ template <typename TO, typename TC>
 struct EpiQKV {
     TO* q;              // [M][qd]
     TO* kws;            // [B][nkv][s_stride][dh] or nullptr
-    TO* vws;            // [B][nkv][dh][s_stride] or nullptr
+    TO* vws;            // [B][nkv][s_stride][dh] or nullptr
     TC* kc;             // [B][nkv][cap][dh]
-    TC* vc;             // [B][nkv][dh][cap]
+    TC* vc;             // [B][nkv][cap][dh]
     const float2* rope; // [max_seq][dh/2] (cos, sin)
     int S, start_pos, cap, s_stride, nkv, dh, qd;
 
@@ -54,12 +54,8 @@ struct EpiQKV {
             const int nn = n - qd - kvd;
             const int g = nn / dh, j = nn % dh;
             const size_t bg = (size_t)b * nkv + g;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vc[(bg * dh + j + e) * cap + pos] = from_f32<TC>(v[e]);
-            if (vws) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vws[(bg * dh + j + e) * s_stride + s] = from_f32<TO>(v[e]);
-            }
+            store8(vc + (bg * cap + pos) * dh + j, v);
+            if (vws) store8(vws + (bg * s_stride + s) * dh + j, v);
         }
     }
 };

@@ -171,9 +171,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
 // ------------------------------------------------------------------------------------
 // Decode GEMM for M <= 16*MT token rows: a weight-streaming kernel.  Grid
 // (N / (16*CT), KS), KW wavefronts per block.  Every wavefront owns the block's
-// 16*CT output columns (CT 16x16x32 MFMA column tiles) and a share of K: k-steps
-// of 32 are dealt round-robin over the KS blocks and their wavefronts, U steps
-// per chunk, two chunks in flight (register double buffering).  Per k-step a
+// 16*CT output columns (CT 16x16x32 MFMA column tiles); the KS blocks of a
+// column tile split K into contiguous ranges and a block deals its k-steps of
+// 32 round-robin to its wavefronts, U steps per chunk, two chunks in flight
+// (register double buffering).  Per k-step a
 // lane loads 16 bytes of each of its CT weight rows (MFMA B operands) straight
 // from HBM and 16 bytes of each token tile (A, hot in L2); CT column tiles per
 // A load keep the activation re-reads at 2*MT/CT of the weight traffic.  The
@@ -193,9 +194,12 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * COLS, ks = blockIdx.y;
     const int nks = K / 32;
-    const int stride = KS * KW;
-    const int first = ks + KS * wave;
-    const int n_my = first < nks ? (nks - first + stride - 1) / stride : 0;
+    // block ks owns the contiguous k-steps [ks*nks/KS, (ks+1)*nks/KS); inside
+    // the block they are dealt round-robin to the wavefronts, so at any moment
+    // the block sweeps each weight row through one contiguous run
+    const int kfirst = (int)((long)ks * nks / KS);
+    const int kcount = (int)((long)(ks + 1) * nks / KS) - kfirst;
+    const int n_my = wave < kcount ? (kcount - wave + KW - 1) / KW : 0;
     const int nchunk = (n_my + U - 1) / U;
     const T* wp[CT];
 #pragma unroll
@@ -215,7 +219,7 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
     auto load = [&](int chunk, int s) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int kstep = min(first + (chunk * U + u) * stride, nks - 1);
+            const int kstep = min(kfirst + wave + (chunk * U + u) * KW, nks - 1);
 #pragma unroll
             for (int c = 0; c < CT; ++c) bw[s][u][c] = *reinterpret_cast<const V8*>(wp[c] + kstep * 32);
 #pragma unroll

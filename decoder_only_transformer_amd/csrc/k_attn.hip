@@ -37,32 +37,59 @@ template <> __device__ __forceinline__ u32x4 to_operand<f16, bf16>(const u32x4& 
 __device__ __forceinline__ int key_perm(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 // LDS chunk swizzle of the key tile, conflict-free for the permuted read.
 __device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// LDS chunk swizzle of a value tile ([key][d] rows): the 16 lanes of a
+// transpose read cover 4 consecutive keys x 2 chunks, which land on 8
+// different bank groups.
+__device__ __forceinline__ int vswz(int row) { return (row & 3) << 1; }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Transpose read (ds_read_b64_tr_b16) of a V^T operand from a [key][DH]
+// value tile in LDS.  Within each 16-lane group, lane s reads 4 values of
+// key k0 + s/4 at d0 + 4*(s%4); the hardware hands lane j the 4 values of
+// column d0 + j at keys k0 .. k0+3.  Two reads (keys k0.. and k0+4..) give the
+// 8 k-slots of one MFMA operand: slot e <-> key k0 + e, column d0 + j.
+template <typename T, int DH>
+__device__ __forceinline__ typename vec8<T>::type vt_fragment(const T* tile, int k0, int d0, int lane) {
+    const int s = lane & 15;
+    const int d = d0 + 4 * (s & 3);
+    const int ka = k0 + (s >> 2), kb = ka + 4;
+    const T* pa = tile + ka * DH + ((((d >> 3) ^ vswz(ka)) << 3) | (d & 7));
+    const T* pb = tile + kb * DH + ((((d >> 3) ^ vswz(kb)) << 3) | (d & 7));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)pa);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)pb);
+    typename vec8<T>::type r;
+    __builtin_memcpy(&r, &lo, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
+    return r;
+}
 
 // ------------------------------------------------------------------------------------
 // Prefill.  Grid (ceil(S/32), B*n_kv*n_hb), NW wavefronts per block: the
 // block owns 32 consecutive queries of one sequence and NW query heads of one
-// KV group; every wavefront is one head and all of them share each K / V^T
+// KV group; every wavefront is one head and all of them share each K / V
 // tile staged in LDS.  Per 64-key tile a wavefront computes S^T (64 keys x
 // 32 queries) with 32x32x16 MFMAs, masks, updates the softmax state of its
 // lane's query (lane = query, so rescaling is lane-local) and accumulates
-// O^T += V^T P^T.  Tiles are prefetched into registers during the MFMAs.
-// Heavier (later) query blocks are launched first.
+// O^T += V^T P^T, the V^T operands read from the [key][d] tile with transpose
+// reads.  Tiles are prefetched into registers during the MFMAs.  Heavier
+// (later) query blocks are launched first.
 // ------------------------------------------------------------------------------------
 template <typename T, typename KVT, int DH, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
     const T* __restrict__ q, const KVT* __restrict__ kbase, const KVT* __restrict__ vbase,
-    T* __restrict__ o, long k_bg, long v_bg, int t_stride, int S, int start_pos, int H, int nkv,
-    int n_rep, int n_hb, float c) {
+    T* __restrict__ o, long kv_bg, int S, int start_pos, int H, int nkv, int n_rep, int n_hb,
+    float c) {
     typedef typename vec8<T>::type V8;
     constexpr int KT = 64;
     constexpr int NT = NW * 64;
     constexpr int KCH = DH / 8;
     constexpr int KCHUNKS = KT * KCH;
-    constexpr int VCHUNKS = DH * (KT / 8);
     constexpr int KPT = (KCHUNKS + NT - 1) / NT;
-    constexpr int VPT = (VCHUNKS + NT - 1) / NT;
     __shared__ __attribute__((aligned(16))) T ks[KT * DH];
-    __shared__ __attribute__((aligned(16))) T vs[DH * KT];
+    __shared__ __attribute__((aligned(16))) T vs[KT * DH];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int qb = gridDim.x - 1 - blockIdx.x;
@@ -86,10 +113,12 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
     }
     const int kv_len = start_pos + min(q0 + 32, S);
     const int ntiles = (kv_len + KT - 1) / KT;
-    const KVT* kp = kbase + (size_t)bg * k_bg;
-    const KVT* vp = vbase + (size_t)bg * v_bg;
+    const KVT* kp = kbase + (size_t)bg * kv_bg;
+    const KVT* vp = vbase + (size_t)bg * kv_bg;
 
-    u32x4 kreg[KPT], vreg[VPT];
+    // rows past kv_len are zero in both tiles (masked keys must not bring
+    // non-finite cache contents into the products)
+    u32x4 kreg[KPT], vreg[KPT];
     auto gload = [&](int tile) {
         const int t0 = tile * KT;
 #pragma unroll
@@ -97,25 +126,12 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
             const int cidx = tid + i * NT;
             if (cidx < KCHUNKS) {
                 const int row = cidx / KCH, ch = cidx % KCH, key = t0 + row;
-                if (key < kv_len)
+                if (key < kv_len) {
                     kreg[i] = *reinterpret_cast<const u32x4*>(kp + (size_t)key * DH + ch * 8);
-                else
-                    kreg[i] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int cidx = tid + i * NT;
-            if (cidx < VCHUNKS) {
-                const int d = cidx / (KT / 8), ch = cidx % (KT / 8), key8 = t0 + ch * 8;
-                const KVT* p = vp + (size_t)d * t_stride + key8;
-                if (key8 + 8 <= kv_len) {
-                    vreg[i] = *reinterpret_cast<const u32x4*>(p);
+                    vreg[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)key * DH + ch * 8);
                 } else {
-                    KVT tmp[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) tmp[e] = (key8 + e < kv_len) ? p[e] : from_f32<KVT>(0.0f);
-                    __builtin_memcpy(&vreg[i], tmp, 16);
+                    kreg[i] = u32x4{0u, 0u, 0u, 0u};
+                    vreg[i] = u32x4{0u, 0u, 0u, 0u};
                 }
             }
         }
@@ -127,14 +143,7 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
             if (cidx < KCHUNKS) {
                 const int row = cidx / KCH, ch = cidx % KCH;
                 *reinterpret_cast<u32x4*>(ks + row * DH + ((ch ^ kswz(row)) << 3)) = to_operand<T, KVT>(kreg[i]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int cidx = tid + i * NT;
-            if (cidx < VCHUNKS) {
-                const int d = cidx / (KT / 8), ch = cidx % (KT / 8);
-                *reinterpret_cast<u32x4*>(vs + d * KT + ((ch ^ (d & 7)) << 3)) = to_operand<T, KVT>(vreg[i]);
+                *reinterpret_cast<u32x4*>(vs + row * DH + ((ch ^ vswz(row)) << 3)) = to_operand<T, KVT>(vreg[i]);
             }
         }
     };
@@ -206,13 +215,13 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
                 for (int e = 0; e < 8; ++e) pf[kb][cc][e] = from_f32<T>(sacc[kb][8 * cc + e]);
 #pragma unroll
         for (int dt = 0; dt < DH / 32; ++dt) {
-            const int d = dt * 32 + (lane & 31);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
-                    const int ch = 4 * kb + 2 * cc + (lane >> 5);
-                    const V8 vf = *reinterpret_cast<const V8*>(vs + d * KT + ((ch ^ (d & 7)) << 3));
+                    // slot e <-> key 32kb + 16cc + 8*(lane/32) + e, column 32dt + lane%32
+                    const V8 vf = vt_fragment<T, DH>(vs, 32 * kb + 16 * cc + 8 * (lane >> 5),
+                                                     32 * dt + 16 * ((lane >> 4) & 1), lane);
                     oacc[dt] = mfma32(vf, pf[kb][cc], oacc[dt]);
                 }
         }
@@ -237,83 +246,105 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
 // ------------------------------------------------------------------------------------
 // Decode (one new token per sequence).  Grid (nsplit, B*n_kv), 4 wavefronts
 // per block; the block owns 4*CH consecutive keys of one (sequence, KV group),
-// each wavefront CH of them in steps of 32,
-// and all n_rep query heads of the group (heads are the 16 columns of a
-// 16x16x32 MFMA; columns >= n_rep are zero).  K rows and V^T rows go straight
-// from HBM into MFMA operand registers with 16-byte loads -- no LDS.  The
-// cache is bf16; q and the probabilities enter the bf16 MFMAs as a hi + lo
-// pair of bf16 values (16 mantissa bits), so only the cache itself is bf16.
-// The block merges its wavefronts in LDS and writes one partial (unnormalised
-// output, running max, running sum) per head; attn_combine_kernel merges the
-// splits.
+// each wavefront CH of them in steps of 32, and all n_rep query heads of the
+// group (heads are the 16 columns of a 16x16x32 MFMA; columns >= n_rep are
+// zero).  K rows go straight from HBM into MFMA operand registers with
+// 16-byte loads; each step's 32 V rows (one contiguous run) go from HBM into
+// the wavefront's own LDS slab (two per wavefront, alternating) with
+// direct-to-LDS loads and come back as V^T operands through transpose reads.
+// Software pipeline without extra registers: as soon as the QK^T MFMAs of
+// step s have consumed the K registers, the K loads and V slab loads of step
+// s+1 are issued into them, so HBM stays busy during step s's softmax and PV.
+// The cache is bf16; q and the probabilities enter the bf16 MFMAs as a hi +
+// lo pair of bf16 values (16 mantissa bits), so only the cache itself is
+// bf16.  The block merges its wavefronts in LDS and writes one partial
+// (unnormalised output, running max, running sum) per head;
+// attn_combine_kernel merges the splits.
 // ------------------------------------------------------------------------------------
+template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) attn_decode_kernel(
     const T* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-    float* __restrict__ part, long k_bg, long v_bg, int t_stride, int H, int nkv, int n_rep,
-    int kv_len, int CH, int nsplit, float c) {
+    float* __restrict__ part, long kv_bg, int H, int nkv, int n_rep, int kv_len, int CH,
+    int nsplit, float c) {
     constexpr int NW = 4;
+    constexpr int KCH = DH / 8;              // 16-byte chunks per row
+    constexpr int VLOADS = 32 * KCH / 64;    // direct-to-LDS instructions per step
+    constexpr int KLOADS = 2 * (DH / 32);    // K operand loads per step
+    constexpr int SLAB = 32 * DH;            // bf16 elements per slab
     __shared__ float sm[NW][16], sl[NW][16];
-    __shared__ float so[NW][16][DH];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Two V slabs per wavefront, one in each array, so that every LDS access
+    // names its array statically and the compiler's wait for the
+    // direct-to-LDS loads of one slab never covers the other.  slab_a is the
+    // merge buffer after the loop.
+    __shared__ __attribute__((aligned(16))) bf16 slab_a[NW * SLAB];
+    __shared__ __attribute__((aligned(16))) bf16 slab_b[NW * SLAB];
+    static_assert(NW * 16 * DH * 4 <= NW * SLAB * 2, "merge buffer fits a slab array");
+    float (*so)[16][DH] = reinterpret_cast<float (*)[16][DH]>(slab_a);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int split = blockIdx.x, bg = blockIdx.y;
     const int b = bg / nkv, g = bg % nkv;
     const int hl = lane & 15, grp = lane >> 4;
+    bf16* my_a = slab_a + wave * SLAB;
+    bf16* my_b = slab_b + wave * SLAB;
 
-    bf16x8 qh[DH / 32], ql[DH / 32];
-#pragma unroll
-    for (int kk = 0; kk < DH / 32; ++kk) {
-        float v[8];
-        if (hl < n_rep) {
-            load8(q + (size_t)b * H * DH + (size_t)(g * n_rep + hl) * DH + 32 * kk + 8 * grp, v);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const bf16 hi = (bf16)v[e];
-            qh[kk][e] = hi;
-            ql[kk][e] = (bf16)(v[e] - (float)hi);
-        }
-    }
-
-    const bf16* kp = kc + (size_t)bg * k_bg;
-    const bf16* vp = vc + (size_t)bg * v_bg;
+    const bf16* kp = kc + (size_t)bg * kv_bg;
+    const bf16* vp = vc + (size_t)bg * kv_bg;
     const int k_begin = (split * NW + wave) * CH;
-    f32x4 oacc[DH / 16];
-#pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    // Steps of 32 keys.  One register buffer: at two wavefronts per SIMD the
-    // other wavefront's loads cover this one's compute (a second buffer would
-    // cost that occupancy).
     int nsteps = (kv_len - k_begin + 31) / 32;
     nsteps = nsteps < 0 ? 0 : (nsteps > CH / 32 ? CH / 32 : nsteps);
-    bf16x8 kf[1][2][DH / 32], vf[1][DH / 16];
-    auto load = [&](int st, int buf) {
+    bf16x8 kf[2][DH / 32];
+    // K operands of step st into kf; V rows of step st into slab (rows past
+    // kv_len repeat the last valid row: finite values that meet zero
+    // probabilities)
+    auto issue = [&](int st, bf16* slab) {
         const int kb0 = k_begin + 32 * st;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int key = kb0 + 8 * ((lane & 15) >> 2) + 4 * t + (lane & 3);
             const bf16* p = kp + (size_t)min(key, kv_len - 1) * DH + 8 * grp;
 #pragma unroll
-            for (int kk = 0; kk < DH / 32; ++kk) kf[buf][t][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
+            for (int kk = 0; kk < DH / 32; ++kk) kf[t][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
         }
-        const int key8 = kb0 + 8 * grp;
 #pragma unroll
-        for (int dt = 0; dt < DH / 16; ++dt) {
-            const bf16* p = vp + (size_t)(16 * dt + (lane & 15)) * t_stride + key8;
-            if (key8 + 8 <= kv_len) {
-                vf[buf][dt] = *reinterpret_cast<const bf16x8*>(p);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vf[buf][dt][e] = (key8 + e < kv_len) ? p[e] : (bf16)0.0f;
-            }
+        for (int i = 0; i < VLOADS; ++i) {
+            const int p = i * 64 + lane, row = p / KCH, pc = p % KCH, ch = pc ^ vswz(row);
+            const bf16* src = vp + (size_t)min(kb0 + row, kv_len - 1) * DH + ch * 8;
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)(slab + i * 64 * 8), 16, 0, 0);
         }
     };
-    auto compute = [&](int st, int buf) {
+    // the first step's loads go out before q's, which the first step needs
+    // only after they have landed anyway
+    if (nsteps > 0) issue(0, my_a);
+
+    // q of head hl (heads >= n_rep read head 0 and are zeroed)
+    bf16x8 qh[DH / 32], ql[DH / 32];
+    {
+        const T* qp = q + (size_t)b * H * DH + (size_t)(g * n_rep + (hl < n_rep ? hl : 0)) * DH + 8 * grp;
+        float v[DH / 32][8];
+#pragma unroll
+        for (int kk = 0; kk < DH / 32; ++kk) load8(qp + 32 * kk, v[kk]);
+        const float keep = hl < n_rep ? 1.0f : 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < DH / 32; ++kk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = v[kk][e] * keep;
+                const bf16 hi = (bf16)x;
+                qh[kk][e] = hi;
+                ql[kk][e] = (bf16)(x - (float)hi);
+            }
+    }
+
+    f32x4 oacc[DH / 16];
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    // one 32-key step whose V rows are in cur; the next step goes to nxt
+    auto step = [&](int st, const bf16* cur, bf16* nxt) {
         const int kb0 = k_begin + 32 * st;
         f32x4 sc[2];
 #pragma unroll
@@ -321,10 +352,13 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
             sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < DH / 32; ++kk) {
-                sc[t] = mfma16(kf[buf][t][kk], qh[kk], sc[t]);
-                sc[t] = mfma16(kf[buf][t][kk], ql[kk], sc[t]);
+                sc[t] = mfma16(kf[t][kk], qh[kk], sc[t]);
+                sc[t] = mfma16(kf[t][kk], ql[kk], sc[t]);
             }
         }
+        const bool more = st + 1 < nsteps;
+        if (more) issue(st + 1, nxt);
+        // lane: head hl, register r of tile t: key kb0 + 8*grp + 4t + r
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -358,21 +392,31 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
             ph[e] = hi;
             pl[e] = (bf16)(pv[e] - (float)hi);
         }
+        // cur has landed once at most the next step's loads are pending
+        // (loads retire in order)
+        if (more) wait_vmcnt<KLOADS + VLOADS>();
+        else wait_vmcnt<0>();
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) {
+            // slot e <-> key 8*grp + e of the step, column 16dt + lane%16
+            const bf16x8 vf = vt_fragment<bf16, DH>(cur, 8 * grp, 16 * dt, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) oacc[dt][r] *= alpha;
-            oacc[dt] = mfma16(vf[buf][dt], ph, oacc[dt]);
-            oacc[dt] = mfma16(vf[buf][dt], pl, oacc[dt]);
+            oacc[dt] = mfma16(vf, ph, oacc[dt]);
+            oacc[dt] = mfma16(vf, pl, oacc[dt]);
         }
+        // cur's transpose reads have returned before the step after next
+        // loads into it
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
-    for (int st = 0; st < nsteps; ++st) {
-        load(st, 0);
-        compute(st, 0);
+    for (int st = 0; st < nsteps; st += 2) {
+        step(st, my_a, my_b);
+        if (st + 1 < nsteps) step(st + 1, my_b, my_a);
     }
 
     float lt = l_run + __shfl_xor(l_run, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
+    __syncthreads();  // all slabs are done before the merge buffer is written
     if (grp == 0) {
         sm[wave][hl] = m_run;
         sl[wave][hl] = lt;
@@ -458,8 +502,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
 __global__ void __launch_bounds__(64) attn_simple_kernel(const float* __restrict__ q,
                                                          const float* __restrict__ kc,
                                                          const float* __restrict__ vc,
-                                                         float* __restrict__ o, long k_bg,
-                                                         long v_bg, int t_stride, int S,
+                                                         float* __restrict__ o, long kv_bg, int S,
                                                          int start_pos, int H, int nkv, int dh,
                                                          float c) {
     __shared__ float qs[256];
@@ -478,7 +521,7 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(const float* __restrict
         const int t = t0 + lane;
         float sv = -INFINITY;
         if (t < n) {
-            const float* kr = kc + bg * k_bg + (size_t)t * dh;
+            const float* kr = kc + bg * kv_bg + (size_t)t * dh;
             float acc = 0.0f;
             for (int d = 0; d < dh; ++d) acc = fmaf(qs[d], kr[d], acc);
             sv = acc * c;
@@ -495,8 +538,8 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(const float* __restrict
             const int d = lane + 64 * j;
             if (d < dh) {
                 float a = oa[j] * alpha;
-                const float* vr = vc + bg * v_bg + (size_t)d * t_stride + t0;
-                for (int u = 0; u < cnt; ++u) a = fmaf(ps[u], vr[u], a);
+                const float* vr = vc + bg * kv_bg + (size_t)t0 * dh + d;
+                for (int u = 0; u < cnt; ++u) a = fmaf(ps[u], vr[(size_t)u * dh], a);
                 oa[j] = a;
             }
         }
@@ -518,8 +561,8 @@ static hipError_t prefill_t(const AttnArgs& a, hipStream_t s) {
     const dim3 grid((a.S + 31) / 32, a.B * a.nkv * n_hb);
     const float c = kLog2e / sqrtf((float)DH);
     attn_prefill_kernel<T, KVT, DH, NW><<<grid, NW * 64, 0, s>>>(
-        (const T*)a.q, (const KVT*)a.k, (const KVT*)a.v, (T*)a.o, a.k_bg, a.v_bg, a.t_stride, a.S,
-        a.start_pos, a.H, a.nkv, n_rep, n_hb, c);
+        (const T*)a.q, (const KVT*)a.k, (const KVT*)a.v, (T*)a.o, a.kv_bg, a.S, a.start_pos, a.H,
+        a.nkv, n_rep, n_hb, c);
     return hipGetLastError();
 }
 
@@ -572,8 +615,8 @@ static hipError_t decode_t(const AttnArgs& a, float* part, hipStream_t s) {
     const int nsplit = (kv_len + 4 * ch - 1) / (4 * ch);
     const float c = kLog2e / sqrtf((float)DH);
     attn_decode_kernel<T, DH><<<dim3(nsplit, a.B * a.nkv), 256, 0, s>>>(
-        (const T*)a.q, (const bf16*)a.k, (const bf16*)a.v, part, a.k_bg, a.v_bg, a.t_stride, a.H,
-        a.nkv, n_rep, kv_len, ch, nsplit, c);
+        (const T*)a.q, (const bf16*)a.k, (const bf16*)a.v, part, a.kv_bg, a.H, a.nkv, n_rep, kv_len,
+        ch, nsplit, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_combine_kernel<T, DH><<<a.B * a.nkv, 256, 0, s>>>(part, (T*)a.o, a.H, a.nkv, n_rep, nsplit);
@@ -595,8 +638,8 @@ hipError_t attn_simple(const AttnArgs& a, hipStream_t s) {
     if (a.dh > 256) return hipErrorInvalidValue;
     const float c = kLog2e / sqrtf((float)a.dh);
     attn_simple_kernel<<<dim3(a.S, a.H, a.B), 64, 0, s>>>(
-        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.k_bg, a.v_bg,
-        a.t_stride, a.S, a.start_pos, a.H, a.nkv, a.dh, c);
+        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.kv_bg, a.S,
+        a.start_pos, a.H, a.nkv, a.dh, c);
     return hipGetLastError();
 }
 

@@ -6,34 +6,46 @@ namespace lb {
 
 // RMSNorm ("The Evolving Transformer 04 LLaMA", 03 RMSNORM; "Full Llama 3
 // transformer block", How it works): out = x / sqrt(mean(x^2) + eps) * g.
-// One wavefront per token row; the sum of squares is accumulated in fp32 per
-// lane (8 elements per 16-byte load) and reduced across the wavefront in a
-// fixed butterfly order, so results are deterministic.
+// One 256-thread block per token row, so even a 32-row decode batch spreads
+// over 32 CUs.  Each thread keeps its (up to 8) 8-element chunks in
+// registers; the sum of squares is accumulated in fp32 and reduced across
+// wavefronts (butterfly) and then across the block in a fixed order, so
+// results are deterministic.  d <= 16384 (d % 8 == 0).
 template <typename TI, typename TO>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const TI* __restrict__ x,
                                                       const float* __restrict__ g,
                                                       TO* __restrict__ out, int M, int d, float eps) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= M) return;
+    __shared__ float part[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x;
     const TI* xr = x + (size_t)row * d;
     TO* orow = out + (size_t)row * d;
+    float v[8][8];
     float ss = 0.0f;
-    for (int c = lane * 8; c < d; c += 512) {
-        float v[8];
-        load8(xr + c, v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    for (int i = 0; i < 8; ++i) {
+        const int c = (threadIdx.x + 256 * i) * 8;
+        if (c < d) {
+            load8(xr + c, v[i]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
+        }
     }
     ss = wave_sum(ss);
+    if (lane == 0) part[wave] = ss;
+    __syncthreads();
+    ss = (part[0] + part[1]) + (part[2] + part[3]);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
-    for (int c = lane * 8; c < d; c += 512) {
-        float v[8], gg[8];
-        load8(xr + c, v);
-        load8(g + c, gg);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = v[e] * r * gg[e];
-        store8(orow + c, v);
+    for (int i = 0; i < 8; ++i) {
+        const int c = (threadIdx.x + 256 * i) * 8;
+        if (c < d) {
+            float gg[8];
+            load8(g + c, gg);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] = v[i][e] * r * gg[e];
+            store8(orow + c, v[i]);
+        }
     }
 }
 
@@ -60,7 +72,8 @@ template <typename TI, typename TO>
 static hipError_t rmsnorm_t(const void* x, const float* g, void* out, int M, int d, float eps,
                             hipStream_t s) {
     if (M <= 0) return hipSuccess;
-    rmsnorm_kernel<TI, TO><<<(M + 3) / 4, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps);
+    if (d > 16384) return hipErrorInvalidValue;
+    rmsnorm_kernel<TI, TO><<<M, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps);
     return hipGetLastError();
 }
 

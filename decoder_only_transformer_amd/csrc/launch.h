@@ -27,9 +27,9 @@ hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const v
 struct QkvEpi {
     void* q;          // [M][qd]           operand type
     void* kws;        // [B][nkv][s_stride][dh] operand type, or nullptr
-    void* vws;        // [B][nkv][dh][s_stride] operand type, or nullptr
+    void* vws;        // [B][nkv][s_stride][dh] operand type, or nullptr
     void* kc;         // [Bc][nkv][cap][dh] cache type
-    void* vc;         // [Bc][nkv][dh][cap] cache type
+    void* vc;         // [Bc][nkv][cap][dh] cache type
     const float2* rope;
     int S, start_pos, cap, s_stride, nkv, dh, qd;
 };
@@ -58,11 +58,10 @@ hipError_t gemm_out(Elem op, Elem out_t, const void* A, const void* W, int M, in
 // ---- attention --------------------------------------------------------------------
 struct AttnArgs {
     const void* q;   // [B*S][H*dh] operand type (fp32 for fp32 blocks)
-    const void* k;   // K rows: element (bg, t, d) at k[bg*k_bg + t*dh + d]
-    const void* v;   // V^T rows: element (bg, d, t) at v[bg*v_bg + d*t_stride + t]
+    const void* k;   // element (bg, t, d) at k[bg*kv_bg + t*dh + d]
+    const void* v;   // element (bg, t, d) at v[bg*kv_bg + t*dh + d]
     void* o;         // [B*S][H*dh] operand type
-    long k_bg, v_bg;
-    int t_stride;
+    long kv_bg;      // elements per (sequence, KV head): positions * dh
     int B, S, start_pos, H, nkv, dh;
 };
 // Causal prefill attention (seq_len > 1).  op: q/o type; kv_t: K/V storage type.

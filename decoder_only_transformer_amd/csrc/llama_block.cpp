@@ -152,6 +152,8 @@ static lb_status validate_config(const lb_config* c) {
         return fail(nullptr, LB_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
     if (c->operands != LB_OPERANDS_AUTO && c->operands != LB_OPERANDS_F16 && c->operands != LB_OPERANDS_BF16)
         return fail(nullptr, LB_ERR_INVALID_ARG, "unknown operands %d", (int)c->operands);
+    if (c->d_model > 16384)
+        return fail(nullptr, LB_ERR_UNSUPPORTED, "d_model > 16384 is not supported (got %d)", c->d_model);
     if (c->dtype == LB_BF16) {
         if (c->d_head != 64 && c->d_head != 128)
             return fail(nullptr, LB_ERR_UNSUPPORTED, "bf16 blocks need d_head 64 or 128 (got %d)", c->d_head);
@@ -340,15 +342,11 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     if (ws_kv) {
         a.k = blk->kws;
         a.v = blk->vws;
-        a.k_bg = (long)s_stride * dh;
-        a.v_bg = (long)dh * s_stride;
-        a.t_stride = s_stride;
+        a.kv_bg = (long)s_stride * dh;
     } else {
         a.k = kv->k;
         a.v = kv->v;
-        a.k_bg = (long)cap * dh;
-        a.v_bg = (long)dh * cap;
-        a.t_stride = cap;
+        a.kv_bg = (long)cap * dh;
     }
     mark(2);
     if (dt == Elem::F32) e = lb::attn_simple(a, s);

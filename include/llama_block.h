@@ -80,9 +80,9 @@ typedef struct {
 
 /* KV cache, caller-owned device memory in cfg.dtype:
  *   k: [batch][n_kv_heads][max_seq_len][d_head]   one row per position
- *   v: [batch][n_kv_heads][d_head][max_seq_len]   TRANSPOSED: one row per
- *      head dimension, so that the decode kernels read V along positions
- *      with full-width loads.
+ *   v: [batch][n_kv_heads][max_seq_len][d_head]   one row per position
+ * (each (sequence, KV head) is one contiguous run of positions, so decode
+ * streams both tensors with contiguous reads and appends contiguous rows).
  * A forward with start_pos p and seq_len S reads positions [0, p) of
  * sequences 0..B-1 and writes positions [p, p+S); no other entry changes.
  * The "Llama 4 From Scratch" worked example counts 2*n_kv*d_head values per
@@ -98,9 +98,11 @@ typedef struct lb_block lb_block;
 
 /* Create a block on the current HIP device.  Validates cfg: d_model ==
  * n_heads*d_head, n_heads % n_kv_heads == 0, d_head even, d_ff, max_tokens,
- * max_seq_len, rope_theta, norm_eps > 0 (LB_ERR_INVALID_ARG); bf16 blocks
- * need d_head in {64, 128}, d_model % 64 == 0 and d_ff % 64 == 0, fp32
- * blocks d_head <= 256 (else LB_ERR_UNSUPPORTED).  Packs the weights, builds
+ * max_seq_len, rope_theta, norm_eps > 0 (LB_ERR_INVALID_ARG).  Supported
+ * shapes (else LB_ERR_UNSUPPORTED): d_model <= 16384; bf16 blocks need d_head
+ * in {64, 128}, d_model % 64 == 0, d_ff % 64 == 0 and n_heads/n_kv_heads <= 16;
+ * fp32 blocks need d_head % 8 == 0, d_head <= 256, d_model % 8 == 0 and
+ * d_ff % 4 == 0.  Packs the weights, builds
  * the RoPE cos/sin table (angles in fp64, stored as fp32) and allocates the
  * workspace.  Synchronous.  *out receives the handle (NULL on error). */
 lb_status llama_block_init(const lb_config* cfg, const lb_weights* weights, lb_block** out);

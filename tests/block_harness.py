@@ -41,7 +41,7 @@ def gpu_cache(w: workloads.BlockWorkload, tensors: Dict[str, torch.Tensor], fill
     k, v = lbmod.new_kv_cache(w.B, w.n_kv, cap, w.d_head, w.torch_dtype, fill=fill)
     if w.start_pos > 0:
         k[:, :, : w.start_pos, :] = tensors["k_prefix"].to("cuda")
-        v[:, :, :, : w.start_pos] = tensors["v_prefix"].to("cuda").transpose(-1, -2)
+        v[:, :, : w.start_pos, :] = tensors["v_prefix"].to("cuda")
     return k, v
 
 
@@ -88,7 +88,7 @@ def gpu_cache_rows(w, kv, b, lo, hi):
     """GPU cache rows [lo, hi) of sequence b as fp64 arrays [n_kv][n][d_head] (K and V)."""
     k, v = kv
     kk = k[b, :, lo:hi, :].double().cpu().numpy()
-    vv = v[b, :, :, lo:hi].transpose(-1, -2).double().cpu().numpy()
+    vv = v[b, :, lo:hi, :].double().cpu().numpy()
     return kk, vv
 
 

@@ -167,9 +167,9 @@ def test_cache_rows_outside_window_untouched():
     # prefix rows are real values; everything past start_pos+S stays NaN
     run.forward()
     k, v = run.kv
-    assert torch.isnan(k[:, :, 36:, :].float()).all() and torch.isnan(v[:, :, :, 36:].float()).all()
+    assert torch.isnan(k[:, :, 36:, :].float()).all() and torch.isnan(v[:, :, 36:, :].float()).all()
     assert not torch.isnan(k[:, :, :36, :].float()).any()
-    assert not torch.isnan(v[:, :, :, :36].float()).any()
+    assert not torch.isnan(v[:, :, :36, :].float()).any()
     assert not torch.isnan(run.out.float()).any()
     run.close()
 
