@@ -80,31 +80,34 @@ def run_gpu(w, steps, warmup):
     x = t["x"].to("cuda")
     out = torch.empty_like(x)
     del t
-    stream = torch.cuda.current_stream()
     for _ in range(warmup):
         blk.forward(x, w.start_pos, (k, v), out)
-    # timed region: `steps` back-to-back forwards, no profiling events
+    # timed region: `steps` back-to-back forwards; the library records one
+    # timing-only HIP event per stage boundary on the forward's stream (the
+    # current torch stream), which gives the per-kernel durations
+    lbmod.llama_block_profile(blk.handle, True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         blk.forward(x, w.start_pos, (k, v), out)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # second pass of the same length with the library's per-stage HIP events
-    # (recorded on this stream); the events add a few us between stages, so
-    # this pass only feeds the per-stage durations
-    lbmod.llama_block_profile(blk.handle, True)
-    for _ in range(steps):
-        blk.forward(x, w.start_pos, (k, v), out)
     stage_ms, calls = lbmod.llama_block_profile_read(blk.handle)
     lbmod.llama_block_profile(blk.handle, False)
+    # the same number of forwards without the events, for comparison
     torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(steps):
+        blk.forward(x, w.start_pos, (k, v), out)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
     blk.close()
     del k, v, x, out
     torch.cuda.empty_cache()
     ms = (t1 - t0) * 1e3 / steps
+    ms_plain = (t3 - t2) * 1e3 / steps
     avg = {n: stage_ms[n] / max(calls, 1) for n in stage_ms}
-    return ms, avg, stream
+    return ms, avg, ms_plain
 
 
 def roofline(w, avg_ms, bound):
@@ -126,6 +129,56 @@ def roofline(w, avg_ms, bound):
         r = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
     return r, stages
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b.txt")
+KERNEL_SOURCES = os.path.join(ROOT, "decoder_only_transformer_amd", "csrc")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` on `workload` from the counter summary
+    under profiles/ (FETCH_SIZE and WRITE_SIZE, each scaled by its reading on a
+    plain copy of known size), or None when there is none or when the kernel
+    sources have changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha, rows = None, {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            p = line.split()
+            if not p or p[0].startswith("#"):
+                continue
+            if p[0] == "sources_sha256":
+                sha = p[1]
+            elif p[0] == "stage" and len(p) >= 4:
+                rows[(p[1], p[2])] = float(p[3])
+    if sha != kernel_sources_sha256():
+        return None
+    v = rows.get((workload, stage))
+    return None if v is None else int(round(v))
+
+
+def copy_only(mib):
+    """A plain device copy of known size (out = in * 1, fp32), three times: the
+    counter reading that scales FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}),
+          flush=True)
 
 
 def cpu_baseline(w, tokens):
@@ -159,6 +212,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -172,11 +227,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_only:
+        copy_only(args.copy_only)
+        return
 
     w = workloads.get(args.workload)
     log(f"[bench] prefill {w.name}: warmup {args.warmup}, steps {args.steps}")
-    ms, avg, _ = run_gpu(w, args.steps, args.warmup)
+    ms, avg, ms_plain = run_gpu(w, args.steps, args.warmup)
     roof, stages = roofline(w, avg, "mfma")
+    roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     total_flops = sum(v["flops"] for v in stage_work(w).values())
     result = {
         "metric": METRIC,
@@ -186,6 +245,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_without_stage_events": round(ms_plain, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -207,12 +267,14 @@ def main():
         wd = workloads.get(args.decode_workload)
         dsteps = args.decode_steps or 5 * args.steps
         log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {dsteps}")
-        dms, davg, _ = run_gpu(wd, dsteps, args.warmup)
+        dms, davg, dms_plain = run_gpu(wd, dsteps, args.warmup)
         droof, dstages = roofline(wd, davg, "hbm")
+        droof["traffic"] = measured_traffic(wd.name, droof["kernel"])
         total_bytes = sum(v["bytes"] for v in stage_work(wd).values())
         result["decode"] = {
             "workload": wd.name, "B": wd.B, "start_pos": wd.start_pos, "steps": dsteps,
             "us_per_step": round(dms * 1e3, 2),
+            "us_per_step_without_stage_events": round(dms_plain * 1e3, 2),
             "tokens_per_s": round(wd.M / (dms * 1e-3), 1),
             "block_gbs": round(total_bytes / (dms * 1e-3) / 1e9, 1),
             "block_hbm_frac": round(total_bytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

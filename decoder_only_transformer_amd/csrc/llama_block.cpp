@@ -452,7 +452,10 @@ extern "C" lb_status llama_block_profile(lb_block* blk, int enable) {
     if (!enable) return LB_OK;
     blk->events.resize((size_t)kProfileSlots * (LB_NUM_STAGES + 1));
     for (size_t i = 0; i < blk->events.size(); ++i) {
-        if (hipEventCreate(&blk->events[i]) != hipSuccess) {
+        // timing-only events: no system-scope fence (cache writeback and
+        // invalidate) when they are recorded, so they barely perturb the
+        // kernels between them
+        if (hipEventCreateWithFlags(&blk->events[i], hipEventDisableSystemFence) != hipSuccess) {
             blk->events.resize(i);
             profile_release(blk);
             return fail(blk, LB_ERR_HIP, "hipEventCreate failed");
