@@ -81,8 +81,9 @@ struct EpiResid {
 // up features of the same four.
 template <typename TO>
 struct EpiSwiGLU {
-    TO* z;    // [M][dff]
+    TO* z;    // [M][dff], or k-step tiled with mt row tiles when mt > 0
     int dff;
+    int mt;
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
         float r[4];
 #pragma unroll
@@ -90,7 +91,8 @@ struct EpiSwiGLU {
             const float a = v[e];
             r[e] = a / (1.0f + expf(-a)) * v[4 + e];
         }
-        store4(z + (size_t)m * dff + (n >> 1), r);
+        const int j = n >> 1;
+        store4(z + (mt > 0 ? ktile_act_off(m, j, mt) : (size_t)m * dff + j), r);
     }
 };
 

@@ -191,7 +191,8 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
     typedef typename vec8<T>::type V8;
     constexpr int COLS = 16 * CT;
     __shared__ float red[KW][MT * 16][COLS + 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * COLS, ks = blockIdx.y;
     const int nks = K / 32;
     // block ks owns the contiguous k-steps [ks*nks/KS, (ks+1)*nks/KS); inside
@@ -244,7 +245,7 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
     for (; c + 1 < nchunk; c += 2) {
         load(c + 1, 1);
         compute(c, 0);
-        if (c + 2 < nchunk) load(c + 2, 0);
+        load(c + 2, 0);  // unconditional: a branch here would make every wait a full drain
         compute(c + 1, 1);
     }
     if (c < nchunk) compute(c, 0);
@@ -269,6 +270,104 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
             }
             if (PARTIAL) store8(part + ((size_t)ks * M + row) * N + n, v);
             else epi.row8(row, n, v);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Decode GEMM over k-step-tiled operands (lb_device.h): A [MT row tiles][K],
+// W [N][K], both tiled, so every operand load of a wavefront is one contiguous
+// 1 KB piece (8 full cache lines).  Grid (N / (16*CT), KS), NW wavefronts per
+// block: the block owns CT 16-column tiles and the KS-th part of K; its
+// k-steps are cut into NW contiguous runs, one per wavefront, and every
+// wavefront streams its run of each of the CT weight tiles, U k-steps per
+// chunk with the next chunk's loads in flight (register double buffering).
+// Loads past the end of a run repeat a valid k-step and are discarded.  The
+// block sums its wavefronts in LDS in a fixed order; with KS == 1 it runs the
+// epilogue on rows < M, otherwise it stores an fp32 partial [ks][M][N] for
+// reduce_epilogue_kernel.  N % (16*CT) == 0, K % 32 == 0.
+// ------------------------------------------------------------------------------------
+template <typename T, int MT, int CT, int U, int NW, bool PARTIAL, class Epi>
+__global__ void __launch_bounds__(NW * 64) gemm_decode_kernel(const T* __restrict__ At,
+                                                              const T* __restrict__ Wt, int M,
+                                                              int N, int K, int KS,
+                                                              float* __restrict__ part, Epi epi) {
+    typedef typename vec8<T>::type V8;
+    constexpr int COLS = 16 * CT;
+    __shared__ float red[NW][MT * 16][COLS + 1];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nt0 = blockIdx.x * CT, ksp = blockIdx.y;
+    const int nks = K / 32;
+    const int kb0 = (int)((long)ksp * nks / KS), kb1 = (int)((long)(ksp + 1) * nks / KS);
+    const int w0 = kb0 + wave * (kb1 - kb0) / NW, w1 = kb0 + (wave + 1) * (kb1 - kb0) / NW;
+    const int n_my = w1 - w0;
+    const int nchunk = (n_my + U - 1) / U;
+    const T* wp[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) wp[c] = Wt + (size_t)(nt0 + c) * nks * 512 + lane * 8;
+    const T* ap = At + lane * 8;
+    f32x4 acc[MT][CT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[t][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    V8 bw[2][U][CT], aa[2][U][MT];
+    auto load = [&](int chunk, int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kstep = min(w0 + chunk * U + u, nks - 1);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) bw[s][u][c] = *reinterpret_cast<const V8*>(wp[c] + (size_t)kstep * 512);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                aa[s][u][t] = *reinterpret_cast<const V8*>(ap + ((size_t)kstep * MT + t) * 512);
+        }
+    };
+    auto compute = [&](int chunk, int s) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = chunk * U + u < n_my;
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                V8 a = aa[s][u][t];
+                if (!ok) a = V8{};
+#pragma unroll
+                for (int c = 0; c < CT; ++c) acc[t][c] = mfma16(a, bw[s][u][c], acc[t][c]);
+            }
+        }
+    };
+    if (nchunk > 0) load(0, 0);
+    int c = 0;
+    for (; c + 1 < nchunk; c += 2) {
+        load(c + 1, 1);
+        compute(c, 0);
+        load(c + 2, 0);  // unconditional: a branch here would make every wait a full drain
+        compute(c + 1, 1);
+    }
+    if (c < nchunk) compute(c, 0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int cc = 0; cc < CT; ++cc)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[wave][t * 16 + 4 * (lane >> 4) + r][cc * 16 + (lane & 15)] = acc[t][cc][r];
+    __syncthreads();
+    const int n0 = nt0 * 16;
+    for (int q = threadIdx.x; q < MT * 16 * (COLS / 8); q += NW * 64) {
+        const int row = q / (COLS / 8), c8 = q % (COLS / 8);
+        if (row < M) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float sacc = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sacc += red[w][row][c8 * 8 + e];
+                v[e] = sacc;
+            }
+            if (PARTIAL) store8(part + ((size_t)ksp * M + row) * N + n0 + c8 * 8, v);
+            else epi.row8(row, n0 + c8 * 8, v);
         }
     }
 }

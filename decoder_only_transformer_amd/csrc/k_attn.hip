@@ -457,7 +457,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restrict__ part,
                                                            T* __restrict__ o, int H, int nkv,
-                                                           int n_rep, int nsplit) {
+                                                           int n_rep, int nsplit, int o_mt) {
     __shared__ float wt[16][kDecodeMaxSplit];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bg = blockIdx.x, b = bg / nkv, g = bg % nkv;
@@ -489,7 +489,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
             o3 += pp[(size_t)(s + 3) * (DH + 2)] * wt[hh][s + 3];
         }
         for (; s < nsplit; ++s) o0 += pp[(size_t)s * (DH + 2)] * wt[hh][s];
-        o[(head0 + hh) * DH + d] = from_f32<T>((o0 + o1) + (o2 + o3));
+        const int col = (g * n_rep + hh) * DH + d;
+        o[o_mt > 0 ? ktile_act_off(b, col, o_mt) : (size_t)b * H * DH + col] =
+            from_f32<T>((o0 + o1) + (o2 + o3));
     }
 }
 
@@ -608,7 +610,7 @@ size_t decode_partials_floats(int max_batch, int H, int dh, int max_kv) {
 }
 
 template <typename T, int DH>
-static hipError_t decode_t(const AttnArgs& a, float* part, hipStream_t s) {
+static hipError_t decode_t(const AttnArgs& a, float* part, int o_mt, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
     const int kv_len = a.start_pos + 1;
     const int ch = decode_keys_per_wave(kv_len);
@@ -619,17 +621,18 @@ static hipError_t decode_t(const AttnArgs& a, float* part, hipStream_t s) {
         ch, nsplit, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attn_combine_kernel<T, DH><<<a.B * a.nkv, 256, 0, s>>>(part, (T*)a.o, a.H, a.nkv, n_rep, nsplit);
+    attn_combine_kernel<T, DH><<<a.B * a.nkv, 256, 0, s>>>(part, (T*)a.o, a.H, a.nkv, n_rep, nsplit, o_mt);
     return hipGetLastError();
 }
 
-hipError_t attn_decode(Elem op, Elem kv_t, const AttnArgs& a, float* part, hipStream_t s) {
+hipError_t attn_decode(Elem op, Elem kv_t, const AttnArgs& a, float* part, int o_mt, hipStream_t s) {
     if (a.B <= 0) return hipSuccess;
     if (kv_t != Elem::BF16 || a.S != 1 || a.H / a.nkv > 16) return hipErrorInvalidValue;
-    if (op == Elem::F16 && a.dh == 128) return decode_t<f16, 128>(a, part, s);
-    if (op == Elem::F16 && a.dh == 64) return decode_t<f16, 64>(a, part, s);
-    if (op == Elem::BF16 && a.dh == 128) return decode_t<bf16, 128>(a, part, s);
-    if (op == Elem::BF16 && a.dh == 64) return decode_t<bf16, 64>(a, part, s);
+    if (o_mt > 0 && a.B > 16 * o_mt) return hipErrorInvalidValue;
+    if (op == Elem::F16 && a.dh == 128) return decode_t<f16, 128>(a, part, o_mt, s);
+    if (op == Elem::F16 && a.dh == 64) return decode_t<f16, 64>(a, part, o_mt, s);
+    if (op == Elem::BF16 && a.dh == 128) return decode_t<bf16, 128>(a, part, o_mt, s);
+    if (op == Elem::BF16 && a.dh == 64) return decode_t<bf16, 64>(a, part, o_mt, s);
     return hipErrorInvalidValue;
 }
 

@@ -37,6 +37,51 @@ static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const 
     return hipGetLastError();
 }
 
+// Decode GEMM over k-step-tiled operands.  Wide outputs (>= 384 16-column
+// tiles) take two column tiles per wavefront, so a wavefront's activation
+// loads feed twice the weight bytes; narrower ones take one and split K
+// across blocks when there are fewer than 192 column tiles.
+int decode_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+template <typename T, int MT, class Epi>
+static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, const Epi& epi,
+                                const SplitWs& ws, hipStream_t s) {
+    const int tiles = N / 16, nks = K / 32;
+    if (tiles >= 384 && tiles % 2 == 0) {
+        gemm_decode_kernel<T, MT, 2, 2, 4, false, Epi><<<dim3(tiles / 2, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
+        return hipGetLastError();
+    }
+    int ks = 1;
+    if (tiles < 192) {
+        ks = (256 + tiles - 1) / tiles;
+        if (ks > kSkinnyMaxSplit) ks = kSkinnyMaxSplit;
+        if (ks > nks / 4) ks = nks / 4;  // at least one k-step per wavefront
+        while (ks > 1 && (size_t)ks * M * N > ws.cap) --ks;
+        if (ks < 1) ks = 1;
+    }
+    if (ks == 1) {
+        gemm_decode_kernel<T, MT, 1, 4, 4, false, Epi><<<dim3(tiles, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
+        return hipGetLastError();
+    }
+    gemm_decode_kernel<T, MT, 1, 4, 4, true, Epi><<<dim3(tiles, ks), 256, 0, s>>>(At, Wt, M, N, K, ks, ws.part, epi);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    reduce_epilogue_kernel<Epi><<<(M * (N / 8) + 255) / 256, 256, 0, s>>>(ws.part, M, N, ks, epi);
+    return hipGetLastError();
+}
+
+template <typename T, class Epi>
+static hipError_t run_decode(const T* At, const T* Wt, int M, int N, int K, const Epi& epi,
+                             const SplitWs& ws, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    if (M > 64 || N % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
+    switch (decode_row_tiles(M)) {
+        case 1: return run_decode_mt<T, 1>(At, Wt, M, N, K, epi, ws, s);
+        case 2: return run_decode_mt<T, 2>(At, Wt, M, N, K, epi, ws, s);
+        default: return run_decode_mt<T, 4>(At, Wt, M, N, K, epi, ws, s);
+    }
+}
+
 template <typename T, class Epi>
 static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Epi& epi,
                            const SplitWs& ws, hipStream_t s) {
@@ -125,6 +170,45 @@ hipError_t gemm_out(Elem op, Elem out_t, const void* A, const void* W, int M, in
         return run_gemm((const f16*)A, (const f16*)W, M, N, K, EpiOut<bf16>{h, (bf16*)y, N}, part, s);
     if (op == Elem::BF16 && out_t == Elem::BF16)
         return run_gemm((const bf16*)A, (const bf16*)W, M, N, K, EpiOut<bf16>{h, (bf16*)y, N}, part, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t decode_qkv(Elem op, Elem cache, const void* At, const void* Wt, int M, int N, int K,
+                      const QkvEpi& e, const SplitWs& part, hipStream_t s) {
+    if (op == Elem::F16 && cache == Elem::BF16)
+        return run_decode((const f16*)At, (const f16*)Wt, M, N, K, make_qkv<f16, bf16>(e), part, s);
+    if (op == Elem::BF16 && cache == Elem::BF16)
+        return run_decode((const bf16*)At, (const bf16*)Wt, M, N, K, make_qkv<bf16, bf16>(e), part, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t decode_resid(Elem op, Elem resid_t, const void* At, const void* Wt, int M, int N, int K,
+                        const void* resid, float* out, const SplitWs& part, hipStream_t s) {
+    if (resid_t != Elem::BF16) return hipErrorInvalidValue;
+    if (op == Elem::F16)
+        return run_decode((const f16*)At, (const f16*)Wt, M, N, K, EpiResid<bf16>{(const bf16*)resid, out, N}, part, s);
+    if (op == Elem::BF16)
+        return run_decode((const bf16*)At, (const bf16*)Wt, M, N, K, EpiResid<bf16>{(const bf16*)resid, out, N}, part, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t decode_swiglu(Elem op, const void* At, const void* Wt, int M, int N, int K, void* zt,
+                         const SplitWs& part, hipStream_t s) {
+    const int dff = N / 2, mt = decode_row_tiles(M);
+    if (op == Elem::F16)
+        return run_decode((const f16*)At, (const f16*)Wt, M, N, K, EpiSwiGLU<f16>{(f16*)zt, dff, mt}, part, s);
+    if (op == Elem::BF16)
+        return run_decode((const bf16*)At, (const bf16*)Wt, M, N, K, EpiSwiGLU<bf16>{(bf16*)zt, dff, mt}, part, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t decode_out(Elem op, Elem out_t, const void* At, const void* Wt, int M, int N, int K,
+                      const float* h, void* y, const SplitWs& part, hipStream_t s) {
+    if (out_t != Elem::BF16) return hipErrorInvalidValue;
+    if (op == Elem::F16)
+        return run_decode((const f16*)At, (const f16*)Wt, M, N, K, EpiOut<bf16>{h, (bf16*)y, N}, part, s);
+    if (op == Elem::BF16)
+        return run_decode((const bf16*)At, (const bf16*)Wt, M, N, K, EpiOut<bf16>{h, (bf16*)y, N}, part, s);
     return hipErrorInvalidValue;
 }
 

@@ -10,11 +10,13 @@ namespace lb {
 // over 32 CUs.  Each thread keeps its (up to 8) 8-element chunks in
 // registers; the sum of squares is accumulated in fp32 and reduced across
 // wavefronts (butterfly) and then across the block in a fixed order, so
-// results are deterministic.  d <= 16384 (d % 8 == 0).
+// results are deterministic.  d <= 16384 (d % 8 == 0).  out_mt > 0 stores
+// the row in the decode (k-step tiled) layout with out_mt row tiles.
 template <typename TI, typename TO>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const TI* __restrict__ x,
                                                       const float* __restrict__ g,
-                                                      TO* __restrict__ out, int M, int d, float eps) {
+                                                      TO* __restrict__ out, int M, int d, float eps,
+                                                      int out_mt) {
     __shared__ float part[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x;
@@ -44,8 +46,33 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const TI* __restrict__ x,
             load8(g + c, gg);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[i][e] = v[i][e] * r * gg[e];
-            store8(orow + c, v[i]);
+            store8(out_mt > 0 ? out + ktile_act_off(row, c, out_mt) : orow + c, v[i]);
         }
+    }
+}
+
+// One 16-byte chunk per thread: chunk q of the tiled layout comes from row
+// 16 * (piece / (K/32)) + q % 16, columns 32 * (piece % (K/32)) + 8 * (q % 64 / 16).
+template <typename T>
+__global__ void tile_weights_kernel(const T* __restrict__ src, T* __restrict__ dst, int N, int K) {
+    const size_t nch = (size_t)N * K / 8;
+    const int nks = K / 32;
+    for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < nch; q += (size_t)gridDim.x * blockDim.x) {
+        const int l = (int)(q & 63);
+        const size_t piece = q >> 6;
+        const size_t n = (piece / nks) * 16 + (l & 15);
+        const size_t k = (piece % nks) * 32 + 8 * (l >> 4);
+        *reinterpret_cast<u32x4*>(dst + q * 8) = *reinterpret_cast<const u32x4*>(src + n * K + k);
+    }
+}
+
+template <typename T>
+__global__ void untile_kernel(const T* __restrict__ src, T* __restrict__ dst, int M, int K, int mt) {
+    const size_t nch = (size_t)M * K / 8;
+    for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < nch; q += (size_t)gridDim.x * blockDim.x) {
+        const int m = (int)(q / (K / 8)), k = (int)(q % (K / 8)) * 8;
+        *reinterpret_cast<u32x4*>(dst + (size_t)m * K + k) =
+            *reinterpret_cast<const u32x4*>(src + ktile_act_off(m, k, mt));
     }
 }
 
@@ -70,16 +97,18 @@ __global__ void pack_gate_up_kernel(const TI* __restrict__ gate, const TI* __res
 
 template <typename TI, typename TO>
 static hipError_t rmsnorm_t(const void* x, const float* g, void* out, int M, int d, float eps,
-                            hipStream_t s) {
+                            int out_mt, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (d > 16384) return hipErrorInvalidValue;
-    rmsnorm_kernel<TI, TO><<<M, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps);
+    if (out_mt > 0 && (d % 32 != 0 || M > 16 * out_mt)) return hipErrorInvalidValue;
+    rmsnorm_kernel<TI, TO><<<M, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps, out_mt);
     return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(Elem in_t, Elem out_t, const void* x, const float* g, void* out, int M,
-                          int d, float eps, hipStream_t s) {
-#define RN(TI, TO) return rmsnorm_t<TI, TO>(x, g, out, M, d, eps, s)
+                          int d, float eps, int out_mt, hipStream_t s) {
+    if (out_mt > 0 && out_t == Elem::F32) return hipErrorInvalidValue;
+#define RN(TI, TO) return rmsnorm_t<TI, TO>(x, g, out, M, d, eps, out_mt, s)
     if (in_t == Elem::F32 && out_t == Elem::F32) RN(float, float);
     if (in_t == Elem::F32 && out_t == Elem::F16) RN(float, f16);
     if (in_t == Elem::F32 && out_t == Elem::BF16) RN(float, bf16);
@@ -87,6 +116,23 @@ hipError_t launch_rmsnorm(Elem in_t, Elem out_t, const void* x, const float* g, 
     if (in_t == Elem::BF16 && out_t == Elem::BF16) RN(bf16, bf16);
 #undef RN
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_tile_weights(Elem t, const void* src, void* dst, int N, int K, hipStream_t s) {
+    if (t == Elem::F32 || N % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
+    if (N <= 0) return hipSuccess;
+    size_t blocks = ((size_t)N * K / 8 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    tile_weights_kernel<f16><<<(unsigned)blocks, 256, 0, s>>>((const f16*)src, (f16*)dst, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_untile(Elem t, const void* src, void* dst, int M, int K, int mt, hipStream_t s) {
+    if (t == Elem::F32 || K % 32 != 0 || mt <= 0 || M > 16 * mt) return hipErrorInvalidValue;
+    if (M <= 0) return hipSuccess;
+    const size_t blocks = ((size_t)M * K / 8 + 255) / 256;
+    untile_kernel<f16><<<(unsigned)blocks, 256, 0, s>>>((const f16*)src, (f16*)dst, M, K, mt);
+    return hipGetLastError();
 }
 
 template <typename TI, typename TO>

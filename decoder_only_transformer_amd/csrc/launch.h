@@ -13,9 +13,14 @@ enum class Elem : int { F32 = 0, BF16 = 1, F16 = 2 };
 inline size_t elem_bytes(Elem e) { return e == Elem::F32 ? 4 : 2; }
 
 // ---- small kernels ------------------------------------------------------------
-// out[m][:] = x[m][:] / sqrt(mean(x[m]^2) + eps) * g  (fp32 arithmetic, one rounding)
+// out[m][:] = x[m][:] / sqrt(mean(x[m]^2) + eps) * g  (fp32 arithmetic, one rounding);
+// out_mt > 0 writes out in the decode (k-step tiled) layout with out_mt row tiles.
 hipError_t launch_rmsnorm(Elem in_t, Elem out_t, const void* x, const float* g, void* out, int M,
-                          int d, float eps, hipStream_t s);
+                          int d, float eps, int out_mt, hipStream_t s);
+// Weights [N][K] (16-bit) -> the decode (k-step tiled) layout; N % 16 == 0, K % 32 == 0.
+hipError_t launch_tile_weights(Elem t, const void* src, void* dst, int N, int K, hipStream_t s);
+// Activations in the decode layout (mt row tiles) -> [M][K] row-major.
+hipError_t launch_untile(Elem t, const void* src, void* dst, int M, int K, int mt, hipStream_t s);
 // dst[i] = src[i] converted (round to nearest even)
 hipError_t launch_convert(Elem src_t, Elem dst_t, const void* src, void* dst, size_t n,
                           hipStream_t s);
@@ -55,6 +60,19 @@ hipError_t gemm_swiglu(Elem op, const void* A, const void* W, int M, int N, int 
 hipError_t gemm_out(Elem op, Elem out_t, const void* A, const void* W, int M, int N, int K,
                     const float* h, void* y, const SplitWs& part, hipStream_t s);
 
+// ---- decode GEMMs: M <= 64 token rows, A and W in the k-step tiled layout ---------
+// (lb_device.h).  A has decode_row_tiles(M) row tiles.
+int decode_row_tiles(int M);
+hipError_t decode_qkv(Elem op, Elem cache, const void* At, const void* Wt, int M, int N, int K,
+                      const QkvEpi& e, const SplitWs& part, hipStream_t s);
+hipError_t decode_resid(Elem op, Elem resid_t, const void* At, const void* Wt, int M, int N, int K,
+                        const void* resid, float* out, const SplitWs& part, hipStream_t s);
+// z is written in the tiled layout (decode_row_tiles(M) row tiles, dff = N / 2 columns)
+hipError_t decode_swiglu(Elem op, const void* At, const void* Wt, int M, int N, int K, void* zt,
+                         const SplitWs& part, hipStream_t s);
+hipError_t decode_out(Elem op, Elem out_t, const void* At, const void* Wt, int M, int N, int K,
+                      const float* h, void* y, const SplitWs& part, hipStream_t s);
+
 // ---- attention --------------------------------------------------------------------
 struct AttnArgs {
     const void* q;   // [B*S][H*dh] operand type (fp32 for fp32 blocks)
@@ -70,7 +88,8 @@ hipError_t attn_prefill(Elem op, Elem kv_t, const AttnArgs& a, hipStream_t s);
 // Split-K decode attention (seq_len == 1) over a bf16/fp16 cache, then the
 // merge of the splits into o.  part: workspace of decode_partials_floats().
 size_t decode_partials_floats(int max_batch, int H, int dh, int max_kv);
-hipError_t attn_decode(Elem op, Elem kv_t, const AttnArgs& a, float* part, hipStream_t s);
+// o_mt > 0 writes o in the decode (k-step tiled) layout with o_mt row tiles.
+hipError_t attn_decode(Elem op, Elem kv_t, const AttnArgs& a, float* part, int o_mt, hipStream_t s);
 
 // Plain fp32 attention (fp32 blocks, any seq_len).
 hipError_t attn_simple(const AttnArgs& a, hipStream_t s);

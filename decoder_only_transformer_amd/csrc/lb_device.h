@@ -104,6 +104,25 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ---- decode operand layout -------------------------------------------------------
+// Token-batch GEMMs of the decode path read their operands in "k-step tiles":
+// for an operand with rows r (tokens or weight rows) and K columns, the 16
+// rows of row tile rt and the 32 columns of k-step ks form one contiguous
+// 1 KB piece whose 16-byte chunk l (l = 16 * (k % 32 / 8) + r % 16) is
+// exactly what lane l of a 16x16x32 MFMA operand needs.
+//   activations [M rows, MT row tiles]: piece (ks * MT + rt)
+//   weights     [N rows]:               piece (rt * (K / 32) + ks)
+// Element offset of (r, k) inside its piece:
+__host__ __device__ __forceinline__ int ktile_in_piece(int r, int k) {
+    return ((((k >> 3) & 3) << 4) + (r & 15)) * 8 + (k & 7);
+}
+__host__ __device__ __forceinline__ size_t ktile_act_off(int m, int k, int mt) {
+    return ((size_t)(k >> 5) * mt + (m >> 4)) * 512 + ktile_in_piece(m, k);
+}
+__host__ __device__ __forceinline__ size_t ktile_w_off(int n, int k, int K) {
+    return ((size_t)(n >> 4) * (K >> 5) + (k >> 5)) * 512 + ktile_in_piece(n, k);
+}
+
 // 8-element operand vector of a 16-bit type.
 template <typename T> struct vec8;
 template <> struct vec8<f16> { typedef f16x8 type; };

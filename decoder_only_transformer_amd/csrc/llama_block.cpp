@@ -34,6 +34,11 @@ struct lb_block {
     void* w_o = nullptr;
     void* w_gu = nullptr;
     void* w_down = nullptr;
+    // the same weights in the decode (k-step tiled) layout, bf16 blocks only
+    void* wt_qkv = nullptr;
+    void* wt_o = nullptr;
+    void* wt_gu = nullptr;
+    void* wt_down = nullptr;
     float* g1 = nullptr;
     float* g2 = nullptr;
     float2* rope = nullptr;
@@ -50,6 +55,13 @@ struct lb_block {
     float* part = nullptr;       // decode attention partials
     float* gpart = nullptr;      // split-K decode GEMM partials
     size_t gpart_cap = 0;        // floats
+    // decode activations (<= kDecodeRows token rows) in the k-step tiled layout
+    void* at_n1 = nullptr;
+    void* at_o = nullptr;
+    void* at_n2 = nullptr;
+    void* at_z = nullptr;
+    int last_mt = 0;             // row tiles of the last forward's tiled activations (0: none)
+    int last_m = 0;
     std::vector<void*> allocs;
     std::string err;
     // per-stage timing: a ring of event sets, LB_NUM_STAGES + 1 events each
@@ -62,6 +74,7 @@ struct lb_block {
 };
 
 static constexpr int kProfileSlots = 256;
+static constexpr int kDecodeRows = 64;  // largest decode batch that runs on the tiled GEMMs
 
 static void profile_release(lb_block* blk) {
     for (hipEvent_t e : blk->events) hipEventDestroy(e);
@@ -217,7 +230,15 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
                     lb::decode_partials_floats(c.max_tokens, c.n_heads, dh, c.max_seq_len) * sizeof(float)) &&
              dalloc(blk, &blk->gpart, (blk->gpart_cap = lb::skinny_partials_floats(
                                            c.max_tokens < 64 ? c.max_tokens : 64,
-                                           std::max(std::max(blk->nqkv, d), 2 * dff))) * sizeof(float));
+                                           std::max(std::max(blk->nqkv, d), 2 * dff))) * sizeof(float)) &&
+             dalloc(blk, &blk->wt_qkv, (size_t)blk->nqkv * d * eo) &&
+             dalloc(blk, &blk->wt_o, (size_t)d * blk->qd * eo) &&
+             dalloc(blk, &blk->wt_gu, (size_t)2 * dff * d * eo) &&
+             dalloc(blk, &blk->wt_down, (size_t)d * dff * eo) &&
+             dalloc(blk, &blk->at_n1, (size_t)kDecodeRows * d * eo) &&
+             dalloc(blk, &blk->at_o, (size_t)kDecodeRows * blk->qd * eo) &&
+             dalloc(blk, &blk->at_n2, (size_t)kDecodeRows * d * eo) &&
+             dalloc(blk, &blk->at_z, (size_t)kDecodeRows * dff * eo);
     }
     if (!ok) {
         free_all(blk);
@@ -250,6 +271,18 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
     if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wo, blk->w_o, (size_t)d * blk->qd, s);
     if (e == hipSuccess) e = lb::launch_pack_gate_up(dt, op, w->w_gate, w->w_up, blk->w_gu, dff, d, s);
     if (e == hipSuccess) e = lb::launch_convert(dt, op, w->w_down, blk->w_down, (size_t)d * dff, s);
+    if (e == hipSuccess && dt == Elem::BF16) {
+        e = lb::launch_tile_weights(op, blk->w_qkv, blk->wt_qkv, blk->nqkv, d, s);
+        if (e == hipSuccess) e = lb::launch_tile_weights(op, blk->w_o, blk->wt_o, d, blk->qd, s);
+        if (e == hipSuccess) e = lb::launch_tile_weights(op, blk->w_gu, blk->wt_gu, 2 * dff, d, s);
+        if (e == hipSuccess) e = lb::launch_tile_weights(op, blk->w_down, blk->wt_down, d, dff, s);
+        // rows past a decode batch are read by the GEMMs (their results are
+        // dropped): start them at zero
+        if (e == hipSuccess) e = hipMemsetAsync(blk->at_n1, 0, (size_t)kDecodeRows * d * eo, s);
+        if (e == hipSuccess) e = hipMemsetAsync(blk->at_o, 0, (size_t)kDecodeRows * blk->qd * eo, s);
+        if (e == hipSuccess) e = hipMemsetAsync(blk->at_n2, 0, (size_t)kDecodeRows * d * eo, s);
+        if (e == hipSuccess) e = hipMemsetAsync(blk->at_z, 0, (size_t)kDecodeRows * dff * eo, s);
+    }
     if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->attn_norm, blk->g1, (size_t)d, s);
     if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->ffn_norm, blk->g2, (size_t)d, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
@@ -306,8 +339,18 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     }
     auto mark = [&](int i) { if (ev) hipEventRecord(ev[i], s); };
 
+    // decode batches of <= kDecodeRows sequences run the weight-streaming
+    // GEMMs on k-step tiled activations and weights
+    const bool dec = dt == Elem::BF16 && S == 1 && M <= kDecodeRows;
+    const int mt = dec ? lb::decode_row_tiles(M) : 0;
+    const lb::SplitWs ws{blk->gpart, blk->gpart_cap};
+    void* n1 = dec ? blk->at_n1 : blk->n1;
+    void* o = dec ? blk->at_o : blk->o;
+    void* n2 = dec ? blk->at_n2 : blk->n2;
+    void* z = dec ? blk->at_z : blk->z;
+
     mark(0);
-    e = lb::launch_rmsnorm(dt, op, x, blk->g1, blk->n1, M, d, (float)c.norm_eps, s);
+    e = lb::launch_rmsnorm(dt, op, x, blk->g1, n1, M, d, (float)c.norm_eps, mt, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_1: %s", hipGetErrorString(e));
 
     const bool ws_kv = (dt == Elem::BF16) && S > 1 && start_pos == 0;
@@ -327,12 +370,13 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     qe.dh = dh;
     qe.qd = blk->qd;
     mark(1);
-    e = lb::gemm_qkv(op, dt, blk->n1, blk->w_qkv, M, blk->nqkv, d, qe, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
+    if (dec) e = lb::decode_qkv(op, dt, n1, blk->wt_qkv, M, blk->nqkv, d, qe, ws, s);
+    else e = lb::gemm_qkv(op, dt, n1, blk->w_qkv, M, blk->nqkv, d, qe, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "qkv projection: %s", hipGetErrorString(e));
 
     lb::AttnArgs a;
     a.q = blk->q;
-    a.o = blk->o;
+    a.o = o;
     a.B = B;
     a.S = S;
     a.start_pos = start_pos;
@@ -350,22 +394,27 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     }
     mark(2);
     if (dt == Elem::F32) e = lb::attn_simple(a, s);
-    else if (S == 1) e = lb::attn_decode(op, dt, a, blk->part, s);
+    else if (S == 1) e = lb::attn_decode(op, dt, a, blk->part, mt, s);
     else e = lb::attn_prefill(op, ws_kv ? op : dt, a, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "attention: %s", hipGetErrorString(e));
 
     mark(3);
-    e = lb::gemm_resid(op, dt, blk->o, blk->w_o, M, d, blk->qd, x, blk->h, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
+    if (dec) e = lb::decode_resid(op, dt, o, blk->wt_o, M, d, blk->qd, x, blk->h, ws, s);
+    else e = lb::gemm_resid(op, dt, o, blk->w_o, M, d, blk->qd, x, blk->h, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "o projection: %s", hipGetErrorString(e));
     mark(4);
-    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, blk->g2, blk->n2, M, d, (float)c.norm_eps, s);
+    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, blk->g2, n2, M, d, (float)c.norm_eps, mt, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_2: %s", hipGetErrorString(e));
     mark(5);
-    e = lb::gemm_swiglu(op, blk->n2, blk->w_gu, M, 2 * dff, d, blk->z, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
+    if (dec) e = lb::decode_swiglu(op, n2, blk->wt_gu, M, 2 * dff, d, z, ws, s);
+    else e = lb::gemm_swiglu(op, n2, blk->w_gu, M, 2 * dff, d, z, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "gate/up projection: %s", hipGetErrorString(e));
     mark(6);
-    e = lb::gemm_out(op, dt, blk->z, blk->w_down, M, d, dff, blk->h, out, lb::SplitWs{blk->gpart, blk->gpart_cap}, s);
+    if (dec) e = lb::decode_out(op, dt, z, blk->wt_down, M, d, dff, blk->h, out, ws, s);
+    else e = lb::gemm_out(op, dt, z, blk->w_down, M, d, dff, blk->h, out, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "down projection: %s", hipGetErrorString(e));
+    blk->last_mt = mt;
+    blk->last_m = M;
     mark(7);
     return LB_OK;
 }
@@ -438,6 +487,16 @@ extern "C" lb_status llama_block_copy_stage(lb_block* blk, lb_stage which, void*
         return fail(blk, LB_ERR_INVALID_ARG, "bad stage or NULL destination");
     const size_t cap = (size_t)blk->cfg.max_tokens * (size_t)cols * esz(e);
     if (bytes > cap) return fail(blk, LB_ERR_INVALID_ARG, "%zu bytes exceed the stage buffer (%zu)", bytes, cap);
+    if (blk->last_mt > 0 && which != LB_STAGE_Q && which != LB_STAGE_H) {
+        // the last forward was a decode: this stage lives in the tiled layout;
+        // lay it out row-major in the (idle) prefill buffer first
+        const void* t = which == LB_STAGE_N1 ? blk->at_n1
+                        : which == LB_STAGE_O ? blk->at_o
+                        : which == LB_STAGE_N2 ? blk->at_n2 : blk->at_z;
+        hipError_t err = lb::launch_untile(e, t, const_cast<void*>(p), blk->last_m, (int)cols, blk->last_mt,
+                                           (hipStream_t)stream);
+        if (err != hipSuccess) return fail(blk, LB_ERR_HIP, "copy_stage: %s", hipGetErrorString(err));
+    }
     hipError_t err = hipMemcpyAsync(dst, p, bytes, hipMemcpyDefault, (hipStream_t)stream);
     if (err != hipSuccess) return fail(blk, LB_ERR_HIP, "copy_stage: %s", hipGetErrorString(err));
     return LB_OK;
