@@ -84,7 +84,7 @@ def lib() -> ctypes.CDLL:
         L.llama_block_stage_info.restype = ctypes.c_int
         L.llama_block_copy_stage.argtypes = [vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
         L.llama_block_copy_stage.restype = ctypes.c_int
-        L.llama_block_profile.argtypes = [vp, ctypes.c_int]
+        L.llama_block_profile.argtypes = [vp, ctypes.c_uint32]
         L.llama_block_profile.restype = ctypes.c_int
         L.llama_block_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_int64)]
@@ -160,8 +160,17 @@ def llama_block_copy_stage(handle: int, stage: str, dst, stream=None) -> None:
     _check(handle, st, "llama_block_copy_stage")
 
 
-def llama_block_profile(handle: int, enable: bool) -> None:
-    _check(handle, lib().llama_block_profile(handle, int(bool(enable))), "llama_block_profile")
+PROFILE_ALL = (1 << len(STAGE_NAMES)) - 1
+
+
+def llama_block_profile(handle: int, stages=PROFILE_ALL) -> None:
+    """Time the given stages on every following forward: a bit mask, or an
+    iterable of stage names; 0 / False / empty stops."""
+    if stages is True:
+        stages = PROFILE_ALL
+    if isinstance(stages, (list, tuple, set, frozenset)):
+        stages = sum(1 << STAGE_NAMES.index(n) for n in stages)
+    _check(handle, lib().llama_block_profile(handle, int(stages)), "llama_block_profile")
 
 
 def llama_block_profile_read(handle: int) -> Tuple[Dict[str, float], int]:

@@ -1,8 +1,10 @@
 // GEMM kernels: C[M][N] = A[M][K] . W[N][K]^T with fp32 accumulation, results
 // handed to an epilogue (epilogues.h) in 8-column chunks.
 //
-//  gemm_mfma_kernel   prefill: 32x32x16 MFMA tiles, direct-to-LDS loads,
-//                     LDS double buffering
+//  gemm_big_kernel    prefill, large: 256 x 256/192 tiles, 16x16x32 MFMA,
+//                     four-stage LDS ring of direct-to-LDS loads
+//  gemm_mfma_kernel   prefill, small: 32x32x16 MFMA tiles, direct-to-LDS
+//                     loads, LDS double buffering
 //  gemm_skinny_kernel decode (M <= 64): 16x16x32 MFMA, split-K over waves
 //                     and blocks, weights streamed from HBM straight into
 //                     MFMA operands (+ reduce_epilogue_kernel)
@@ -17,8 +19,9 @@ namespace lb {
 // Prefill GEMM.  Block tile BM x BN x 64, NW wavefronts in a (BM/WM) x (BN/WN)
 // grid, each computing WM x WN with (WM/32)*(WN/32) accumulator tiles.
 // A and W tiles live in LDS as [rows][64] with the 16-byte chunk index XORed
-// by (row & 7): the 8 lanes of one ds_read_b128 phase read 8 different rows
-// at one logical chunk and hit 8 different bank groups.  Tiles are fetched
+// by (row / 2) & 7: the 16 lanes of one ds_read_b128 phase (64 banks of 4
+// bytes) read 16 consecutive rows at one logical chunk and hit 16 different
+// 16-byte bank groups.  Tiles are fetched
 // straight from global memory into LDS (global_load_lds_dwordx4, no VGPR
 // staging): instruction i of wavefront w fills the 64 consecutive 16-byte
 // LDS slots starting at (i*NW + w)*64, lane l the slot l, so every lane loads
@@ -70,12 +73,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
     const T* bbase[BCH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-        const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ (row & 7);
+        const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
         abase[i] = A + (size_t)min(m0 + row, M - 1) * K + c * 8;
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-        const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ (row & 7);
+        const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
         bbase[i] = W + (size_t)min(n0 + row, N - 1) * K + c * 8;
     }
     auto gload = [&](int k0, int buf) {
@@ -114,12 +117,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int row = wm * WM + i * 32 + (lane & 31);
-                af[i] = *reinterpret_cast<const V8*>(la + row * BK + ((kc ^ (row & 7)) << 3));
+                af[i] = *reinterpret_cast<const V8*>(la + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = wn * WN + j * 32 + (lane & 31);
-                bfr[j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ (row & 7)) << 3));
+                bfr[j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -161,6 +164,179 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
                 const f32x4 b = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8 + 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+                epi.row8(m, n, v);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Large prefill GEMM.  Block tile 256 x BN (BN = 256 or 192), BK = 32, four
+// wavefronts in a 2 x 2 grid, each 128 x BN/2 with 16x16x32 MFMAs (8 x BN/32
+// accumulator tiles, all in AGPRs; one wavefront per SIMD).  A four-stage
+// LDS ring is filled by direct-to-LDS loads issued from inline assembly (so
+// the compiler's counters for LDS reads stay exact; the kernel waits for
+// the loads itself).  Each k-step runs its MFMAs in two halves with the one
+// barrier of the step between them: after it, stage k+1 is complete for
+// every wavefront and the second half reads the next step's operands under
+// its MFMAs; the loads of stage k+3 are spread over both halves.  LDS rows
+// are 64 bytes (4 chunks) with chunk index XORed by (row / 4) & 3: a
+// 16-lane phase reads 16 rows at one logical chunk without bank conflicts.
+// Rows beyond M / N are clamped to the last valid row.  K % 64 == 0.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ void lds_dma16(const void* g, unsigned lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte_addr)
+                 : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+template <typename T, int BN, class Epi>
+__global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
+                                                      const T* __restrict__ W, int M, int N,
+                                                      int K, Epi epi) {
+    typedef typename vec8<T>::type V8;
+    constexpr int STAGES = 4, BM = 256, BK = 32, NW = 4, NT = 256, WM = 128, WN = BN / 2;
+    constexpr int TI = WM / 16, TJ = WN / 16;
+    constexpr int SA = BM * BK, SB = BN * BK, STG = SA + SB;  // elements per stage
+    constexpr int NA = BM * BK / 8 / NT, NB = BN * BK / 8 / NT; // loads per thread per stage
+    constexpr int ND = NA + NB, H0 = (ND + 1) / 2;
+    constexpr int EPR = 64, CPAD = BN + 8;
+    static_assert(NA * NT * 8 == SA && NB * NT * 8 == SB, "whole load instructions");
+    static_assert(EPR * CPAD * 4 <= STAGES * STG * (int)sizeof(T), "epilogue stage fits");
+    __shared__ __attribute__((aligned(16))) T lds[STAGES * STG];
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (bid / per_group) * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int in_group = bid % per_group;
+    const int tm = first_m + in_group % gsize;
+    const int tn = in_group / gsize;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    // load d of a stage: instruction (d % NA or d - NA) of this wavefront fills
+    // 64 consecutive 16-byte slots; lane l the slot l
+    const T* gsrc[ND];
+    unsigned ldst[ND];
+    const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)lds;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+        const bool isa = d < NA;
+        const int slot0 = ((isa ? d : d - NA) * NW + wave) * 64;
+        const int p = slot0 + lane, row = p >> 2, c = (p & 3) ^ ((row >> 2) & 3);
+        gsrc[d] = isa ? A + (size_t)min(m0 + row, M - 1) * K + c * 8
+                      : W + (size_t)min(n0 + row, N - 1) * K + c * 8;
+        ldst[d] = lds0 + (unsigned)(((isa ? 0 : SA) + slot0 * 8) * (int)sizeof(T));
+    }
+    const int nk = K / BK;
+    // k-steps past the end reload the last one into a stage nobody reads
+    auto dma = [&](int kstep, int d) {
+        const int ks = kstep < nk ? kstep : nk - 1;
+        lds_dma16(gsrc[d] + ks * BK, ldst[d] + (unsigned)((kstep % STAGES) * STG * (int)sizeof(T)));
+    };
+    f32x4 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    V8 af[2][TI], bf[2][TJ];
+    // 16x16x32 operand: lane l holds row l % 16 and logical chunk l / 16
+    auto rd_a = [&](int kstep, int fb, int i) {
+        const T* la = lds + (kstep % STAGES) * STG;
+        const int row = wm * WM + i * 16 + (lane & 15), kc = lane >> 4;
+        af[fb][i] = *reinterpret_cast<const V8*>(la + row * BK + ((kc ^ ((row >> 2) & 3)) << 3));
+    };
+    auto rd_b = [&](int kstep, int fb, int j) {
+        const T* lb = lds + (kstep % STAGES) * STG + SA;
+        const int row = wn * WN + j * 16 + (lane & 15), kc = lane >> 4;
+        bf[fb][j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ ((row >> 2) & 3)) << 3));
+    };
+
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st)
+#pragma unroll
+        for (int d = 0; d < ND; ++d) dma(st, d);
+    wait_vm<2 * ND>();  // stage 0 has landed
+    asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < TI; ++i) rd_a(0, 0, i);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) rd_b(0, 0, j);
+
+    // one k-step; fb (the operand buffer) is a constant after inlining
+    auto step = [&](const int kt, const int fb) {
+        const int kd = kt + STAGES - 1;
+#pragma unroll
+        for (int i = 0; i < TI / 2; ++i) {
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[fb][i], bf[fb][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = i; d < H0; d += TI / 2) dma(kd, d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // stage kt+1 complete: only stage kt+2 and the first loads of kd may fly
+        wait_vm<ND + H0>();
+        asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+        for (int i = TI / 2; i < TI; ++i) {
+            const int g = i - TI / 2;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[fb][i], bf[fb][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int d = H0 + g; d < ND; d += TI / 2) dma(kd, d);
+            rd_a(kt + 1, fb ^ 1, 2 * g);
+            rd_a(kt + 1, fb ^ 1, 2 * g + 1);
+#pragma unroll
+            for (int j = g; j < TJ; j += TI / 2) rd_b(kt + 1, fb ^ 1, j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, 0);
+        step(kt + 1, 1);
+    }
+    wait_vm<0>();
+    __syncthreads();
+
+    // Epilogue: stage EPR rows of the fp32 tile through LDS, then hand
+    // contiguous 8-column chunks to the epilogue.
+    float* cst = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int p = 0; p < BM / EPR; ++p) {
+        if (wm == (p * EPR) / WM) {
+#pragma unroll
+            for (int ii = 0; ii < EPR / 16; ++ii) {
+                const int i = ((p * EPR) % WM) / 16 + ii;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        cst[(ii * 16 + 4 * (lane >> 4) + r) * CPAD + wn * WN + j * 16 + (lane & 15)] = acc[i][j][r];
+            }
+        }
+        __syncthreads();
+        for (int c = tid; c < EPR * (BN / 8); c += NT) {
+            const int row = c / (BN / 8), c8 = c % (BN / 8);
+            const int m = m0 + p * EPR + row, n = n0 + c8 * 8;
+            if (m < M && n < N) {
+                float v[8];
+                const f32x4 a = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = a[e];
+                    v[4 + e] = b[e];
+                }
                 epi.row8(m, n, v);
             }
         }

@@ -66,6 +66,7 @@ struct lb_block {
     std::string err;
     // per-stage timing: a ring of event sets, LB_NUM_STAGES + 1 events each
     bool profiling = false;
+    uint32_t profile_mask = 0;
     std::vector<hipEvent_t> events;
     std::vector<int> pending;      // ring slots recorded but not yet summed
     int next_slot = 0;
@@ -84,11 +85,19 @@ static void profile_release(lb_block* blk) {
 }
 
 // Sum one recorded slot into the per-stage totals (waits for its events).
+// event i is recorded when stage i or stage i-1 is timed
+static bool mark_needed(uint32_t mask, int i) {
+    return ((mask >> i) & 1u) || (i > 0 && ((mask >> (i - 1)) & 1u));
+}
+
 static hipError_t profile_collect(lb_block* blk, int slot) {
     hipEvent_t* ev = &blk->events[(size_t)slot * (LB_NUM_STAGES + 1)];
-    hipError_t e = hipEventSynchronize(ev[LB_NUM_STAGES]);
+    int last = LB_NUM_STAGES;
+    while (last > 0 && !mark_needed(blk->profile_mask, last)) --last;
+    hipError_t e = hipEventSynchronize(ev[last]);
     if (e != hipSuccess) return e;
     for (int i = 0; i < LB_NUM_STAGES; ++i) {
+        if (!((blk->profile_mask >> i) & 1u)) continue;
         float ms = 0.0f;
         e = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
         if (e != hipSuccess) return e;
@@ -337,7 +346,10 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
         blk->pending.push_back(slot);
         blk->next_slot = (slot + 1) % kProfileSlots;
     }
-    auto mark = [&](int i) { if (ev) hipEventRecord(ev[i], s); };
+    const uint32_t pmask = blk->profile_mask;
+    auto mark = [&](int i) {
+        if (ev && mark_needed(pmask, i)) hipEventRecord(ev[i], s);
+    };
 
     // decode batches of <= kDecodeRows sequences run the weight-streaming
     // GEMMs on k-step tiled activations and weights
@@ -502,13 +514,15 @@ extern "C" lb_status llama_block_copy_stage(lb_block* blk, lb_stage which, void*
     return LB_OK;
 }
 
-extern "C" lb_status llama_block_profile(lb_block* blk, int enable) {
+extern "C" lb_status llama_block_profile(lb_block* blk, uint32_t stage_mask) {
     if (!blk) return LB_ERR_INVALID_ARG;
     profile_release(blk);
     for (double& v : blk->stage_ms) v = 0.0;
     blk->profiled_calls = 0;
     blk->next_slot = 0;
-    if (!enable) return LB_OK;
+    stage_mask &= LB_PROFILE_ALL;
+    blk->profile_mask = stage_mask;
+    if (!stage_mask) return LB_OK;
     blk->events.resize((size_t)kProfileSlots * (LB_NUM_STAGES + 1));
     for (size_t i = 0; i < blk->events.size(); ++i) {
         // timing-only events: no system-scope fence (cache writeback and

@@ -151,16 +151,20 @@ lb_status llama_block_stage_info(const lb_block* blk, lb_stage which, lb_elem* e
 lb_status llama_block_copy_stage(lb_block* blk, lb_stage which, void* dst, size_t bytes,
                                  void* stream);
 
-/* Per-stage GPU timing.  While enabled, each forward records HIP events on
- * its stream between its stages:
+/* Per-stage GPU timing.  While enabled, each forward records HIP events
+ * (timing only, no system-scope fence) on its stream at the boundaries of the
+ * selected stages:
  *   0 RMSNorm_1   1 q/k/v projection (+RoPE, cache append)   2 attention
  *   3 o projection (+x)   4 RMSNorm_2   5 gate/up (+SiLU*up)   6 down (+h)
- * llama_block_profile(blk, 1) resets the sums and starts recording; 0 stops.
- * llama_block_profile_read waits for the recorded events and returns the
- * summed milliseconds per stage in stage_ms[0..n) (n <= LB_NUM_STAGES) and
- * the number of profiled forwards in *calls. */
+ * llama_block_profile(blk, mask) resets the sums and times the stages whose
+ * bit is set in mask (LB_PROFILE_ALL: every stage; 0 stops).  Fewer stages
+ * mean fewer events between kernels.  llama_block_profile_read waits for the
+ * recorded events and returns the summed milliseconds per stage in
+ * stage_ms[0..n) (n <= LB_NUM_STAGES; 0 for stages not timed) and the number
+ * of profiled forwards in *calls. */
 #define LB_NUM_STAGES 7
-lb_status llama_block_profile(lb_block* blk, int enable);
+#define LB_PROFILE_ALL ((1u << LB_NUM_STAGES) - 1u)
+lb_status llama_block_profile(lb_block* blk, uint32_t stage_mask);
 lb_status llama_block_profile_read(lb_block* blk, double* stage_ms, int n, int64_t* calls);
 
 #ifdef __cplusplus
