@@ -1,7 +1,7 @@
 // GEMM kernels: C[M][N] = A[M][K] . W[N][K]^T with fp32 accumulation, results
 // handed to an epilogue (epilogues.h) in 8-column chunks.
 //
-//  gemm_big_kernel    prefill, large: 256 x 256/192 tiles, 16x16x32 MFMA,
+//  gemm_big_kernel    prefill, large: 256 x 256 tiles, 16x16x32 MFMA,
 //                     four-stage LDS ring of direct-to-LDS loads
 //  gemm_mfma_kernel   prefill, small: 32x32x16 MFMA tiles, direct-to-LDS
 //                     loads, LDS double buffering
@@ -172,7 +172,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
 }
 
 // ------------------------------------------------------------------------------------
-// Large prefill GEMM.  Block tile 256 x BN (BN = 256 or 192), BK = 32, four
+// Large prefill GEMM.  Block tile 256 x BN (BN = 256), BK = 32, four
 // wavefronts in a 2 x 2 grid, each 128 x BN/2 with 16x16x32 MFMAs (8 x BN/32
 // accumulator tiles, all in AGPRs; one wavefront per SIMD).  A four-stage
 // LDS ring is filled by direct-to-LDS loads issued from inline assembly (so
@@ -185,11 +185,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
 // 16-lane phase reads 16 rows at one logical chunk without bank conflicts.
 // Rows beyond M / N are clamped to the last valid row.  K % 64 == 0.
 // ------------------------------------------------------------------------------------
-__device__ __forceinline__ void lds_dma16(const void* g, unsigned lds_byte_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte_addr)
-                 : "memory", "m0");
-}
-template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 template <typename T, int BN, class Epi>
 __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
@@ -265,7 +260,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
 #pragma unroll
         for (int d = 0; d < ND; ++d) dma(st, d);
     wait_vm<2 * ND>();  // stage 0 has landed
-    asm volatile("s_barrier" ::: "memory");
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < TI; ++i) rd_a(0, 0, i);
 #pragma unroll
@@ -285,7 +280,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
         }
         // stage kt+1 complete: only stage kt+2 and the first loads of kd may fly
         wait_vm<ND + H0>();
-        asm volatile("s_barrier" ::: "memory");
+        lds_barrier();
 #pragma unroll
         for (int i = TI / 2; i < TI; ++i) {
             const int g = i - TI / 2;

@@ -9,6 +9,8 @@
 // log2(e)/sqrt(d_head) and exponentiated with exp2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "lb_device.h"
 
@@ -222,6 +224,205 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
                     // slot e <-> key 32kb + 16cc + 8*(lane/32) + e, column 32dt + lane%32
                     const V8 vf = vt_fragment<T, DH>(vs, 32 * kb + 16 * cc + 8 * (lane >> 5),
                                                      32 * dt + 16 * ((lane >> 4) & 1), lane);
+                    oacc[dt] = mfma32(vf, pf[kb][cc], oacc[dt]);
+                }
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l_tot;
+    if (head_ok && qi < S) {
+        T* op = o + (size_t)(b * S + qi) * qd + h * DH;
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                float vv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vv[e] = oacc[dt][4 * a + e] * inv;
+                store4(op + dt * 32 + 8 * a + 4 * (lane >> 5), vv);
+            }
+    }
+}
+
+// ------------------------------------------------------------------------------------
+// Prefill, d_head 128, q and K/V in the same 16-bit type (a prefill from
+// position 0 reads the workspace copies of k and v).  Same block shape and
+// products as attn_prefill_kernel, reorganised for the chip:
+//  * the K and V tiles of 64 keys go from global memory straight into a
+//    two-stage LDS ring (direct-to-LDS loads issued from inline assembly,
+//    one barrier per tile); the next tile loads under the current one;
+//  * LDS swizzles for 64 four-byte banks: key rows XOR their chunk index by
+//    row % 16 (16 rows per ds_read_b128 phase), value rows by
+//    4*(row % 4) ^ 2*(row / 8 % 2) (the 32 lanes of a transpose read cover
+//    4 keys x 4 chunks or 8 keys x 2 chunks);
+//  * the mask is applied only on tiles that reach past the block's first
+//    query; the softmax scale is folded into exp2(s*c - m);
+//  * the running maximum used for the exponentials is raised only when a
+//    tile's maximum exceeds it by more than 8 (factor 256), so the output
+//    rescale is skipped on most tiles (probabilities stay below 256, far
+//    inside fp16 range);
+//  * at most ~128 VGPRs + 64 AGPRs, so two blocks share a CU.
+// Keys past kv_len load the last valid row (finite) and are masked.
+// ------------------------------------------------------------------------------------
+__device__ __forceinline__ int kswz128(int row) { return row & 15; }
+__device__ __forceinline__ int vswz128(int row) { return ((row & 3) << 2) ^ ((row & 8) >> 2); }
+
+template <typename T, int NW>
+__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
+    const T* __restrict__ q, const T* __restrict__ kbase, const T* __restrict__ vbase,
+    T* __restrict__ o, long kv_bg, int S, int start_pos, int H, int nkv, int n_rep, int n_hb,
+    float c) {
+    typedef typename vec8<T>::type V8;
+    constexpr int DH = 128, KT = 64, NT = NW * 64;
+    constexpr int TILE = KT * DH;                 // elements of one K or V tile
+    constexpr int ND = 2 * TILE / 8 / NT;          // 16-byte loads per thread per stage
+    static_assert(ND * NT * 8 == 2 * TILE, "whole load instructions");
+    __shared__ __attribute__((aligned(16))) T lds[2 * 2 * TILE];  // stage s: K at 2sTILE, V after
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qb = gridDim.x - 1 - blockIdx.x;
+    const int hb = blockIdx.y % n_hb;
+    const int bg = blockIdx.y / n_hb;
+    const int g = bg % nkv, b = bg / nkv;
+    const int hl = hb * NW + wave;
+    const bool head_ok = hl < n_rep;
+    const int h = g * n_rep + (head_ok ? hl : n_rep - 1);
+    const int q0 = qb * 32;
+    const int qi = q0 + (lane & 31);
+    const int qrow = min(qi, S - 1);
+    const int qpos = start_pos + qrow;
+    const int qd = H * DH;
+
+    V8 qf[DH / 16];
+    {
+        const T* qp = q + (size_t)(b * S + qrow) * qd + h * DH + 8 * (lane >> 5);
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qp + 16 * kk);
+    }
+    const int kv_len = start_pos + min(q0 + 32, S);
+    const int ntiles = (kv_len + KT - 1) / KT;
+    const int first_masked = start_pos + q0;     // keys above this need the mask
+    const T* kp = kbase + (size_t)bg * kv_bg;
+    const T* vp = vbase + (size_t)bg * kv_bg;
+
+    // load d: 64 consecutive 16-byte slots (d*NW + wave)*64 ..; slots 0..1023
+    // are the K tile (row = slot/16), 1024..2047 the V tile
+    int src_off[ND];
+    unsigned dst_off[ND];
+    const unsigned lds0 = (unsigned)(size_t)(lds_void_ptr)lds;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+        const int slot = (d * NW + wave) * 64 + lane;
+        const bool isk = slot < TILE / 8;
+        const int sl = isk ? slot : slot - TILE / 8;
+        const int row = sl >> 4, pc = sl & 15;
+        const int ch = pc ^ (isk ? kswz128(row) : vswz128(row));
+        src_off[d] = (isk ? 0 : (1 << 30)) | (row * DH + ch * 8);   // bit 30 tags V
+        dst_off[d] = lds0 + (unsigned)(((d * NW + wave) * 64 * 8) * (int)sizeof(T));
+    }
+    auto issue = [&](int tile) {
+        const int t0 = tile * KT;
+        const unsigned stage = (unsigned)((tile & 1) * 2 * TILE * (int)sizeof(T));
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+            const bool isv = src_off[d] >> 30;
+            const int off = src_off[d] & ((1 << 30) - 1);
+            const int row = off / DH;
+            const int key = min(t0 + row, kv_len - 1);
+            const T* src = (isv ? vp : kp) + (size_t)key * DH + (off - row * DH);
+            lds_dma16(src, dst_off[d] + stage);
+        }
+    };
+
+    f32x16 oacc[DH / 32];
+#pragma unroll
+    for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    float m_used = -INFINITY, l_run = 0.0f;
+    const int prow = key_perm(lane & 31);
+
+    issue(0);
+    for (int tile = 0; tile < ntiles; ++tile) {
+        wait_vm<0>();
+        lds_barrier();  // tile landed everywhere; every wave is done with the other stage
+        if (tile + 1 < ntiles) issue(tile + 1);
+        const T* ks = lds + (tile & 1) * 2 * TILE;
+        const T* vs = ks + TILE;
+
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
+            const int row = kb * 32 + prow;
+#pragma unroll
+            for (int kk = 0; kk < DH / 16; ++kk) {
+                const int ch = 2 * kk + (lane >> 5);
+                const V8 kf = *reinterpret_cast<const V8*>(ks + row * DH + ((ch ^ kswz128(row)) << 3));
+                sacc[kb] = mfma32(kf, qf[kk], sacc[kb]);
+            }
+        }
+        const int t0 = tile * KT;
+        float mx = -INFINITY;
+        if (t0 + KT - 1 > first_masked) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t0 + kb * 32 + 16 * (r >> 3) + 8 * (lane >> 5) + (r & 7);
+                    if (key > qpos) sacc[kb][r] = -INFINITY;
+                    mx = fmaxf(mx, sacc[kb][r]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+        const bool raise = mx > m_used + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            const float m_new = raise ? mx : m_used;
+            const float alpha = exp2f(m_used - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DH / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+            m_used = m_new;
+        }
+        V8 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float p = exp2f(fmaf(sacc[kb][8 * cc + e], c, -m_used));
+                    l_run += p;
+                    pf[kb][cc][e] = from_f32<T>(p);
+                }
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    // slot e <-> key 32kb + 16cc + 8*(lane/32) + e, column 32dt + lane%32
+                    const int k0 = 32 * kb + 16 * cc + 8 * (lane >> 5);
+                    const int sg = lane & 15;
+                    const int dcol = 32 * dt + 16 * ((lane >> 4) & 1) + 4 * (sg & 3);
+                    const int ka = k0 + (sg >> 2), kb2 = ka + 4;
+                    const T* pa = vs + ka * DH + ((((dcol >> 3) ^ vswz128(ka)) << 3) | (dcol & 7));
+                    const T* pb = vs + kb2 * DH + ((((dcol >> 3) ^ vswz128(kb2)) << 3) | (dcol & 7));
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)pa);
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)pb);
+                    V8 vf;
+                    __builtin_memcpy(&vf, &lo, 8);
+                    __builtin_memcpy(reinterpret_cast<char*>(&vf) + 8, &hi, 8);
                     oacc[dt] = mfma32(vf, pf[kb][cc], oacc[dt]);
                 }
         }
@@ -568,9 +769,26 @@ static hipError_t prefill_t(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <typename T, int NW>
+static hipError_t prefill_fa_t(const AttnArgs& a, hipStream_t s) {
+    const int n_rep = a.H / a.nkv;
+    const int n_hb = n_rep / NW;
+    const dim3 grid((a.S + 31) / 32, a.B * a.nkv * n_hb);
+    const float c = kLog2e / sqrtf(128.0f);
+    attn_prefill_fa_kernel<T, NW><<<grid, NW * 64, 0, s>>>(
+        (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.kv_bg, a.S, a.start_pos, a.H,
+        a.nkv, n_rep, n_hb, c);
+    return hipGetLastError();
+}
+
 template <typename T, typename KVT, int DH>
 static hipError_t prefill_nw(const AttnArgs& a, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
+    if constexpr (DH == 128 && std::is_same<T, KVT>::value) {
+        if (n_rep % 8 == 0) return prefill_fa_t<T, 8>(a, s);
+        if (n_rep % 4 == 0) return prefill_fa_t<T, 4>(a, s);
+        if (n_rep % 2 == 0) return prefill_fa_t<T, 2>(a, s);
+    }
     if (n_rep % 8 == 0) return prefill_t<T, KVT, DH, 8>(a, s);
     if (n_rep % 4 == 0) return prefill_t<T, KVT, DH, 4>(a, s);
     if (n_rep % 3 == 0) return prefill_t<T, KVT, DH, 3>(a, s);

@@ -89,16 +89,9 @@ static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Ep
     if (M <= 16) return run_skinny<T, 1>(A, W, M, N, K, epi, ws.part, ws.cap, s);
     if (M <= 32) return run_skinny<T, 2>(A, W, M, N, K, epi, ws.part, ws.cap, s);
     if (M <= 64) return run_skinny<T, 4>(A, W, M, N, K, epi, ws.part, ws.cap, s);
-    // 256 x 256 or 256 x 192 tiles, whichever fills its last round of 256
-    // CUs better (a 1.5-round grid leaves half the chip idle in its tail)
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
-    const long t192 = (long)((M + 255) / 256) * ((N + 191) / 192);
-    auto fill = [](long t) { return (double)t / (double)(((t + 255) / 256) * 256); };
     if (K % 64 == 0 && t256 >= 192) {
-        if (fill(t192) > fill(t256) + 0.05)
-            gemm_big_kernel<T, 192, Epi><<<(unsigned)t192, 256, 0, s>>>(A, W, M, N, K, epi);
-        else
-            gemm_big_kernel<T, 256, Epi><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
+        gemm_big_kernel<T, 256, Epi><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
     } else {
         const long t = (long)((M + 127) / 128) * ((N + 127) / 128);
         gemm_mfma_kernel<T, 128, 128, 64, 64, 4, Epi><<<(unsigned)t, 256, 0, s>>>(A, W, M, N, K, epi);

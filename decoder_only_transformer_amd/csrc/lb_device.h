@@ -123,6 +123,20 @@ __host__ __device__ __forceinline__ size_t ktile_w_off(int n, int k, int K) {
     return ((size_t)(n >> 4) * (K >> 5) + (k >> 5)) * 512 + ktile_in_piece(n, k);
 }
 
+// ---- direct-to-LDS loads issued from inline assembly -------------------------------
+// One global_load_lds_dwordx4: lane l copies 16 bytes from g (its own
+// address) to LDS byte address lds_byte_addr + 16 * l (M0 holds the
+// wave-uniform base).  The compiler does not see these loads, so its waits
+// for ordinary LDS reads stay exact; the caller waits for them with wait_vm
+// (they are the only vector-memory loads in flight where it does) before a
+// barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* g, unsigned lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_byte_addr)
+                 : "memory", "m0");
+}
+template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 // 8-element operand vector of a 16-bit type.
 template <typename T> struct vec8;
 template <> struct vec8<f16> { typedef f16x8 type; };
