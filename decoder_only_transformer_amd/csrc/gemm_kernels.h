@@ -172,9 +172,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
 }
 
 // ------------------------------------------------------------------------------------
-// Large prefill GEMM.  Block tile 256 x BN (BN = 256), BK = 32, four
-// wavefronts in a 2 x 2 grid, each 128 x BN/2 with 16x16x32 MFMAs (8 x BN/32
-// accumulator tiles, all in AGPRs; one wavefront per SIMD).  A four-stage
+// Large prefill GEMM.  Block tile BM x BN (256 x 256 in use; 128-row tiles
+// measured slower), BK = 32, four wavefronts in a 2 x 2 grid, each
+// BM/2 x BN/2 with 16x16x32 MFMAs (accumulators in AGPRs; one wavefront per
+// SIMD).  A four-stage
 // LDS ring is filled by direct-to-LDS loads issued from inline assembly (so
 // the compiler's counters for LDS reads stay exact; the kernel waits for
 // the loads itself).  Each k-step runs its MFMAs in two halves with the one
@@ -186,12 +187,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
 // Rows beyond M / N are clamped to the last valid row.  K % 64 == 0.
 // ------------------------------------------------------------------------------------
 
-template <typename T, int BN, class Epi>
+template <typename T, int BM, int BN, class Epi>
 __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
                                                       const T* __restrict__ W, int M, int N,
                                                       int K, Epi epi) {
     typedef typename vec8<T>::type V8;
-    constexpr int STAGES = 4, BM = 256, BK = 32, NW = 4, NT = 256, WM = 128, WN = BN / 2;
+    constexpr int STAGES = 4, BK = 32, NW = 4, NT = 256, WM = BM / 2, WN = BN / 2;
     constexpr int TI = WM / 16, TJ = WN / 16;
     constexpr int SA = BM * BK, SB = BN * BK, STG = SA + SB;  // elements per stage
     constexpr int NA = BM * BK / 8 / NT, NB = BN * BK / 8 / NT; // loads per thread per stage
@@ -281,6 +282,11 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
         // stage kt+1 complete: only stage kt+2 and the first loads of kd may fly
         wait_vm<ND + H0>();
         lds_barrier();
+        // the next step's operands in the order its first half uses them:
+        // every B fragment and the first A rows early, the last A rows late
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) rd_b(kt + 1, fb ^ 1, j);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = TI / 2; i < TI; ++i) {
             const int g = i - TI / 2;
@@ -289,10 +295,10 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int d = H0 + g; d < ND; d += TI / 2) dma(kd, d);
-            rd_a(kt + 1, fb ^ 1, 2 * g);
-            rd_a(kt + 1, fb ^ 1, 2 * g + 1);
+            if (g < 2) {
 #pragma unroll
-            for (int j = g; j < TJ; j += TI / 2) rd_b(kt + 1, fb ^ 1, j);
+                for (int q = 0; q < TI / 2; ++q) rd_a(kt + 1, fb ^ 1, g * (TI / 2) + q);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };

@@ -91,7 +91,7 @@ static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Ep
     if (M <= 64) return run_skinny<T, 4>(A, W, M, N, K, epi, ws.part, ws.cap, s);
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     if (K % 64 == 0 && t256 >= 192) {
-        gemm_big_kernel<T, 256, Epi><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
+        gemm_big_kernel<T, 256, 256, Epi><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
     } else {
         const long t = (long)((M + 127) / 128) * ((N + 127) / 128);
         gemm_mfma_kernel<T, 128, 128, 64, 64, 4, Epi><<<(unsigned)t, 256, 0, s>>>(A, W, M, N, K, epi);
