@@ -464,12 +464,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
 // ------------------------------------------------------------------------------------
 template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-template <typename T, int DH>
-__global__ void __launch_bounds__(256) attn_decode_kernel(
+template <typename T, int DH, int NW, bool DIRECT>
+__global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
     const T* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-    float* __restrict__ part, long kv_bg, int H, int nkv, int n_rep, int kv_len, int CH,
-    int nsplit, float c) {
-    constexpr int NW = 4;
+    float* __restrict__ part, T* __restrict__ o, int o_mt, long kv_bg, int H, int nkv, int n_rep,
+    int kv_len, int CH, int nsplit, float c) {
     constexpr int KCH = DH / 8;              // 16-byte chunks per row
     constexpr int VLOADS = 32 * KCH / 64;    // direct-to-LDS instructions per step
     constexpr int KLOADS = 2 * (DH / 32);    // K operand loads per step
@@ -641,11 +640,17 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
                 O += so[w][hh][d] * f;
             }
         }
-        float* pp = part + (((size_t)b * H + g * n_rep + hh) * nsplit + split) * (DH + 2);
-        pp[d] = O;
-        if (d == 0) {
-            pp[DH] = M;
-            pp[DH + 1] = L;
+        if (DIRECT) {
+            // one block covers every key of the group: the normalised output
+            const int col = (g * n_rep + hh) * DH + d;
+            o[o_mt > 0 ? ktile_act_off(b, col, o_mt) : (size_t)b * H * DH + col] = from_f32<T>(O / L);
+        } else {
+            float* pp = part + (((size_t)b * H + g * n_rep + hh) * nsplit + split) * (DH + 2);
+            pp[d] = O;
+            if (d == 0) {
+                pp[DH] = M;
+                pp[DH + 1] = L;
+            }
         }
     }
 }
@@ -811,35 +816,54 @@ hipError_t attn_prefill(Elem op, Elem kv_t, const AttnArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-// Keys per wavefront: 128, or more (a multiple of 32) when that would need
-// more than kDecodeMaxSplit blocks per (sequence, KV group).
-static int decode_keys_per_wave(int kv_len) {
-    int ch = 128;
-    while ((kv_len + 4 * ch - 1) / (4 * ch) > kDecodeMaxSplit) ch += 128;
-    return ch;
+// Launch shape of the split-KV decode: 8 wavefronts per block and about one
+// block per CU.  With at least 256 (sequence, KV group) pairs every block
+// takes all keys of one pair and writes the output itself; otherwise the keys
+// of a pair are split so that about 256 blocks run, and a merge kernel
+// combines the splits.  Keys per wavefront are a multiple of 32.
+constexpr int kDecodeWaves = 8;
+struct DecodeShape {
+    int nsplit, ch;
+};
+static DecodeShape decode_shape(int bgs, int kv_len) {
+    int nsplit = (256 + bgs - 1) / bgs;
+    const int max_split = (kv_len + kDecodeWaves * 32 - 1) / (kDecodeWaves * 32);  // >= 32 keys per wave
+    if (nsplit > max_split) nsplit = max_split;
+    if (nsplit > kDecodeMaxSplit) nsplit = kDecodeMaxSplit;
+    if (nsplit < 1) nsplit = 1;
+    int ch = (kv_len + nsplit * kDecodeWaves - 1) / (nsplit * kDecodeWaves);
+    ch = (ch + 31) / 32 * 32;
+    nsplit = (kv_len + kDecodeWaves * ch - 1) / (kDecodeWaves * ch);
+    return {nsplit, ch};
 }
 
-// Any kv_len <= max_kv uses at most min(kDecodeMaxSplit, ceil(max_kv / 512))
-// splits (keys per wavefront never drop below 128).
+// Partials for any batch <= max_batch: B * nsplit <= B + 256 / n_kv blocks'
+// worth of (sequence, head) rows.
 size_t decode_partials_floats(int max_batch, int H, int dh, int max_kv) {
-    size_t nsplit = (size_t)(max_kv + 511) / 512;
-    if (nsplit > (size_t)kDecodeMaxSplit) nsplit = kDecodeMaxSplit;
-    return (size_t)max_batch * H * nsplit * (dh + 2);
+    (void)max_kv;
+    return (size_t)(max_batch + 256) * H * (dh + 2);
 }
 
 template <typename T, int DH>
 static hipError_t decode_t(const AttnArgs& a, float* part, int o_mt, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
     const int kv_len = a.start_pos + 1;
-    const int ch = decode_keys_per_wave(kv_len);
-    const int nsplit = (kv_len + 4 * ch - 1) / (4 * ch);
+    const DecodeShape sh = decode_shape(a.B * a.nkv, kv_len);
     const float c = kLog2e / sqrtf((float)DH);
-    attn_decode_kernel<T, DH><<<dim3(nsplit, a.B * a.nkv), 256, 0, s>>>(
-        (const T*)a.q, (const bf16*)a.k, (const bf16*)a.v, part, a.kv_bg, a.H, a.nkv, n_rep, kv_len,
-        ch, nsplit, c);
+    const dim3 grid(sh.nsplit, a.B * a.nkv);
+    constexpr int NW = kDecodeWaves;
+    if (sh.nsplit == 1) {
+        attn_decode_kernel<T, DH, NW, true><<<grid, NW * 64, 0, s>>>(
+            (const T*)a.q, (const bf16*)a.k, (const bf16*)a.v, part, (T*)a.o, o_mt, a.kv_bg, a.H,
+            a.nkv, n_rep, kv_len, sh.ch, 1, c);
+        return hipGetLastError();
+    }
+    attn_decode_kernel<T, DH, NW, false><<<grid, NW * 64, 0, s>>>(
+        (const T*)a.q, (const bf16*)a.k, (const bf16*)a.v, part, (T*)a.o, o_mt, a.kv_bg, a.H,
+        a.nkv, n_rep, kv_len, sh.ch, sh.nsplit, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    attn_combine_kernel<T, DH><<<a.B * a.nkv, 256, 0, s>>>(part, (T*)a.o, a.H, a.nkv, n_rep, nsplit, o_mt);
+    attn_combine_kernel<T, DH><<<a.B * a.nkv, 256, 0, s>>>(part, (T*)a.o, a.H, a.nkv, n_rep, sh.nsplit, o_mt);
     return hipGetLastError();
 }
 
