@@ -549,6 +549,94 @@ __global__ void __launch_bounds__(NW * 64) gemm_decode_kernel(const T* __restric
     }
 }
 
+// ------------------------------------------------------------------------------------
+// Decode GEMM for wide outputs: the NW wavefronts of a block own NW different
+// 16-column weight tiles and all of K, and share the activations: chunks of AC
+// k-steps of the (k-step tiled) activation rows go from global memory into
+// LDS once per block (direct-to-LDS loads issued from inline assembly, two
+// buffers) and every wavefront reads its MFMA operands from there, so the
+// activation traffic per weight byte drops by NW.  Each wavefront streams its
+// weight tile with U k-steps in flight in registers.  The output tile of a
+// wavefront goes through LDS to form the 8-column chunks of the epilogue.
+// Grid N / (16*NW).  N % (16*NW) == 0, K % 32 == 0.
+// ------------------------------------------------------------------------------------
+template <typename T, int MT, int U, int NW, int AC, class Epi>
+__global__ void __launch_bounds__(NW * 64) gemm_decode_wide_kernel(const T* __restrict__ At,
+                                                                   const T* __restrict__ Wt, int M,
+                                                                   int N, int K, Epi epi) {
+    typedef typename vec8<T>::type V8;
+    constexpr int APC = AC * MT;  // 1 KB activation pieces per chunk
+    static_assert(APC % NW == 0 && AC % U == 0, "chunk shape");
+    __shared__ __attribute__((aligned(16))) T abuf[2 * APC * 512];
+    __shared__ float ost[NW][MT * 16][17];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nks = K / 32;
+    const int nchunk = (nks + AC - 1) / AC;
+    const int nt = blockIdx.x * NW + wave;
+    const T* wp = Wt + (size_t)nt * nks * 512 + lane * 8;
+    const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)abuf;
+    // pieces past the last k-step reload the last one (never used)
+    auto dma_chunk = [&](int chunk) {
+#pragma unroll
+        for (int i = 0; i < APC / NW; ++i) {
+            const int pc = i * NW + wave;
+            const int ks = min(chunk * AC + pc / MT, nks - 1);
+            lds_dma16(At + ((size_t)ks * MT + pc % MT) * 512 + lane * 8,
+                      lds0 + (unsigned)((((chunk & 1) * APC + pc) * 512) * (int)sizeof(T)));
+        }
+    };
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    V8 bw[U];
+    auto wload = [&](int step, int slot) { bw[slot] = *reinterpret_cast<const V8*>(wp + (size_t)min(step, nks - 1) * 512); };
+#pragma unroll
+    for (int u = 0; u < U; ++u) wload(u, u);
+    dma_chunk(0);
+    wait_vm<0>();
+    __syncthreads();
+    for (int ch = 0; ch < nchunk; ++ch) {
+        dma_chunk(ch + 1);
+        const T* ab = abuf + (ch & 1) * APC * 512;
+        for (int s0 = 0; s0 < AC; s0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int step = ch * AC + s0 + u;
+                V8 a[MT];
+#pragma unroll
+                for (int t = 0; t < MT; ++t) a[t] = *reinterpret_cast<const V8*>(ab + ((s0 + u) * MT + t) * 512 + lane * 8);
+                if (step >= nks) {
+#pragma unroll
+                    for (int t = 0; t < MT; ++t) a[t] = V8{};
+                }
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] = mfma16(a[t], bw[u], acc[t]);
+                wload(step + U, u);
+            }
+        }
+        // chunk ch+1 has landed: only this chunk's AC weight loads may still fly
+        wait_vm<AC>();
+        __syncthreads();
+    }
+    wait_vm<0>();
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ost[wave][t * 16 + 4 * (lane >> 4) + r][lane & 15] = acc[t][r];
+    __syncthreads();
+    // lane -> (row, 8-column half) of this wavefront's tile
+    for (int q = lane; q < MT * 16 * 2; q += 64) {
+        const int row = q >> 1, h = q & 1;
+        if (row < M) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = ost[wave][row][8 * h + e];
+            epi.row8(row, nt * 16 + 8 * h, v);
+        }
+    }
+}
+
 // Sum the KS fp32 partials of a split-K decode GEMM (in split order) and run
 // the epilogue: one thread per 8-column chunk.
 template <class Epi>

@@ -37,8 +37,9 @@ static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const 
     return hipGetLastError();
 }
 
-// Decode GEMM over k-step-tiled operands.  Wide outputs (>= 384 16-column
-// tiles) take two column tiles per wavefront, so a wavefront's activation
+// Decode GEMM over k-step-tiled operands.  Very wide outputs (>= 1536
+// 16-column tiles) share the activations of a block through LDS; wide ones
+// (>= 384 tiles) take two column tiles per wavefront, so a wavefront's activation
 // loads feed twice the weight bytes; narrower ones take one and split K
 // across blocks when there are fewer than 192 column tiles.
 int decode_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
@@ -47,6 +48,13 @@ template <typename T, int MT, class Epi>
 static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, const Epi& epi,
                                 const SplitWs& ws, hipStream_t s) {
     const int tiles = N / 16, nks = K / 32;
+    // very wide outputs (gate/up): blocks of 8 column tiles sharing the
+    // activations through LDS
+    if (tiles >= 8 * 192 && tiles % 8 == 0) {
+        constexpr int AC = MT == 4 ? 8 : 16;
+        gemm_decode_wide_kernel<T, MT, 8, 8, AC, Epi><<<tiles / 8, 512, 0, s>>>(At, Wt, M, N, K, epi);
+        return hipGetLastError();
+    }
     if (tiles >= 384 && tiles % 2 == 0) {
         gemm_decode_kernel<T, MT, 2, 2, 4, false, Epi><<<dim3(tiles / 2, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
         return hipGetLastError();
