@@ -182,8 +182,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
 // barrier of the step between them: after it, stage k+1 is complete for
 // every wavefront and the second half reads the next step's operands under
 // its MFMAs; the loads of stage k+3 are spread over both halves.  LDS rows
-// are 64 bytes (4 chunks) with chunk index XORed by (row / 4) & 3: a
-// 16-lane phase reads 16 rows at one logical chunk without bank conflicts.
+// are 64 bytes (4 chunks) with chunk index XORed by (row / 2) & 3, the
+// pattern measured free of bank conflicts for this operand read (16 rows at
+// each of the 4 chunks of a 64-byte row per instruction).
 // Rows beyond M / N are clamped to the last valid row.  K % 64 == 0.
 // ------------------------------------------------------------------------------------
 
@@ -197,7 +198,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
     constexpr int SA = BM * BK, SB = BN * BK, STG = SA + SB;  // elements per stage
     constexpr int NA = BM * BK / 8 / NT, NB = BN * BK / 8 / NT; // loads per thread per stage
     constexpr int ND = NA + NB, H0 = (ND + 1) / 2;
-    constexpr int EPR = 64, CPAD = BN + 8;
+    constexpr int EPR = 64, CPAD = BN + 4;  // rows r, r+4, r+8, r+12 of a store on distinct banks
     static_assert(NA * NT * 8 == SA && NB * NT * 8 == SB, "whole load instructions");
     static_assert(EPR * CPAD * 4 <= STAGES * STG * (int)sizeof(T), "epilogue stage fits");
     __shared__ __attribute__((aligned(16))) T lds[STAGES * STG];
@@ -227,7 +228,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
     for (int d = 0; d < ND; ++d) {
         const bool isa = d < NA;
         const int slot0 = ((isa ? d : d - NA) * NW + wave) * 64;
-        const int p = slot0 + lane, row = p >> 2, c = (p & 3) ^ ((row >> 2) & 3);
+        const int p = slot0 + lane, row = p >> 2, c = (p & 3) ^ ((row >> 1) & 3);
         gsrc[d] = isa ? A + (size_t)min(m0 + row, M - 1) * K + c * 8
                       : W + (size_t)min(n0 + row, N - 1) * K + c * 8;
         ldst[d] = lds0 + (unsigned)(((isa ? 0 : SA) + slot0 * 8) * (int)sizeof(T));
@@ -248,12 +249,12 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
     auto rd_a = [&](int kstep, int fb, int i) {
         const T* la = lds + (kstep % STAGES) * STG;
         const int row = wm * WM + i * 16 + (lane & 15), kc = lane >> 4;
-        af[fb][i] = *reinterpret_cast<const V8*>(la + row * BK + ((kc ^ ((row >> 2) & 3)) << 3));
+        af[fb][i] = *reinterpret_cast<const V8*>(la + row * BK + ((kc ^ ((row >> 1) & 3)) << 3));
     };
     auto rd_b = [&](int kstep, int fb, int j) {
         const T* lb = lds + (kstep % STAGES) * STG + SA;
         const int row = wn * WN + j * 16 + (lane & 15), kc = lane >> 4;
-        bf[fb][j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ ((row >> 2) & 3)) << 3));
+        bf[fb][j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ ((row >> 1) & 3)) << 3));
     };
 
 #pragma unroll
