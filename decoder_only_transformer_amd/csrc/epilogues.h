@@ -89,7 +89,8 @@ struct EpiSwiGLU {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float a = v[e];
-            r[e] = a / (1.0f + expf(-a)) * v[4 + e];
+            // e^-a as 2^(-a log2 e); 1 / (1 + e^-a) by the hardware reciprocal
+            r[e] = a * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-a * 1.4426950408889634f)) * v[4 + e];
         }
         const int j = n >> 1;
         store4(z + (mt > 0 ? ktile_act_off(m, j, mt) : (size_t)m * dff + j), r);

@@ -192,13 +192,13 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
             }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = exp2_hw(m_run - m_new);
         float ls = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(sacc[kb][r] - m_new);
+                const float p = exp2_hw(sacc[kb][r] - m_new);
                 sacc[kb][r] = p;
                 ls += p;
             }
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
         const bool raise = mx > m_used + 8.0f;
         if (__builtin_amdgcn_ballot_w64(raise)) {
             const float m_new = raise ? mx : m_used;
-            const float alpha = exp2f(m_used - m_new);
+            const float alpha = exp2_hw(m_used - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < DH / 32; ++dt)
@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float p = exp2f(fmaf(sacc[kb][8 * cc + e], c, -m_used));
+                    const float p = exp2_hw(fmaf(sacc[kb][8 * cc + e], c, -m_used));
                     l_run += p;
                     pf[kb][cc][e] = from_f32<T>(p);
                 }
@@ -573,13 +573,13 @@ __global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = exp2_hw(m_run - m_new);
         float pv[8], ls = 0.0f;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = exp2f(sc[t][r] - m_new);
+                const float p = exp2_hw(sc[t][r] - m_new);
                 pv[4 * t + r] = p;
                 ls += p;
             }
@@ -635,7 +635,7 @@ __global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             if (sm[w][hh] != -INFINITY) {
-                const float f = exp2f(sm[w][hh] - M);
+                const float f = exp2_hw(sm[w][hh] - M);
                 L += sl[w][hh] * f;
                 O += so[w][hh][d] * f;
             }
@@ -675,7 +675,7 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(const float* __restri
         const float M = wave_max(m);
         float l = 0.0f;
         for (int s = lane; s < nsplit; s += 64) {
-            const float f = exp2f(pp[(size_t)s * (DH + 2) + DH] - M);
+            const float f = exp2_hw(pp[(size_t)s * (DH + 2) + DH] - M);
             wt[hh][s] = f;
             l += pp[(size_t)s * (DH + 2) + DH + 1] * f;
         }

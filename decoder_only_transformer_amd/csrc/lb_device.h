@@ -73,6 +73,11 @@ template <typename T> __device__ __forceinline__ void store4(T* p, const float* 
     for (int i = 0; i < 4; ++i) p[i] = from_f32<T>(v[i]);
 }
 
+// 2^x from the hardware base-2 exponential (about 1 ulp; -inf gives 0 and
+// results below the smallest normal flush toward zero).  Used where the result
+// only ever meets a sum that is at least one: softmax weights and SiLU.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---- wavefront reductions (64 lanes, fixed butterfly order) ----------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
