@@ -59,6 +59,17 @@ static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, c
         gemm_decode_kernel<T, MT, 2, 2, 4, false, Epi><<<dim3(tiles / 2, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
         return hipGetLastError();
     }
+    // long K at mid widths (the down projection): two column tiles per
+    // wavefront halve the activation loads per weight byte; a two-way K
+    // split keeps one block per CU (measured faster than one split, despite
+    // the extra reduction launch, from K = 8192 up)
+    if (tiles >= 192 && tiles % 2 == 0 && nks >= 256 && (size_t)2 * M * N <= ws.cap) {
+        gemm_decode_kernel<T, MT, 2, 2, 4, true, Epi><<<dim3(tiles / 2, 2), 256, 0, s>>>(At, Wt, M, N, K, 2, ws.part, epi);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        reduce_epilogue_kernel<Epi><<<(M * (N / 8) + 255) / 256, 256, 0, s>>>(ws.part, M, N, 2, epi);
+        return hipGetLastError();
+    }
     int ks = 1;
     if (tiles < 192) {
         ks = (256 + tiles - 1) / tiles;

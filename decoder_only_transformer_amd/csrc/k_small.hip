@@ -22,13 +22,22 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const TI* __restrict__ x,
     const int row = blockIdx.x;
     const TI* xr = x + (size_t)row * d;
     TO* orow = out + (size_t)row * d;
-    float v[8][8];
+    float v[8][8], gg[8][8];
     float ss = 0.0f;
+    // the gains are loaded with the row so that one memory round trip
+    // precedes the reduction
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int c = (threadIdx.x + 256 * i) * 8;
         if (c < d) {
             load8(xr + c, v[i]);
+            load8(g + c, gg[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = (threadIdx.x + 256 * i) * 8;
+        if (c < d) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
         }
@@ -42,10 +51,8 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const TI* __restrict__ x,
     for (int i = 0; i < 8; ++i) {
         const int c = (threadIdx.x + 256 * i) * 8;
         if (c < d) {
-            float gg[8];
-            load8(g + c, gg);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[i][e] = v[i][e] * r * gg[e];
+            for (int e = 0; e < 8; ++e) v[i][e] = v[i][e] * r * gg[i][e];
             store8(out_mt > 0 ? out + ktile_act_off(row, c, out_mt) : orow + c, v[i]);
         }
     }
