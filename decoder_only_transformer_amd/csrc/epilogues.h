@@ -112,4 +112,13 @@ struct EpiOut {
     }
 };
 
+// Any epilogue applied to a launch that covers the output columns from
+// n_off on (the launch sees column n, the output column is n + n_off).
+template <class Epi>
+struct EpiShift {
+    Epi e;
+    int n_off;
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const { e.row8(m, n + n_off, v); }
+};
+
 }  // namespace lb

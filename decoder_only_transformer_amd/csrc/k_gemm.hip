@@ -101,6 +101,19 @@ static hipError_t run_decode(const T* At, const T* Wt, int M, int N, int K, cons
     }
 }
 
+// compute units of the current device, cached per device
+static int device_cus() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 template <typename T, class Epi>
 static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Epi& epi,
                            const SplitWs& ws, hipStream_t s) {
@@ -108,9 +121,24 @@ static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Ep
     if (M <= 16) return run_skinny<T, 1>(A, W, M, N, K, epi, ws.part, ws.cap, s);
     if (M <= 32) return run_skinny<T, 2>(A, W, M, N, K, epi, ws.part, ws.cap, s);
     if (M <= 64) return run_skinny<T, 4>(A, W, M, N, K, epi, ws.part, ws.cap, s);
-    const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+    const long tm = (M + 255) / 256, tn = (N + 255) / 256, t256 = tm * tn;
     if (K % 64 == 0 && t256 >= 192) {
-        gemm_big_kernel<T, 256, 256, Epi><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
+        // A CU runs one 256 x 256 tile at a time, so a launch takes
+        // ceil(tiles / CUs) rounds.  When the last round would be at most
+        // half full and made of whole tile columns (the 8B q/k/v product:
+        // 384 tiles), those columns go to the 128 x 128 kernel instead, two
+        // blocks per CU: measured 82 us for them there against a 113 us round.
+        const long cus = device_cus();
+        const long rem = t256 % cus;
+        if (rem > 0 && 2 * rem <= cus && rem % tm == 0 && rem / tm < tn) {
+            const int n1 = (int)(tn - rem / tm) * 256, nt = N - n1;
+            gemm_big_kernel<T, 256, 256, Epi><<<(unsigned)(tm * (tn - rem / tm)), 256, 0, s>>>(A, W, M, n1, K, epi);
+            const long t = (long)((M + 127) / 128) * ((nt + 127) / 128);
+            gemm_mfma_kernel<T, 128, 128, 64, 64, 4, EpiShift<Epi>><<<(unsigned)t, 256, 0, s>>>(
+                A, W + (size_t)n1 * K, M, nt, K, EpiShift<Epi>{epi, n1});
+        } else {
+            gemm_big_kernel<T, 256, 256, Epi><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
+        }
     } else {
         const long t = (long)((M + 127) / 128) * ((N + 127) / 128);
         gemm_mfma_kernel<T, 128, 128, 64, 64, 4, Epi><<<(unsigned)t, 256, 0, s>>>(A, W, M, N, K, epi);
