@@ -69,7 +69,7 @@ __device__ __forceinline__ typename vec8<T>::type vt_fragment(const T* tile, int
 }
 
 // ------------------------------------------------------------------------------------
-// Prefill.  Grid (ceil(S/32), B*n_kv*n_hb), NW wavefronts per block: the
+// Prefill.  Grid (B*n_kv*n_hb, ceil(S/32)), NW wavefronts per block: the
 // block owns 32 consecutive queries of one sequence and NW query heads of one
 // KV group; every wavefront is one head and all of them share each K / V
 // tile staged in LDS.  Per 64-key tile a wavefront computes S^T (64 keys x
@@ -77,7 +77,7 @@ __device__ __forceinline__ typename vec8<T>::type vt_fragment(const T* tile, int
 // lane's query (lane = query, so rescaling is lane-local) and accumulates
 // O^T += V^T P^T, the V^T operands read from the [key][d] tile with transpose
 // reads.  Tiles are prefetched into registers during the MFMAs.  Heavier
-// (later) query blocks are launched first.
+// (later) query blocks of every head group are launched first.
 // ------------------------------------------------------------------------------------
 template <typename T, typename KVT, int DH, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
@@ -94,9 +94,9 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
     __shared__ __attribute__((aligned(16))) T vs[KT * DH];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int qb = gridDim.x - 1 - blockIdx.x;
-    const int hb = blockIdx.y % n_hb;
-    const int bg = blockIdx.y / n_hb;
+    const int qb = gridDim.y - 1 - blockIdx.y;
+    const int hb = blockIdx.x % n_hb;
+    const int bg = blockIdx.x / n_hb;
     const int g = bg % nkv, b = bg / nkv;
     const int hl = hb * NW + wave;
     const bool head_ok = hl < n_rep;
@@ -282,9 +282,9 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qb = gridDim.x - 1 - blockIdx.x;
-    const int hb = blockIdx.y % n_hb;
-    const int bg = blockIdx.y / n_hb;
+    const int qb = gridDim.y - 1 - blockIdx.y;
+    const int hb = blockIdx.x % n_hb;
+    const int bg = blockIdx.x / n_hb;
     const int g = bg % nkv, b = bg / nkv;
     const int hl = hb * NW + wave;
     const bool head_ok = hl < n_rep;
@@ -766,7 +766,10 @@ template <typename T, typename KVT, int DH, int NW>
 static hipError_t prefill_t(const AttnArgs& a, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
     const int n_hb = n_rep / NW;
-    const dim3 grid((a.S + 31) / 32, a.B * a.nkv * n_hb);
+    // blocks are dispatched x-fastest: every (sequence, head group) of the
+    // last query block first, so the longest blocks (causal: the most key
+    // tiles) start first and the short ones fill the tail
+    const dim3 grid(a.B * a.nkv * n_hb, (a.S + 31) / 32);
     const float c = kLog2e / sqrtf((float)DH);
     attn_prefill_kernel<T, KVT, DH, NW><<<grid, NW * 64, 0, s>>>(
         (const T*)a.q, (const KVT*)a.k, (const KVT*)a.v, (T*)a.o, a.kv_bg, a.S, a.start_pos, a.H,
@@ -778,7 +781,10 @@ template <typename T, int NW>
 static hipError_t prefill_fa_t(const AttnArgs& a, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
     const int n_hb = n_rep / NW;
-    const dim3 grid((a.S + 31) / 32, a.B * a.nkv * n_hb);
+    // blocks are dispatched x-fastest: every (sequence, head group) of the
+    // last query block first, so the longest blocks (causal: the most key
+    // tiles) start first and the short ones fill the tail
+    const dim3 grid(a.B * a.nkv * n_hb, (a.S + 31) / 32);
     const float c = kLog2e / sqrtf(128.0f);
     attn_prefill_fa_kernel<T, NW><<<grid, NW * 64, 0, s>>>(
         (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.kv_bg, a.S, a.start_pos, a.H,

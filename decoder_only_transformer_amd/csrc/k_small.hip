@@ -58,6 +58,50 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const TI* __restrict__ x,
     }
 }
 
+// Same RMSNorm for many rows (prefill): one wavefront per row, four rows per
+// block, the row in registers (CPL 8-element chunks per lane, d <= 512*CPL),
+// the sum of squares reduced by a butterfly inside the wavefront, no LDS and
+// no block barrier.  Deterministic (fixed order).
+template <typename TI, typename TO, int CPL>
+__global__ void __launch_bounds__(256) rmsnorm_rows_kernel(const TI* __restrict__ x,
+                                                           const float* __restrict__ g,
+                                                           TO* __restrict__ out, int M, int d,
+                                                           float eps) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;  // whole wavefronts leave together
+    const TI* xr = x + (size_t)row * d;
+    TO* orow = out + (size_t)row * d;
+    float v[CPL][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = (lane + 64 * i) * 8;
+        if (c < d) load8(xr + c, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = (lane + 64 * i) * 8;
+        if (c < d) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
+        }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = (lane + 64 * i) * 8;
+        if (c < d) {
+            float gg[8];
+            load8(g + c, gg);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] = v[i][e] * r * gg[e];
+            store8(orow + c, v[i]);
+        }
+    }
+}
+
 // One 16-byte chunk per thread: chunk q of the tiled layout comes from row
 // 16 * (piece / (K/32)) + q % 16, columns 32 * (piece % (K/32)) + 8 * (q % 64 / 16).
 template <typename T>
@@ -108,6 +152,14 @@ static hipError_t rmsnorm_t(const void* x, const float* g, void* out, int M, int
     if (M <= 0) return hipSuccess;
     if (d > 16384) return hipErrorInvalidValue;
     if (out_mt > 0 && (d % 32 != 0 || M > 16 * out_mt)) return hipErrorInvalidValue;
+    if (out_mt == 0 && M >= 256 && d <= 512 * 16) {
+        const unsigned blocks = (unsigned)((M + 3) / 4);
+        if (d <= 512 * 8)
+            rmsnorm_rows_kernel<TI, TO, 8><<<blocks, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps);
+        else
+            rmsnorm_rows_kernel<TI, TO, 16><<<blocks, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps);
+        return hipGetLastError();
+    }
     rmsnorm_kernel<TI, TO><<<M, 256, 0, s>>>((const TI*)x, g, (TO*)out, M, d, eps, out_mt);
     return hipGetLastError();
 }
