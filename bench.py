@@ -65,6 +65,9 @@ def stage_work(w):
     }
 
 
+PER_CALL = 50  # forwards timed one by one for the median / p10 / p90
+
+
 def run_gpu(w, steps, warmup):
     import torch
 
@@ -112,10 +115,33 @@ def run_gpu(w, steps, warmup):
     ms, avg_dom = timed([dom])
     # 3) the same forwards without any event, for comparison
     ms_plain, _ = timed([])
+    # 4) per-call spread: each forward between its own pair of events, as is
+    #    and after a 512 MB read that evicts the 256 MB MALL and the L2s (a
+    #    read, so that no dirty lines are left to be written back during the
+    #    timed call)
+    per_call = {"calls": PER_CALL}
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    for tag, flush in (("", False), ("flushed_", True)):
+        ev = []
+        for _ in range(PER_CALL):
+            if flush:
+                scratch.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            blk.forward(x, w.start_pos, (k, v), out)
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        d = sorted(a.elapsed_time(b) for a, b in ev)
+        q = lambda f: d[min(len(d) - 1, int(round(f * (len(d) - 1))))]
+        per_call.update({tag + "median_ms": round(q(0.5), 4), tag + "p10_ms": round(q(0.1), 4),
+                         tag + "p90_ms": round(q(0.9), 4)})
+    del scratch
     blk.close()
     del k, v, x, out
     torch.cuda.empty_cache()
-    return ms, avg_all, dom, avg_dom[dom], ms_plain, ms_all
+    return ms, avg_all, dom, avg_dom[dom], ms_plain, ms_all, per_call
 
 
 def roofline(w, avg_ms, dom, dom_ms, bound):
@@ -244,7 +270,7 @@ def main():
 
     w = workloads.get(args.workload)
     log(f"[bench] prefill {w.name}: warmup {args.warmup}, steps {args.steps}")
-    ms, avg, dom, dom_ms, ms_plain, ms_all = run_gpu(w, args.steps, args.warmup)
+    ms, avg, dom, dom_ms, ms_plain, ms_all, per_call = run_gpu(w, args.steps, args.warmup)
     roof, stages = roofline(w, avg, dom, dom_ms, "mfma")
     roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     total_flops = sum(v["flops"] for v in stage_work(w).values())
@@ -272,6 +298,7 @@ def main():
         "block_mfma_frac": round(total_flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
         "roofline": roof,
         "stages": stages,
+        "per_call": per_call,
     }
     log(f"[bench] prefill {ms:.3f} ms/step, {result['value']:.0f} tokens/s")
 
@@ -279,7 +306,7 @@ def main():
         wd = workloads.get(args.decode_workload)
         dsteps = args.decode_steps or 5 * args.steps
         log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {dsteps}")
-        dms, davg, ddom, ddom_ms, dms_plain, dms_all = run_gpu(wd, dsteps, args.warmup)
+        dms, davg, ddom, ddom_ms, dms_plain, dms_all, dper_call = run_gpu(wd, dsteps, args.warmup)
         droof, dstages = roofline(wd, davg, ddom, ddom_ms, "hbm")
         droof["traffic"] = measured_traffic(wd.name, droof["kernel"])
         total_bytes = sum(v["bytes"] for v in stage_work(wd).values())
@@ -291,7 +318,7 @@ def main():
             "tokens_per_s": round(wd.M / (dms * 1e-3), 1),
             "block_gbs": round(total_bytes / (dms * 1e-3) / 1e9, 1),
             "block_hbm_frac": round(total_bytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "roofline": droof, "stages": dstages,
+            "roofline": droof, "stages": dstages, "per_call": dper_call,
         }
         log(f"[bench] decode {dms * 1e3:.1f} us/step")
 
