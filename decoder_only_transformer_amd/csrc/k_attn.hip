@@ -262,18 +262,22 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
 //    tile's maximum exceeds it by more than 8 (factor 256), so the output
 //    rescale is skipped on most tiles (probabilities stay below 256, far
 //    inside fp16 range);
-//  * at most ~128 VGPRs + 64 AGPRs, so two blocks share a CU.
+//  * a block is NWH heads of one KV group x QB consecutive query blocks of
+//    32 (eight wavefronts in use), all sharing each staged tile; a
+//    wavefront whose queries end before the block's last tile skips the
+//    products of that tile but keeps loading and syncing.
 // Keys past kv_len load the last valid row (finite) and are masked.
 // ------------------------------------------------------------------------------------
 __device__ __forceinline__ int kswz128(int row) { return row & 15; }
 __device__ __forceinline__ int vswz128(int row) { return ((row & 3) << 2) ^ ((row & 8) >> 2); }
 
-template <typename T, int NW>
-__global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
+template <typename T, int NWH, int QB>
+__global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa_kernel(
     const T* __restrict__ q, const T* __restrict__ kbase, const T* __restrict__ vbase,
     T* __restrict__ o, long kv_bg, int S, int start_pos, int H, int nkv, int n_rep, int n_hb,
     float c) {
     typedef typename vec8<T>::type V8;
+    constexpr int NW = NWH * QB;
     constexpr int DH = 128, KT = 64, NT = NW * 64;
     constexpr int TILE = KT * DH;                 // elements of one K or V tile
     constexpr int ND = 2 * TILE / 8 / NT;          // 16-byte loads per thread per stage
@@ -282,14 +286,15 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qb = gridDim.y - 1 - blockIdx.y;
+    const int hw = wave % NWH, qs = wave / NWH;   // head and query block of this wavefront
+    const int qblk = gridDim.y - 1 - blockIdx.y;
     const int hb = blockIdx.x % n_hb;
     const int bg = blockIdx.x / n_hb;
     const int g = bg % nkv, b = bg / nkv;
-    const int hl = hb * NW + wave;
+    const int hl = hb * NWH + hw;
     const bool head_ok = hl < n_rep;
     const int h = g * n_rep + (head_ok ? hl : n_rep - 1);
-    const int q0 = qb * 32;
+    const int q0 = (qblk * QB + qs) * 32;
     const int qi = q0 + (lane & 31);
     const int qrow = min(qi, S - 1);
     const int qpos = start_pos + qrow;
@@ -301,8 +306,11 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
 #pragma unroll
         for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qp + 16 * kk);
     }
-    const int kv_len = start_pos + min(q0 + 32, S);
+    // keys the block loads: up to its last query; keys this wavefront uses:
+    // up to its own last query (none past S)
+    const int kv_len = start_pos + min((qblk + 1) * QB * 32, S);
     const int ntiles = (kv_len + KT - 1) / KT;
+    const int my_tiles = q0 < S ? (start_pos + min(q0 + 32, S) + KT - 1) / KT : 0;
     const int first_masked = start_pos + q0;     // keys above this need the mask
     const T* kp = kbase + (size_t)bg * kv_bg;
     const T* vp = vbase + (size_t)bg * kv_bg;
@@ -349,6 +357,7 @@ __global__ void __launch_bounds__(NW * 64, 8 / NW) attn_prefill_fa_kernel(
         wait_vm<0>();
         lds_barrier();  // tile landed everywhere; every wave is done with the other stage
         if (tile + 1 < ntiles) issue(tile + 1);
+        if (tile >= my_tiles) continue;  // past this wavefront's queries (it keeps loading and syncing)
         const T* ks = lds + (tile & 1) * 2 * TILE;
         const T* vs = ks + TILE;
 
@@ -777,16 +786,16 @@ static hipError_t prefill_t(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int NW>
+template <typename T, int NWH, int QB>
 static hipError_t prefill_fa_t(const AttnArgs& a, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
-    const int n_hb = n_rep / NW;
+    const int n_hb = n_rep / NWH;
     // blocks are dispatched x-fastest: every (sequence, head group) of the
     // last query block first, so the longest blocks (causal: the most key
     // tiles) start first and the short ones fill the tail
-    const dim3 grid(a.B * a.nkv * n_hb, (a.S + 31) / 32);
+    const dim3 grid(a.B * a.nkv * n_hb, (a.S + 32 * QB - 1) / (32 * QB));
     const float c = kLog2e / sqrtf(128.0f);
-    attn_prefill_fa_kernel<T, NW><<<grid, NW * 64, 0, s>>>(
+    attn_prefill_fa_kernel<T, NWH, QB><<<grid, NWH * QB * 64, 0, s>>>(
         (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.kv_bg, a.S, a.start_pos, a.H,
         a.nkv, n_rep, n_hb, c);
     return hipGetLastError();
@@ -796,9 +805,11 @@ template <typename T, typename KVT, int DH>
 static hipError_t prefill_nw(const AttnArgs& a, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
     if constexpr (DH == 128 && std::is_same<T, KVT>::value) {
-        if (n_rep % 8 == 0) return prefill_fa_t<T, 8>(a, s);
-        if (n_rep % 4 == 0) return prefill_fa_t<T, 4>(a, s);
-        if (n_rep % 2 == 0) return prefill_fa_t<T, 2>(a, s);
+        // eight wavefronts per block: n_rep heads x the query blocks that fill
+        // the rest share every staged K / V tile
+        if (n_rep % 8 == 0) return prefill_fa_t<T, 8, 1>(a, s);
+        if (n_rep % 4 == 0) return prefill_fa_t<T, 4, 2>(a, s);
+        if (n_rep % 2 == 0) return prefill_fa_t<T, 2, 4>(a, s);
     }
     if (n_rep % 8 == 0) return prefill_t<T, KVT, DH, 8>(a, s);
     if (n_rep % 4 == 0) return prefill_t<T, KVT, DH, 4>(a, s);
