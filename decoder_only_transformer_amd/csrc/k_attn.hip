@@ -361,6 +361,10 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
         const T* ks = lds + (tile & 1) * 2 * TILE;
         const T* vs = ks + TILE;
 
+        // the matrix-core sections run at raised wavefront priority, so the
+        // SIMD prefers the wavefront that feeds the MFMA unit while the other
+        // one runs its softmax
+        __builtin_amdgcn_s_setprio(1);
         f32x16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -374,6 +378,7 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
                 sacc[kb] = mfma32(kf, qf[kk], sacc[kb]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         const int t0 = tile * KT;
         float mx = -INFINITY;
         if (t0 + KT - 1 > first_masked) {
@@ -414,6 +419,7 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
                     l_run += p;
                     pf[kb][cc][e] = from_f32<T>(p);
                 }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < DH / 32; ++dt) {
 #pragma unroll
@@ -435,6 +441,7 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
                     oacc[dt] = mfma32(vf, pf[kb][cc], oacc[dt]);
                 }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
