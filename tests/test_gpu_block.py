@@ -235,6 +235,29 @@ def test_bf16_operand_mode_smollm2():
     run.close()
 
 
+def test_bf16_operands_at_8b_width_lose_to_fp16():
+    """The literal bf16-MFMA reading at the 8B-width prefill: the same block
+    with every operand in bf16 lands well above the fp16-operand default on the
+    same 130 sampled rows (every 32nd row of each sequence: the FFN amplifies
+    the rounding of its operands); the fp16 default meets the 2e-2 bar.  Both
+    errors are logged."""
+    w = workloads.get("llama3_8b_prefill")
+    rows = sample_rows(w, list(range(0, w.S, 32)) + [w.S - 1])
+    t = workloads.generate(w)
+    y_orc, *_ = oracle_rows(w, t, rows=rows)
+    y_orc = y_orc.reshape(w.M, w.d)[rows]
+    errs = {}
+    for operands in ("auto", "bf16"):
+        run = GpuRun(w, t, operands=operands)
+        y = run.forward().double().cpu().numpy().reshape(w.M, w.d)[rows]
+        errs[operands] = rel_err(y, y_orc)
+        log(f"    8B prefill operands={operands}: max|err|/rms = {errs[operands]:.3e}")
+        run.close()
+        del run
+    assert errs["auto"] <= 2e-2, errs
+    assert errs["bf16"] > 1.3 * errs["auto"], errs
+
+
 def test_forward_rejects_bad_arguments_without_writing():
     import decoder_only_transformer_amd as lbmod
     w = workloads.with_overrides(workloads.get("tiny_f32"), B=1, S=8)
