@@ -40,15 +40,17 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_work(w):
+def stage_work(w, positions=None):
     """Algorithmic work per forward, per profiled stage: flops (matrix products,
     causal attention over visible (query, key) pairs only) and HBM bytes (each
-    operand read once, each result written once)."""
+    operand read once, each result written once).  positions: the start
+    position of each sequence (default: w.start_pos for all)."""
     M, d, dh, H, G, dff = w.M, w.d, w.d_head, w.H, w.n_kv, w.d_ff
     qd, kvd = H * dh, G * dh
     e = 2  # bytes per bf16/fp16 element
-    vis = sum(w.start_pos + s + 1 for s in range(w.S)) * w.B       # visible pairs per head
-    kv_read = w.B * G * (w.start_pos + w.S) * dh * 2 * e            # K and V, every visible row
+    starts = list(positions) if positions is not None else [w.start_pos] * w.B
+    vis = sum(p + s + 1 for p in starts for s in range(w.S))       # visible pairs per head
+    kv_read = sum(G * (p + w.S) * dh * 2 * e for p in starts)       # K and V, every visible row
     return {
         "rmsnorm_1": {"flops": 0, "bytes": M * d * (e + e)},
         "qkv_rope_append": {"flops": 2 * M * (qd + 2 * kvd) * d,
@@ -68,7 +70,7 @@ def stage_work(w):
 PER_CALL = 50  # forwards timed one by one for the median / p10 / p90
 
 
-def run_gpu(w, steps, warmup):
+def run_gpu(w, steps, warmup, positions=None):
     import torch
 
     import decoder_only_transformer_amd as lbmod
@@ -85,8 +87,9 @@ def run_gpu(w, steps, warmup):
     x = t["x"].to("cuda")
     out = torch.empty_like(x)
     del t
+    sp = list(positions) if positions is not None else w.start_pos
     for _ in range(warmup):
-        blk.forward(x, w.start_pos, (k, v), out)
+        blk.forward(x, sp, (k, v), out)
 
     def timed(stages):
         """`steps` back-to-back forwards with the library's timing-only HIP
@@ -97,7 +100,7 @@ def run_gpu(w, steps, warmup):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
-            blk.forward(x, w.start_pos, (k, v), out)
+            blk.forward(x, sp, (k, v), out)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         avg = {}
@@ -129,7 +132,7 @@ def run_gpu(w, steps, warmup):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            blk.forward(x, w.start_pos, (k, v), out)
+            blk.forward(x, sp, (k, v), out)
             e1.record()
             ev.append((e0, e1))
         torch.cuda.synchronize()
@@ -144,10 +147,10 @@ def run_gpu(w, steps, warmup):
     return ms, avg_all, dom, avg_dom[dom], ms_plain, ms_all, per_call
 
 
-def roofline(w, avg_ms, dom, dom_ms, bound):
+def roofline(w, avg_ms, dom, dom_ms, bound, positions=None):
     """Per-stage figures from the all-stage pass; the roofline entry from the
     dominant stage's own timed region."""
-    work = stage_work(w)
+    work = stage_work(w, positions)
     stages = {}
     for n, ms in avg_ms.items():
         s = ms * 1e-3
@@ -321,6 +324,25 @@ def main():
             "roofline": droof, "stages": dstages, "per_call": dper_call,
         }
         log(f"[bench] decode {dms * 1e3:.1f} us/step")
+
+        # the same decode with every sequence at its own position (ragged
+        # batch): positions spread evenly from 1024 to the workload's last one
+        pos = [1024 + (wd.start_pos - 1024) * b // max(wd.B - 1, 1) for b in range(wd.B)]
+        log(f"[bench] ragged decode: positions {pos[0]}..{pos[-1]}")
+        rms, ravg, rdom, rdom_ms, rms_plain, rms_all, _ = run_gpu(wd, dsteps, args.warmup, pos)
+        rroof, rstages = roofline(wd, ravg, rdom, rdom_ms, "hbm", pos)
+        rroof["traffic"] = None  # counters are taken for the uniform decode only
+        rbytes = sum(v["bytes"] for v in stage_work(wd, pos).values())
+        result["decode_ragged"] = {
+            "workload": wd.name, "B": wd.B, "positions": f"{pos[0]}..{pos[-1]} evenly spread",
+            "steps": dsteps, "us_per_step": round(rms * 1e3, 2),
+            "us_per_step_without_events": round(rms_plain * 1e3, 2),
+            "tokens_per_s": round(wd.M / (rms * 1e-3), 1),
+            "block_gbs": round(rbytes / (rms * 1e-3) / 1e9, 1),
+            "block_hbm_frac": round(rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline": rroof, "stages": rstages,
+        }
+        log(f"[bench] ragged decode {rms * 1e3:.1f} us/step")
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")

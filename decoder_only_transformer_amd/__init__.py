@@ -21,7 +21,8 @@ LB_OK, LB_ERR_INVALID_ARG, LB_ERR_UNSUPPORTED, LB_ERR_OOM, LB_ERR_HIP = 0, 1, 2,
 STAGES = {"n1": 0, "q": 1, "o": 2, "h": 3, "n2": 4, "z": 5}
 ELEM_NAMES = {0: "f32", 1: "bf16", 2: "f16"}
 
-EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_destroy",
+MAX_RAGGED_BATCH = 64
+EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_forward_ragged", "llama_block_destroy",
            "llama_block_status_string", "llama_block_last_error", "llama_block_stage_info",
            "llama_block_copy_stage", "llama_block_profile", "llama_block_profile_read")
 STAGE_NAMES = ("rmsnorm_1", "qkv_rope_append", "attention", "o_proj_residual", "rmsnorm_2",
@@ -73,6 +74,9 @@ def lib() -> ctypes.CDLL:
         L.llama_block_init.restype = ctypes.c_int
         L.llama_block_forward.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(LbKVCache), vp, vp]
         L.llama_block_forward.restype = ctypes.c_int
+        L.llama_block_forward_ragged.argtypes = [vp, vp, i32, i32, ctypes.POINTER(ctypes.c_int32),
+                                                 ctypes.POINTER(LbKVCache), vp, vp]
+        L.llama_block_forward_ragged.restype = ctypes.c_int
         L.llama_block_destroy.argtypes = [vp]
         L.llama_block_destroy.restype = None
         L.llama_block_status_string.argtypes = [ctypes.c_int]
@@ -140,6 +144,21 @@ def llama_block_forward(handle: int, x, start_pos: int, kv: Tuple, out, stream=N
     st = lib().llama_block_forward(handle, _ptr(x), B, S, int(start_pos), ctypes.byref(c),
                                    _ptr(out), _stream(stream))
     _check(handle, st, "llama_block_forward")
+
+
+def llama_block_forward_ragged(handle: int, x, start_pos, kv: Tuple, out, stream=None) -> None:
+    """As llama_block_forward with one start position per sequence
+    (start_pos: a sequence of len(x) ints, at most MAX_RAGGED_BATCH)."""
+    k, v = kv
+    B, S = int(x.shape[0]), int(x.shape[1])
+    pos = [int(p) for p in start_pos]
+    if len(pos) != B:
+        raise ValueError(f"need one start position per sequence ({B}), got {len(pos)}")
+    arr = (ctypes.c_int32 * B)(*pos)
+    c = LbKVCache(_ptr(k), _ptr(v), int(k.shape[0]), int(k.shape[2]))
+    st = lib().llama_block_forward_ragged(handle, _ptr(x), B, S, arr, ctypes.byref(c), _ptr(out),
+                                          _stream(stream))
+    _check(handle, st, "llama_block_forward_ragged")
 
 
 def llama_block_destroy(handle: int) -> None:
@@ -212,8 +231,12 @@ class LlamaBlock:
         self.cfg = cfg
         self.handle = llama_block_init(cfg, weights)
 
-    def forward(self, x, start_pos: int, kv, out, stream=None):
-        llama_block_forward(self.handle, x, start_pos, kv, out, stream)
+    def forward(self, x, start_pos, kv, out, stream=None):
+        """start_pos: one int for every sequence, or one per sequence (ragged)."""
+        if not hasattr(start_pos, "__len__"):
+            llama_block_forward(self.handle, x, int(start_pos), kv, out, stream)
+        else:
+            llama_block_forward_ragged(self.handle, x, start_pos, kv, out, stream)
         return out
 
     def stage(self, name: str, rows: int):

@@ -14,7 +14,7 @@ namespace lb {
 // RoPE ("The Evolving Transformer 04 LLaMA", 02 RoPE; "Mini Llama 2
 // Implementation", Rotary positional embeddings): the pair (2i, 2i+1) of a
 // head is turned by the angle pos * theta^(-2i/d_head) with
-// pos = start_pos + s ("Full Llama 3 transformer block", How it works).  The
+// pos = start_pos(b) + s ("Full Llama 3 transformer block", How it works).  The
 // (cos, sin) table is built in fp64 on the host and stored as fp32 pairs.
 //
 // Column ranges of the packed projection: [0, qd) q heads, [qd, qd+kvd) k
@@ -27,10 +27,11 @@ struct EpiQKV {
     TC* kc;             // [B][nkv][cap][dh]
     TC* vc;             // [B][nkv][cap][dh]
     const float2* rope; // [max_seq][dh/2] (cos, sin)
-    int S, start_pos, cap, s_stride, nkv, dh, qd;
+    SeqPos sp;
+    int S, cap, s_stride, nkv, dh, qd;
 
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
-        const int b = m / S, s = m - b * S, pos = start_pos + s;
+        const int b = m / S, s = m - b * S, pos = (sp.ragged ? sp.pos[b] : sp.base) + s;
         const int kvd = nkv * dh;
         if (n < qd + kvd) {
             const int j = (n < qd ? n : n - qd) % dh;

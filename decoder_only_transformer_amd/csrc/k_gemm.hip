@@ -165,7 +165,7 @@ static EpiQKV<TO, TC> make_qkv(const QkvEpi& e) {
     r.vc = (TC*)e.vc;
     r.rope = e.rope;
     r.S = e.S;
-    r.start_pos = e.start_pos;
+    r.sp = e.sp;
     r.cap = e.cap;
     r.s_stride = e.s_stride;
     r.nkv = e.nkv;

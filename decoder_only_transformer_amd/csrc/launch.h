@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lb_device.h"
+
 namespace lb {
 
 enum class Elem : int { F32 = 0, BF16 = 1, F16 = 2 };
@@ -36,7 +38,8 @@ struct QkvEpi {
     void* kc;         // [Bc][nkv][cap][dh] cache type
     void* vc;         // [Bc][nkv][cap][dh] cache type
     const float2* rope;
-    int S, start_pos, cap, s_stride, nkv, dh, qd;
+    SeqPos sp;        // start position of each sequence
+    int S, cap, s_stride, nkv, dh, qd;
 };
 // op: operand type of A and W (F32 selects the plain fp32 kernels); cache: cache type.
 // part: fp32 workspace for the split-K decode GEMMs (M <= 64), cap floats;
@@ -80,7 +83,8 @@ struct AttnArgs {
     const void* v;   // element (bg, t, d) at v[bg*kv_bg + t*dh + d]
     void* o;         // [B*S][H*dh] operand type
     long kv_bg;      // elements per (sequence, KV head): positions * dh
-    int B, S, start_pos, H, nkv, dh;
+    SeqPos sp;       // start position of each sequence
+    int B, S, max_start, H, nkv, dh;  // max_start: the largest start position
 };
 // Causal prefill attention (seq_len > 1).  op: q/o type; kv_t: K/V storage type.
 hipError_t attn_prefill(Elem op, Elem kv_t, const AttnArgs& a, hipStream_t s);

@@ -17,6 +17,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Start position of every sequence of one forward: all at `base`, or (ragged)
+// sequence b at pos[b], b < kMaxRagged.  Passed by value in kernel arguments;
+// device code reads `ragged ? pos[b] : base` from the argument itself (a
+// member function taking `this` would copy the argument to scratch memory).
+constexpr int kMaxRagged = 64;
+struct SeqPos {
+    int base;
+    int ragged;
+    int pos[kMaxRagged];
+};
+
 // ---- scalar conversions (fp32 <-> storage types, round to nearest even) ----
 __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(f16 v) { return (float)v; }

@@ -324,7 +324,8 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
-static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int start_pos,
+// sp: start position of every sequence (validated by the caller)
+static lb_status run_forward(lb_block* blk, const void* x, int B, int S, const lb::SeqPos& sp,
                              const lb_kv_cache* kv, void* out, hipStream_t s) {
     const lb_config& c = blk->cfg;
     const int M = B * S, d = c.d_model, dh = c.d_head, nkv = c.n_kv_heads, dff = c.d_ff;
@@ -365,7 +366,16 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     e = lb::launch_rmsnorm(dt, op, x, blk->g1, n1, M, d, (float)c.norm_eps, mt, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_1: %s", hipGetErrorString(e));
 
-    const bool ws_kv = (dt == Elem::BF16) && S > 1 && start_pos == 0;
+    int max_start = sp.base, all_zero = sp.base == 0;
+    if (sp.ragged) {
+        max_start = 0;
+        all_zero = 1;
+        for (int b = 0; b < B; ++b) {
+            max_start = std::max(max_start, sp.pos[b]);
+            all_zero &= sp.pos[b] == 0;
+        }
+    }
+    const bool ws_kv = (dt == Elem::BF16) && S > 1 && all_zero;
     const int s_stride = (S + 7) & ~7;
     lb::QkvEpi qe;
     qe.q = blk->q;
@@ -375,7 +385,7 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     qe.vc = kv->v;
     qe.rope = blk->rope;
     qe.S = S;
-    qe.start_pos = start_pos;
+    qe.sp = sp;
     qe.cap = cap;
     qe.s_stride = s_stride;
     qe.nkv = nkv;
@@ -391,7 +401,8 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     a.o = o;
     a.B = B;
     a.S = S;
-    a.start_pos = start_pos;
+    a.sp = sp;
+    a.max_start = max_start;
     a.H = c.n_heads;
     a.nkv = nkv;
     a.dh = dh;
@@ -431,9 +442,11 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, int sta
     return LB_OK;
 }
 
-extern "C" lb_status llama_block_forward(lb_block* blk, const void* x, int32_t batch, int32_t seq_len,
-                                         int32_t start_pos, const lb_kv_cache* kv, void* out,
-                                         void* stream) {
+// Validation and launch shared by the uniform and the ragged entry points;
+// starts == nullptr: every sequence at start_pos.
+static lb_status forward_checked(lb_block* blk, const void* x, int32_t batch, int32_t seq_len,
+                                 int32_t start_pos, const int32_t* starts, const lb_kv_cache* kv,
+                                 void* out, void* stream) {
     if (!blk) return LB_ERR_INVALID_ARG;
     blk->err.clear();
     const lb_config& c = blk->cfg;
@@ -444,11 +457,22 @@ extern "C" lb_status llama_block_forward(lb_block* blk, const void* x, int32_t b
     if ((long)batch * seq_len > c.max_tokens)
         return fail(blk, LB_ERR_INVALID_ARG, "batch*seq_len (%ld) exceeds max_tokens (%d)",
                     (long)batch * seq_len, c.max_tokens);
-    if (start_pos < 0) return fail(blk, LB_ERR_INVALID_ARG, "start_pos (%d) < 0", start_pos);
-    if ((long)start_pos + seq_len > c.max_seq_len || (long)start_pos + seq_len > kv->max_seq_len)
-        return fail(blk, LB_ERR_INVALID_ARG,
-                    "start_pos+seq_len (%ld) exceeds max_seq_len (config %d, cache %d)",
-                    (long)start_pos + seq_len, c.max_seq_len, kv->max_seq_len);
+    lb::SeqPos sp;
+    sp.base = start_pos;
+    sp.ragged = starts != nullptr;
+    for (int b = 0; b < lb::kMaxRagged; ++b) sp.pos[b] = 0;
+    if (starts && batch > lb::kMaxRagged)
+        return fail(blk, LB_ERR_INVALID_ARG, "a ragged forward takes at most %d sequences (got %d)",
+                    lb::kMaxRagged, batch);
+    for (int b = 0; b < (starts ? batch : 1); ++b) {
+        const int32_t p = starts ? starts[b] : start_pos;
+        if (p < 0) return fail(blk, LB_ERR_INVALID_ARG, "start_pos of sequence %d (%d) < 0", b, p);
+        if ((long)p + seq_len > c.max_seq_len || (long)p + seq_len > kv->max_seq_len)
+            return fail(blk, LB_ERR_INVALID_ARG,
+                        "start_pos+seq_len of sequence %d (%ld) exceeds max_seq_len (config %d, cache %d)",
+                        b, (long)p + seq_len, c.max_seq_len, kv->max_seq_len);
+        if (starts) sp.pos[b] = p;
+    }
     if (batch > kv->batch)
         return fail(blk, LB_ERR_INVALID_ARG, "batch (%d) exceeds the cache's batch (%d)", batch, kv->batch);
     if (blk->dt == Elem::BF16 && kv->max_seq_len % 8 != 0)
@@ -459,9 +483,25 @@ extern "C" lb_status llama_block_forward(lb_block* blk, const void* x, int32_t b
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) return fail(blk, LB_ERR_HIP, "hipGetDevice failed");
     if (cur != blk->dev) hipSetDevice(blk->dev);
-    lb_status st = run_forward(blk, x, batch, seq_len, start_pos, kv, out, (hipStream_t)stream);
+    lb_status st = run_forward(blk, x, batch, seq_len, sp, kv, out, (hipStream_t)stream);
     if (cur != blk->dev) hipSetDevice(cur);
     return st;
+}
+
+extern "C" lb_status llama_block_forward(lb_block* blk, const void* x, int32_t batch, int32_t seq_len,
+                                         int32_t start_pos, const lb_kv_cache* kv, void* out,
+                                         void* stream) {
+    return forward_checked(blk, x, batch, seq_len, start_pos, nullptr, kv, out, stream);
+}
+
+extern "C" lb_status llama_block_forward_ragged(lb_block* blk, const void* x, int32_t batch,
+                                                int32_t seq_len, const int32_t* start_pos,
+                                                const lb_kv_cache* kv, void* out, void* stream) {
+    if (blk && !start_pos) {
+        blk->err.clear();
+        return fail(blk, LB_ERR_INVALID_ARG, "start_pos must be non-NULL");
+    }
+    return forward_checked(blk, x, batch, seq_len, 0, start_pos, kv, out, stream);
 }
 
 static bool stage_buffer(const lb_block* blk, lb_stage which, const void** ptr, Elem* elem, int64_t* cols) {

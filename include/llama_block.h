@@ -121,6 +121,24 @@ lb_status llama_block_forward(lb_block* blk, const void* x, int32_t batch, int32
                               int32_t start_pos, const lb_kv_cache* kv, void* out,
                               void* stream);
 
+/* llama_block_forward with a start position per sequence, for batches whose
+ * sequences have different lengths (decode of sequences at different
+ * positions, or prefill chunks at different offsets): sequence b has its
+ * queries at positions start_pos[b] + s, reads its cache positions
+ * [0, start_pos[b]) and writes [start_pos[b], start_pos[b] + seq_len); no
+ * other cache entry changes.  start_pos is a HOST array of `batch` values,
+ * read during the call (they travel in the kernel arguments), so the caller
+ * may reuse it as soon as the call returns.  batch <= LB_MAX_RAGGED_BATCH.
+ * Checks as llama_block_forward, per sequence; a NULL start_pos is
+ * LB_ERR_INVALID_ARG.  With every start_pos[b] equal it computes exactly what
+ * llama_block_forward computes for that start_pos.  ("Full Llama 3
+ * transformer block", How it works: the cache offset and the causal rule are
+ * per sequence.) */
+#define LB_MAX_RAGGED_BATCH 64
+lb_status llama_block_forward_ragged(lb_block* blk, const void* x, int32_t batch,
+                                     int32_t seq_len, const int32_t* start_pos,
+                                     const lb_kv_cache* kv, void* out, void* stream);
+
 /* Free the handle and everything it owns (synchronises the device first). */
 void llama_block_destroy(lb_block* blk);
 
