@@ -26,7 +26,19 @@ _dp = ctypes.POINTER(ctypes.c_double)
 class _Cfg(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int), ("n_heads", ctypes.c_int), ("n_kv_heads", ctypes.c_int),
                 ("d_head", ctypes.c_int), ("d_ff", ctypes.c_int),
-                ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_double)]
+                ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_double),
+                ("rope_half", ctypes.c_int), ("rope_scale", ctypes.c_double),
+                ("rope_low", ctypes.c_double), ("rope_high", ctypes.c_double),
+                ("rope_orig", ctypes.c_double)]
+
+
+def _cfg_struct(cfg: Dict) -> "_Cfg":
+    """cfg keys: d, H, n_kv, d_head, d_ff, theta, eps; optional rope_half (bool),
+    rope_scaling (None or (scale, low, high, orig))."""
+    sc = cfg.get("rope_scaling") or (0.0, 0.0, 0.0, 0.0)
+    return _Cfg(cfg["d"], cfg["H"], cfg["n_kv"], cfg["d_head"], cfg["d_ff"], float(cfg["theta"]),
+                float(cfg["eps"]), 1 if cfg.get("rope_half") else 0, float(sc[0]), float(sc[1]),
+                float(sc[2]), float(sc[3]))
 
 
 class _Weights(ctypes.Structure):
@@ -52,6 +64,9 @@ def lib():
         L.orc_rms_norm.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_double, _dp]
         L.orc_linear.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_int, _dp]
         L.orc_rope.argtypes = [_dp, ctypes.c_int, ctypes.c_long, ctypes.c_double]
+        L.orc_rope_freq.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int]
+        L.orc_rope_freq.restype = ctypes.c_double
+        L.orc_rope_cfg.argtypes = [_dp, ctypes.c_long, ctypes.POINTER(_Cfg)]
         L.orc_silu.argtypes = [ctypes.c_double]
         L.orc_silu.restype = ctypes.c_double
         L.orc_attend.argtypes = [_dp, _dp, _dp, ctypes.c_long, ctypes.c_int, _dp, _dp]
@@ -104,6 +119,20 @@ def rope(v, pos: int, theta: float) -> np.ndarray:
     return out
 
 
+def rope_freq(cfg: Dict, i: int) -> float:
+    """Rotation speed of pair i under cfg's RoPE settings (see _cfg_struct)."""
+    c = _cfg_struct(cfg)
+    return lib().orc_rope_freq(ctypes.byref(c), int(i))
+
+
+def rope_cfg(v, pos: int, cfg: Dict) -> np.ndarray:
+    """RoPE on one head vector with cfg's layout and frequency settings."""
+    out = _f64(v).copy()
+    c = _cfg_struct(cfg)
+    lib().orc_rope_cfg(_p(out), int(pos), ctypes.byref(c))
+    return out
+
+
 def silu(a: float) -> float:
     return lib().orc_silu(float(a))
 
@@ -135,8 +164,7 @@ def block_forward(cfg: Dict, x, weights: Dict, start_pos: int, k_cache: np.ndarr
     B, S, d = x.shape
     assert d == cfg["d"]
     cap = k_cache.shape[2]
-    c = _Cfg(cfg["d"], cfg["H"], cfg["n_kv"], cfg["d_head"], cfg["d_ff"],
-             float(cfg["theta"]), float(cfg["eps"]))
+    c = _cfg_struct(cfg)
     ws = {n: _f64(weights[n]) for n in WEIGHT_NAMES}
     wstruct = _Weights(*[_p(ws[n]) for n in WEIGHT_NAMES])
     y = np.zeros((B, S, d), dtype=np.float64)
@@ -165,7 +193,7 @@ def block_forward(cfg: Dict, x, weights: Dict, start_pos: int, k_cache: np.ndarr
 def cfg_of(w) -> Dict:
     """Oracle config dict from a workloads.BlockWorkload."""
     return {"d": w.d, "H": w.H, "n_kv": w.n_kv, "d_head": w.d_head, "d_ff": w.d_ff,
-            "theta": w.theta, "eps": w.eps}
+            "theta": w.theta, "eps": w.eps, "rope_half": w.rope_half, "rope_scaling": w.rope_scaling}
 
 
 def empty_cache(w, cap: Optional[int] = None):

@@ -81,6 +81,46 @@ void orc_rope(double* v, int d_head, long pos, double theta)
     }
 }
 
+/* Rotation speed of pair i under a block's RoPE settings [LL 02 RoPE: the
+ * base speed theta^(-2i/d_head); G2L Positions become a rotation: Llama 3.1
+ * keeps its original 8192-position context and stretches the slowest pairs by
+ * its scale factor, leaves the fastest alone and blends the ones between].
+ * Reading of the blend (the page names it only): with wavelength
+ * L = 2 pi / speed, pairs with L < orig / high keep their speed, pairs with
+ * L > orig / low are slowed by `scale`, and in between the speed is
+ * (1 - t) * speed / scale + t * speed with t = (orig / L - low) / (high - low),
+ * which meets both neighbours at the class boundaries.  With the page's
+ * 8B settings (theta 500 000, 64 pairs, scale 8, low 1, high 4, orig 8192)
+ * this makes 29 slow, 29 fast and 6 blended pairs, the page's counts. */
+double orc_rope_freq(const orc_cfg* c, int i)
+{
+    const double speed = pow(c->rope_theta, -2.0 * (double)i / (double)c->d_head);
+    if (!(c->rope_scale > 1.0)) return speed;
+    const double two_pi = 6.283185307179586476925286766559;
+    const double wavelen = two_pi / speed;
+    if (wavelen < c->rope_orig / c->rope_high) return speed;
+    if (wavelen > c->rope_orig / c->rope_low) return speed / c->rope_scale;
+    const double t = (c->rope_orig / wavelen - c->rope_low) / (c->rope_high - c->rope_low);
+    return (1.0 - t) * speed / c->rope_scale + t * speed;
+}
+
+/* RoPE on one head vector with a block's settings: pair i is (v[2i], v[2i+1])
+ * [LL 02 RoPE; ML] or, in the rotate_half form, (v[i], v[i + d_head/2])
+ * [G2L Positions become a rotation: q*cos + rotate_half(q)*sin], turned by
+ * pos * orc_rope_freq(i) exactly as in orc_rope. */
+void orc_rope_cfg(double* v, long pos, const orc_cfg* c)
+{
+    const int dh = c->d_head, half = dh / 2;
+    for (int i = 0; i < half; ++i) {
+        const double a = (double)pos * orc_rope_freq(c, i);
+        const double cs = cos(a), sn = sin(a);
+        const int iu = c->rope_half ? i : 2 * i, iw = c->rope_half ? i + half : 2 * i + 1;
+        const double u = v[iu], w = v[iw];
+        v[iu] = u * cs - w * sn;
+        v[iw] = u * sn + w * cs;
+    }
+}
+
 /* SiLU [LL 04 SWIGLU (F.silu); L4 The idea (Swish)]: a * sigmoid(a). */
 double orc_silu(double a)
 {
@@ -124,6 +164,9 @@ static int check_cfg(const orc_cfg* c, int B, int S, long start_pos, long cap)
     if (c->n_heads % c->n_kv_heads != 0) return -2;
     if (c->d_head % 2 != 0) return -3;
     if (B < 0 || S < 0 || start_pos < 0 || start_pos + S > cap) return -4;
+    if (c->rope_half != 0 && c->rope_half != 1) return -7;
+    if (c->rope_scale > 1.0 && !(c->rope_low > 0.0 && c->rope_high > c->rope_low && c->rope_orig > 0.0))
+        return -8;
     return 0;
 }
 
@@ -182,7 +225,7 @@ int orc_block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, 
         orc_linear(n1, w->wk, kvd, d, k);
         orc_linear(n1, w->wv, kvd, d, v);
         for (int g = 0; g < G; ++g) {
-            orc_rope(k + (size_t)g * dh, dh, pos, c->rope_theta);
+            orc_rope_cfg(k + (size_t)g * dh, pos, c);
             memcpy(cache_row(k_cache, c, cap, b, g, pos), k + (size_t)g * dh, sizeof(double) * dh);
             memcpy(cache_row(v_cache, c, cap, b, g, pos), v + (size_t)g * dh, sizeof(double) * dh);
         }
@@ -212,7 +255,7 @@ int orc_block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, 
         double* scr = (double*)malloc(sizeof(double) * (size_t)n_keys);
 
         orc_linear(n1, w->wq, qd, d, q);
-        for (int hh = 0; hh < H; ++hh) orc_rope(q + (size_t)hh * dh, dh, pos, c->rope_theta);
+        for (int hh = 0; hh < H; ++hh) orc_rope_cfg(q + (size_t)hh * dh, pos, c);
         for (int hh = 0; hh < H; ++hh) {
             const int g = hh / n_rep;
             orc_attend(q + (size_t)hh * dh, cache_row(k_cache, c, cap, b, g, 0),

@@ -26,6 +26,13 @@ extern "C" {
 typedef struct {
     int d, n_heads, n_kv_heads, d_head, d_ff;
     double rope_theta, norm_eps;
+    /* RoPE variants ("From GPT-2 to Llama", Positions become a rotation):
+     * rope_half = 0 turns the interleaved pairs (2i, 2i+1), 1 the pairs
+     * (i, i + d_head/2) of the rotate_half form.  rope_scale > 1 stretches the
+     * slow pairs as Llama 3.1 does (rope_low / rope_high: the low and high
+     * frequency factors, rope_orig: the original context length); <= 1: none. */
+    int rope_half;
+    double rope_scale, rope_low, rope_high, rope_orig;
 } orc_cfg;
 
 typedef struct {
@@ -45,6 +52,8 @@ int orc_num_threads(void);
 void orc_rms_norm(const double* v, const double* g, int d, double eps, double* out);
 void orc_linear(const double* in, const double* w, int n_out, int n_in, double* out);
 void orc_rope(double* v, int d_head, long pos, double theta);
+double orc_rope_freq(const orc_cfg* c, int i);
+void orc_rope_cfg(double* v, long pos, const orc_cfg* c);
 double orc_silu(double a);
 void orc_attend(const double* q, const double* k_rows, const double* v_rows, long n_keys,
                 int d_head, double* scratch, double* out);

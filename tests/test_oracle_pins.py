@@ -139,6 +139,88 @@ def test_rope_is_complex_rotation_of_adjacent_pairs():
                                    rtol=1e-13)
 
 
+# ------------------------------------------------------------ RoPE variants ----
+
+_L31 = (8.0, 1.0, 4.0, 8192.0)  # scale, low and high frequency factors, original length
+
+
+def _cfg(dh, theta, half=False, scaling=None):
+    return {"d": dh, "H": 1, "n_kv": 1, "d_head": dh, "d_ff": 4, "theta": theta, "eps": 1e-5,
+            "rope_half": half, "rope_scaling": scaling}
+
+
+def test_rope_default_settings_are_the_plain_rotation():
+    """The block's RoPE with interleaved pairs and no frequency scaling is the
+    pinned plain rotation above, bit for bit."""
+    r = rng(21)
+    for dh, theta in [(16, 1e4), (64, 1e5), (128, 5e5)]:
+        v = r.normal(0, 1, dh)
+        for m in (0, 1, 37, 8191):
+            np.testing.assert_array_equal(oracle.rope_cfg(v, m, _cfg(dh, theta)), oracle.rope(v, m, theta))
+
+
+def test_rope_half_layout_is_a_permutation_of_interleaved():
+    """"From GPT-2 to Llama", Positions become a rotation: the rotate_half form
+    pairs dimension i with i + d_head/2; laid out so that those two sit side by
+    side it is the interleaved rotation, bit for bit (both turn pair i by the
+    same angle)."""
+    r = rng(22)
+    for dh, theta, sc in [(64, 1e5, None), (128, 5e5, _L31)]:
+        half = dh // 2
+        perm = np.empty(dh, dtype=int)            # interleaved slot -> half-layout index
+        perm[0::2] = np.arange(half)
+        perm[1::2] = np.arange(half) + half
+        v = r.normal(0, 1, dh)
+        for m in (0, 3, 999, 8191):
+            got = oracle.rope_cfg(v, m, _cfg(dh, theta, half=True, scaling=sc))
+            want_inter = oracle.rope_cfg(v[perm], m, _cfg(dh, theta, half=False, scaling=sc))
+            np.testing.assert_array_equal(got[perm], want_inter)
+
+
+def test_rope_llama31_scaling_counts_match_page():
+    """"From GPT-2 to Llama", Positions become a rotation: Llama 3.1 8B (heads
+    of 128, so 64 pairs, original length 8192) slows its 29 slowest pairs by a
+    factor of 8, leaves its 29 fastest alone and blends the six between."""
+    dh, theta = 128, 5e5
+    base = np.array([oracle.rope_freq(_cfg(dh, theta), i) for i in range(dh // 2)])
+    scaled = np.array([oracle.rope_freq(_cfg(dh, theta, scaling=_L31), i) for i in range(dh // 2)])
+    same = np.sum(scaled == base)
+    slowed = np.sum(scaled == base / 8.0)
+    between = np.sum((scaled < base) & (scaled > base / 8.0))
+    assert (same, slowed, between) == (29, 29, 6), (same, slowed, between)
+    # the fast pairs are the first ones, the slowed ones the last
+    assert np.all(scaled[:29] == base[:29]) and np.all(scaled[-29:] == base[-29:] / 8.0)
+
+
+def test_rope_llama31_blend_meets_both_classes():
+    """The blended speeds join the unchanged and the slowed classes without a
+    jump: sweeping the base continuously moves pairs across the class
+    boundaries, and the scaled speed changes only as much as the base does."""
+    dh = 128
+    i = 32
+    prev = None
+    for theta in np.geomspace(1e4, 1e7, 4001):
+        base = oracle.rope_freq(_cfg(dh, theta), i)
+        sc = oracle.rope_freq(_cfg(dh, theta, scaling=_L31), i)
+        assert base / 8.0 - 1e-15 <= sc <= base + 1e-15
+        if prev is not None:
+            # neighbouring bases differ by < 0.5 %, so must the scaled speeds
+            assert abs(sc / prev - 1.0) < 0.02, (theta, sc, prev)
+        prev = sc
+
+
+def test_rope_variants_keep_relative_invariance():
+    """Every layout / scaling variant still depends only on the distance m - n."""
+    r = rng(23)
+    for half, sc in [(True, None), (False, _L31), (True, _L31)]:
+        c = _cfg(128, 5e5, half=half, scaling=sc)
+        q, k = r.normal(0, 1, 128), r.normal(0, 1, 128)
+        base = float(oracle.rope_cfg(q, 10, c) @ oracle.rope_cfg(k, 3, c))
+        for delta in (1, 1000, 50000):
+            s2 = float(oracle.rope_cfg(q, 10 + delta, c) @ oracle.rope_cfg(k, 3 + delta, c))
+            assert abs(s2 - base) <= 1e-10 * (1 + abs(base))
+
+
 # --------------------------------------------------------------------- SiLU ----
 
 def test_silu_special_values_and_library():
@@ -217,11 +299,23 @@ def _library_block(w, t, start_pos=0, k_prefix=None, v_prefix=None):
     q = F.linear(n1, T["wq"]).view(B, S, H, dh)
     k = F.linear(n1, T["wk"]).view(B, S, G, dh)
     v = F.linear(n1, T["wv"]).view(B, S, G, dh)
-    om = torch.from_numpy(_omegas(dh, w.theta))
+    if w.rope_scaling:
+        # scaled speeds read back from the oracle (pinned by the page's counts)
+        om = torch.tensor([oracle.rope_freq(oracle.cfg_of(w), i) for i in range(dh // 2)],
+                          dtype=torch.float64)
+    else:
+        om = torch.from_numpy(_omegas(dh, w.theta))
     pos = torch.arange(start_pos, start_pos + S, dtype=torch.float64)
     rot = torch.polar(torch.ones(S, dh // 2, dtype=torch.float64), pos[:, None] * om[None, :])
 
     def turn(a):
+        if w.rope_half:
+            # the rotate_half form: a * cos + rotate_half(a) * sin, with
+            # rotate_half(a) = (-a[half:], a[:half]) and the angles repeated
+            a1 = pos[:, None] * om[None, :]
+            ang = torch.cat([a1, a1], dim=-1)[None, :, None, :]
+            rh = torch.cat([-a[..., dh // 2:], a[..., : dh // 2]], dim=-1)
+            return a * torch.cos(ang) + rh * torch.sin(ang)
         c = torch.view_as_complex(a.reshape(*a.shape[:-1], dh // 2, 2).contiguous())
         return torch.view_as_real(c * rot[None, :, None, :]).reshape(a.shape)
 
@@ -250,6 +344,20 @@ def test_block_matches_library_composition(name, kw):
     t = workloads.generate(w)
     y, _, _, _ = oracle.run_workload(w, t)
     want = _library_block(w, t)
+    err = np.abs(y - want).max() / np.sqrt((want ** 2).mean())
+    assert err < 1e-12, err
+
+
+@pytest.mark.parametrize("half,scaling", [(True, None), (False, _L31), (True, _L31)])
+def test_block_rope_variants_match_library_composition(half, scaling):
+    """The rotate_half layout written the way "From GPT-2 to Llama" (Positions
+    become a rotation) prints it, and the Llama 3.1 speeds, through the whole
+    block at a cache offset."""
+    w = _small("tiny_f32", B=2, S=5, start_pos=11, seed=7, rope_half=half, rope_scaling=scaling,
+               theta=5e5)
+    t = workloads.generate(w)
+    y, _, _, _ = oracle.run_workload(w, t)
+    want = _library_block(w, t, 11, t["k_prefix"], t["v_prefix"])
     err = np.abs(y - want).max() / np.sqrt((want ** 2).mean())
     assert err < 1e-12, err
 
@@ -402,6 +510,17 @@ MUTANTS = [
     ("transposed projection", "const double* row = w + (size_t)j * (size_t)n_in;",
      "const double* row = w + (size_t)j;",
      ["test_linear_matches_numpy_matmul"]),
+    ("rotate_half partner off by one", "iw = c->rope_half ? i + half : 2 * i + 1;",
+     "iw = c->rope_half ? (i + half + 1) % dh : 2 * i + 1;",
+     ["test_rope_half_layout_is_a_permutation_of_interleaved"]),
+    ("block RoPE sign", "v[iw] = u * sn + w * cs;", "v[iw] = -u * sn + w * cs;",
+     ["test_rope_default_settings_are_the_plain_rotation", "test_block_matches_library_composition"]),
+    ("scaling classes swapped", "if (wavelen < c->rope_orig / c->rope_high) return speed;",
+     "if (wavelen < c->rope_orig / c->rope_low) return speed;",
+     ["test_rope_llama31_scaling_counts_match_page"]),
+    ("blend weight reversed", "return (1.0 - t) * speed / c->rope_scale + t * speed;",
+     "return t * speed / c->rope_scale + (1.0 - t) * speed;",
+     ["test_rope_llama31_blend_meets_both_classes"]),
 ]
 
 
@@ -429,8 +548,8 @@ def test_planted_mistake_is_caught(tmp_path, label, old, new, pins):
         real = oracle.lib()  # argtypes set on the real library object
         import ctypes
         mut = ctypes.CDLL(str(so))
-        for name in ("orc_rms_norm", "orc_linear", "orc_rope", "orc_silu", "orc_attend",
-                     "orc_block_forward"):
+        for name in ("orc_rms_norm", "orc_linear", "orc_rope", "orc_rope_freq", "orc_rope_cfg",
+                     "orc_silu", "orc_attend", "orc_block_forward"):
             getattr(mut, name).argtypes = getattr(real, name).argtypes
             getattr(mut, name).restype = getattr(real, name).restype
         oracle._lib = mut

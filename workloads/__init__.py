@@ -58,6 +58,8 @@ class BlockWorkload:
     cache_std: float = 1.0  # pre-filled cache rows ~ N(0, cache_std)
     max_seq: int = 0      # cache capacity per sequence (0 -> start_pos + S)
     seed: int = 0
+    rope_half: bool = False   # RoPE pairs (i, i + d_head/2) instead of (2i, 2i+1)
+    rope_scaling: Optional[tuple] = None  # (scale, low, high, original length) or None
 
     @property
     def capacity(self) -> int:
