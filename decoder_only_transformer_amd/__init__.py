@@ -35,7 +35,10 @@ class LbConfig(ctypes.Structure):
                 ("d_ff", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("norm_eps", ctypes.c_double), ("dtype", ctypes.c_int),
-                ("operands", ctypes.c_int)]
+                ("operands", ctypes.c_int), ("rope_layout", ctypes.c_int),
+                ("rope_scale_factor", ctypes.c_double), ("rope_low_freq_factor", ctypes.c_double),
+                ("rope_high_freq_factor", ctypes.c_double),
+                ("rope_original_max_pos", ctypes.c_double)]
 
 
 class LbWeights(ctypes.Structure):
@@ -205,11 +208,15 @@ def llama_block_profile_read(handle: int) -> Tuple[Dict[str, float], int]:
 # ---- small conveniences (allocation / argument packing only) ----------------------------
 
 def make_config(d_model, n_heads, n_kv_heads, d_head, d_ff, max_tokens, max_seq_len, rope_theta,
-                norm_eps, dtype: str, operands: str = "auto") -> LbConfig:
+                norm_eps, dtype: str, operands: str = "auto", rope_half: bool = False,
+                rope_scaling=None) -> LbConfig:
+    """rope_scaling: None or (factor, low_freq_factor, high_freq_factor, original_max_pos)."""
+    sc = rope_scaling or (0.0, 0.0, 0.0, 0.0)
     return LbConfig(d_model, n_heads, n_kv_heads, d_head, d_ff, max_tokens, max_seq_len,
                     float(rope_theta), float(norm_eps), {"f32": LB_F32, "bf16": LB_BF16}[dtype],
                     {"auto": LB_OPERANDS_AUTO, "f16": LB_OPERANDS_F16,
-                     "bf16": LB_OPERANDS_BF16}[operands])
+                     "bf16": LB_OPERANDS_BF16}[operands], 1 if rope_half else 0,
+                    float(sc[0]), float(sc[1]), float(sc[2]), float(sc[3]))
 
 
 def new_kv_cache(batch: int, n_kv: int, max_seq_len: int, d_head: int, dtype, device="cuda",

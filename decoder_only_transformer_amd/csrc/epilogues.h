@@ -29,6 +29,21 @@ struct EpiQKV {
     const float2* rope; // [max_seq][dh/2] (cos, sin)
     SeqPos sp;
     int S, cap, s_stride, nkv, dh, qd;
+    int rope_half;      // columns of a q/k head arrive pair-interleaved (rotate_half weights)
+
+    // 8 rotated values of head columns [j, j+8) to the head that starts at
+    // `head`: as they are, or (rotate_half) slot 2i back to dimension i and
+    // slot 2i+1 back to dimension i + dh/2
+    template <typename T>
+    __device__ __forceinline__ void put(T* head, int j, const float (&v)[8]) const {
+        if (!rope_half) {
+            store8(head + j, v);
+            return;
+        }
+        const float lo[4] = {v[0], v[2], v[4], v[6]}, hi[4] = {v[1], v[3], v[5], v[7]};
+        store4(head + j / 2, lo);
+        store4(head + j / 2 + dh / 2, hi);
+    }
 
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
         const int b = m / S, s = m - b * S, pos = (sp.ragged ? sp.pos[b] : sp.base) + s;
@@ -44,12 +59,12 @@ struct EpiQKV {
                 v[2 * e + 1] = u * t.y + w * t.x;
             }
             if (n < qd) {
-                store8(q + (size_t)m * qd + n, v);
+                put(q + (size_t)m * qd + (n - j), j, v);
             } else {
                 const int g = (n - qd) / dh;
                 const size_t bg = (size_t)b * nkv + g;
-                store8(kc + (bg * cap + pos) * dh + j, v);
-                if (kws) store8(kws + (bg * s_stride + s) * dh + j, v);
+                put(kc + (bg * cap + pos) * dh, j, v);
+                if (kws) put(kws + (bg * s_stride + s) * dh, j, v);
             }
         } else {
             const int nn = n - qd - kvd;

@@ -166,6 +166,7 @@ static EpiQKV<TO, TC> make_qkv(const QkvEpi& e) {
     r.rope = e.rope;
     r.S = e.S;
     r.sp = e.sp;
+    r.rope_half = e.rope_half;
     r.cap = e.cap;
     r.s_stride = e.s_stride;
     r.nkv = e.nkv;

@@ -134,6 +134,23 @@ __global__ void convert_kernel(const TI* __restrict__ src, TO* __restrict__ dst,
         dst[i] = from_f32<TO>(to_f32(src[i]));
 }
 
+// One block per destination row r of a [rows][K] weight; with perm_dh > 0,
+// inside each block of perm_dh rows, row 2i takes source row i and row 2i+1
+// source row i + perm_dh/2.
+template <typename TI, typename TO>
+__global__ void convert_rows_kernel(const TI* __restrict__ src, TO* __restrict__ dst, int K,
+                                    int perm_dh) {
+    const int r = blockIdx.x;
+    int sr = r;
+    if (perm_dh > 0) {
+        const int h = r / perm_dh, j = r % perm_dh;
+        sr = h * perm_dh + (j & 1 ? j / 2 + perm_dh / 2 : j / 2);
+    }
+    const TI* in = src + (size_t)sr * K;
+    TO* out = dst + (size_t)r * K;
+    for (int k = threadIdx.x; k < K; k += blockDim.x) out[k] = from_f32<TO>(to_f32(in[k]));
+}
+
 // Packed row p: group c = p / 8; rows 8c..8c+3 = gate rows 4c..4c+3,
 // rows 8c+4..8c+7 = up rows 4c..4c+3.
 template <typename TI, typename TO>
@@ -213,6 +230,26 @@ hipError_t launch_convert(Elem src_t, Elem dst_t, const void* src, void* dst, si
     if (src_t == Elem::F32 && dst_t == Elem::BF16) CV(float, bf16);
     if (src_t == Elem::F32 && dst_t == Elem::F16) CV(float, f16);
 #undef CV
+    return hipErrorInvalidValue;
+}
+
+template <typename TI, typename TO>
+static hipError_t convert_rows_t(const void* src, void* dst, int rows, int K, int perm_dh,
+                                 hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    convert_rows_kernel<TI, TO><<<rows, 256, 0, s>>>((const TI*)src, (TO*)dst, K, perm_dh);
+    return hipGetLastError();
+}
+
+hipError_t launch_convert_rows(Elem src_t, Elem dst_t, const void* src, void* dst, int rows, int K,
+                               int perm_dh, hipStream_t s) {
+    if (perm_dh < 0 || (perm_dh > 0 && (perm_dh % 2 != 0 || rows % perm_dh != 0)))
+        return hipErrorInvalidValue;
+#define CR(TI, TO) return convert_rows_t<TI, TO>(src, dst, rows, K, perm_dh, s)
+    if (src_t == Elem::F32 && dst_t == Elem::F32) CR(float, float);
+    if (src_t == Elem::BF16 && dst_t == Elem::F16) CR(bf16, f16);
+    if (src_t == Elem::BF16 && dst_t == Elem::BF16) CR(bf16, bf16);
+#undef CR
     return hipErrorInvalidValue;
 }
 

@@ -26,6 +26,11 @@ hipError_t launch_untile(Elem t, const void* src, void* dst, int M, int K, int m
 // dst[i] = src[i] converted (round to nearest even)
 hipError_t launch_convert(Elem src_t, Elem dst_t, const void* src, void* dst, size_t n,
                           hipStream_t s);
+// Row-wise conversion of a [rows][K] weight; with perm_dh > 0 the rows of each
+// block of perm_dh (one head) are reordered: dst row 2i <- src row i,
+// dst row 2i+1 <- src row i + perm_dh/2.
+hipError_t launch_convert_rows(Elem src_t, Elem dst_t, const void* src, void* dst, int rows, int K,
+                               int perm_dh, hipStream_t s);
 // dst [2*dff][d]: row groups of 8 = four gate rows then the same four up rows
 hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const void* up, void* dst,
                                int dff, int d, hipStream_t s);
@@ -40,6 +45,7 @@ struct QkvEpi {
     const float2* rope;
     SeqPos sp;        // start position of each sequence
     int S, cap, s_stride, nkv, dh, qd;
+    int rope_half;    // q/k columns of a head come pair-interleaved; store them in natural order
 };
 // op: operand type of A and W (F32 selects the plain fp32 kernels); cache: cache type.
 // part: fp32 workspace for the split-K decode GEMMs (M <= 64), cap floats;

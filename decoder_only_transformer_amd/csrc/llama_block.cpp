@@ -174,6 +174,14 @@ static lb_status validate_config(const lb_config* c) {
         return fail(nullptr, LB_ERR_INVALID_ARG, "unknown dtype %d", (int)c->dtype);
     if (c->operands != LB_OPERANDS_AUTO && c->operands != LB_OPERANDS_F16 && c->operands != LB_OPERANDS_BF16)
         return fail(nullptr, LB_ERR_INVALID_ARG, "unknown operands %d", (int)c->operands);
+    if (c->rope_layout != LB_ROPE_INTERLEAVED && c->rope_layout != LB_ROPE_HALF)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "unknown rope_layout %d", (int)c->rope_layout);
+    if (c->rope_scale_factor > 1.0 &&
+        !(c->rope_low_freq_factor > 0.0 && c->rope_high_freq_factor > c->rope_low_freq_factor &&
+          c->rope_original_max_pos > 0.0 && std::isfinite(c->rope_scale_factor) &&
+          std::isfinite(c->rope_high_freq_factor) && std::isfinite(c->rope_original_max_pos)))
+        return fail(nullptr, LB_ERR_INVALID_ARG,
+                    "rope scaling needs 0 < low_freq_factor < high_freq_factor and original_max_pos > 0");
     if (c->d_model > 16384)
         return fail(nullptr, LB_ERR_UNSUPPORTED, "d_model > 16384 is not supported (got %d)", c->d_model);
     if (c->dtype == LB_BF16) {
@@ -255,11 +263,24 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
         return fail(nullptr, LB_ERR_OOM, "device allocation failed");
     }
 
-    // RoPE table: (cos, sin) of pos * theta^(-2i/d_head), angles in fp64
-    // ("The Evolving Transformer 04 LLaMA", 02 RoPE).
+    // RoPE table: (cos, sin) of pos * speed_i, angles in fp64, speed_i =
+    // theta^(-2i/d_head) ("The Evolving Transformer 04 LLaMA", 02 RoPE),
+    // stretched as in Llama 3.1 when a scale factor is given ("From GPT-2 to
+    // Llama", Positions become a rotation; the rule is stated in the header).
     std::vector<float2> table((size_t)c.max_seq_len * (dh / 2));
     for (int i = 0; i < dh / 2; ++i) {
-        const double freq = std::pow(c.rope_theta, -2.0 * (double)i / (double)dh);
+        double freq = std::pow(c.rope_theta, -2.0 * (double)i / (double)dh);
+        if (c.rope_scale_factor > 1.0) {
+            const double wavelen = 2.0 * M_PI / freq;
+            const double orig = c.rope_original_max_pos, lo = c.rope_low_freq_factor,
+                         hi = c.rope_high_freq_factor, f = c.rope_scale_factor;
+            if (wavelen > orig / lo) {
+                freq /= f;
+            } else if (wavelen >= orig / hi) {
+                const double t = (orig / wavelen - lo) / (hi - lo);
+                freq = (1.0 - t) * freq / f + t * freq;
+            }
+        }
         for (long pos = 0; pos < c.max_seq_len; ++pos) {
             const double a = (double)pos * freq;
             table[(size_t)pos * (dh / 2) + i] = make_float2((float)std::cos(a), (float)std::sin(a));
@@ -271,9 +292,14 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
     if (e == hipSuccess)
         e = hipMemcpyAsync(blk->rope, table.data(), table.size() * sizeof(float2), hipMemcpyHostToDevice, s);
     const size_t eo_row = (size_t)d * eo;
-    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wq, blk->w_qkv, (size_t)blk->qd * d, s);
+    // rotate_half layout: the rows of each q and k head are reordered so that
+    // the projection puts dimensions i and i + d_head/2 side by side, where the
+    // epilogue turns adjacent pairs; it stores them back in natural order
+    const int perm_dh = c.rope_layout == LB_ROPE_HALF ? dh : 0;
+    if (e == hipSuccess) e = lb::launch_convert_rows(dt, op, w->wq, blk->w_qkv, blk->qd, d, perm_dh, s);
     if (e == hipSuccess)
-        e = lb::launch_convert(dt, op, w->wk, (char*)blk->w_qkv + (size_t)blk->qd * eo_row, (size_t)blk->kvd * d, s);
+        e = lb::launch_convert_rows(dt, op, w->wk, (char*)blk->w_qkv + (size_t)blk->qd * eo_row, blk->kvd, d,
+                                    perm_dh, s);
     if (e == hipSuccess)
         e = lb::launch_convert(dt, op, w->wv, (char*)blk->w_qkv + (size_t)(blk->qd + blk->kvd) * eo_row,
                                (size_t)blk->kvd * d, s);
@@ -391,6 +417,7 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, const l
     qe.nkv = nkv;
     qe.dh = dh;
     qe.qd = blk->qd;
+    qe.rope_half = c.rope_layout == LB_ROPE_HALF;
     mark(1);
     if (dec) e = lb::decode_qkv(op, dt, n1, blk->wt_qkv, M, blk->nqkv, d, qe, ws, s);
     else e = lb::gemm_qkv(op, dt, n1, blk->w_qkv, M, blk->nqkv, d, qe, ws, s);

@@ -58,6 +58,13 @@ typedef enum {
     LB_ERR_HIP = 4           /* a HIP runtime call failed */
 } lb_status;
 
+/* Pairing of the rotated dimensions of a head.  INTERLEAVED turns (2i, 2i+1)
+ * ("The Evolving Transformer 04 LLaMA", 02 RoPE); HALF turns (i, i + d_head/2),
+ * the rotate_half form of "From GPT-2 to Llama", Positions become a rotation
+ * (the layout the SmolLM2 / Hugging Face weights expect).  Either way q, k and
+ * the K cache hold head dimensions in their natural order. */
+typedef enum { LB_ROPE_INTERLEAVED = 0, LB_ROPE_HALF = 1 } lb_rope_layout;
+
 typedef struct {
     int32_t d_model;      /* model width; must equal n_heads * d_head */
     int32_t n_heads;      /* query heads H */
@@ -70,6 +77,20 @@ typedef struct {
     double norm_eps;      /* RMSNorm epsilon (> 0), added to mean(v^2) inside the root */
     lb_dtype dtype;
     lb_operands operands;
+    /* RoPE variants (all zero: interleaved pairs, no frequency scaling). */
+    lb_rope_layout rope_layout;
+    /* Frequency scaling as in Llama 3.1 ("From GPT-2 to Llama", Positions become
+     * a rotation: the slowest pairs are slowed by the factor, the fastest left
+     * alone, those between blended).  rope_scale_factor <= 1: none.  Otherwise,
+     * with wavelength L = 2 pi / speed of a pair: L < original / high_freq_factor
+     * keeps its speed, L > original / low_freq_factor is divided by the factor,
+     * and between them the speed is (1-t) speed / factor + t speed with
+     * t = (original / L - low) / (high - low).  Needs 0 < low < high and
+     * original > 0. */
+    double rope_scale_factor;
+    double rope_low_freq_factor;
+    double rope_high_freq_factor;
+    double rope_original_max_pos;
 } lb_config;
 
 /* Device pointers in cfg.dtype, layouts as above.  init copies (and repacks)

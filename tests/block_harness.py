@@ -25,7 +25,8 @@ def log(msg: str):
 def config_for(w: workloads.BlockWorkload, operands: str = "auto", max_tokens: Optional[int] = None,
                max_seq_len: Optional[int] = None):
     return lbmod.make_config(w.d, w.H, w.n_kv, w.d_head, w.d_ff, max_tokens or w.M,
-                             max_seq_len or w.capacity, w.theta, w.eps, w.dtype, operands)
+                             max_seq_len or w.capacity, w.theta, w.eps, w.dtype, operands,
+                             rope_half=w.rope_half, rope_scaling=w.rope_scaling)
 
 
 def device_weights(tensors: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:

@@ -174,6 +174,48 @@ def test_prefill_two_heads_per_group_dh128(operands):
     run.close()
 
 
+_L31 = (8.0, 1.0, 4.0, 8192.0)  # Llama 3.1 scaling: factor, low / high frequency factors, original length
+
+
+@pytest.mark.parametrize("half,scaling", [(True, None), (True, _L31), (False, _L31)])
+def test_rope_variants_smollm2_width_prefill(half, scaling):
+    """RoPE in the rotate_half layout ("From GPT-2 to Llama", Positions become a
+    rotation: the layout SmolLM2's weights use) and with Llama 3.1 frequency
+    scaling, full parity of y and of the written cache rows (natural dimension
+    order) on a ragged prefill chunk at a cache offset."""
+    w = workloads.with_overrides(workloads.get("smollm2_135m_prefill"), B=2, S=70, start_pos=30,
+                                 max_seq=104, seed=31, rope_half=half, rope_scaling=scaling)
+    run, *_ = _check_block(w)
+    run.close()
+
+
+@pytest.mark.parametrize("half", [False, True])
+def test_rope_variants_llama3_width_decode(half):
+    """Llama-3.1-8B-width decode with its frequency scaling, in both layouts."""
+    w = workloads.with_overrides(workloads.get("llama3_8b_decode"), B=3, start_pos=100, max_seq=128,
+                                 seed=33, rope_half=half, rope_scaling=_L31)
+    run, *_ = _check_block(w)
+    run.close()
+
+
+def test_rope_variants_dh128_prefill_from_zero():
+    """d_head 128 prefill from position 0 (the workspace k / v copies feed the
+    attention) in the rotate_half layout with scaling."""
+    w = workloads.BlockWorkload("dh128_rope", "bf16", B=2, S=130, start_pos=0, d=512, H=4,
+                                n_kv=1, d_head=128, d_ff=1408, theta=5e5, eps=1e-5, w_std=0.02,
+                                g_mean=1.0, g_std=0.05, seed=35, rope_half=True, rope_scaling=_L31)
+    run, *_ = _check_block(w)
+    run.close()
+
+
+def test_rope_variants_fp32_block():
+    """fp32 block (1e-4 bar) in the rotate_half layout with scaling."""
+    w = workloads.with_overrides(workloads.get("tiny_f32"), B=2, S=6, start_pos=5, max_seq=16,
+                                 seed=37, rope_half=True, rope_scaling=_L31, theta=5e5)
+    run, *_ = _check_block(w)
+    run.close()
+
+
 def test_decode_token_by_token_matches_prefill():
     """"Full Llama 3 transformer block", How it works: prefill 40 tokens, then
     decode 8 more one call each; every row matches the oracle's single prefill
