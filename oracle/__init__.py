@@ -76,6 +76,11 @@ def lib():
                                         ctypes.POINTER(ctypes.c_int), ctypes.c_int,
                                         ctypes.POINTER(_Stages)]
         L.orc_block_forward.restype = ctypes.c_int
+        _pp = ctypes.POINTER(_dp)
+        L.orc_stack_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp,
+                                        ctypes.POINTER(_Weights), _dp, _pp, _pp, _dp, _dp]
+        L.orc_stack_forward.restype = ctypes.c_int
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
@@ -188,6 +193,38 @@ def block_forward(cfg: Dict, x, weights: Dict, start_pos: int, k_cache: np.ndarr
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return y, st_arrays
+
+
+def stack_forward(cfg: Dict, x, layers: Sequence[Dict], final_norm, start_pos: int,
+                  caches: Sequence, hidden: bool = False):
+    """Run a stack of blocks and the final RMSNorm (orc_stack_forward).
+
+    layers: one weight dict per block (WEIGHT_NAMES).  caches: one (k, v) pair
+    of float64 [B][n_kv][cap][d_head] arrays per block, updated in place.
+    Returns (y, hidden) with hidden [n_layers][B][S][d] (each block's output)
+    when asked for, else None.
+    """
+    x = _f64(x)
+    B, S, d = x.shape
+    L = len(layers)
+    assert L >= 1 and len(caches) == L and d == cfg["d"]
+    cap = caches[0][0].shape[2]
+    for kc, vc in caches:
+        assert kc.shape == vc.shape and kc.shape[2] == cap
+        _p(kc), _p(vc)
+    c = _cfg_struct(cfg)
+    ws = [{n: _f64(lw[n]) for n in WEIGHT_NAMES} for lw in layers]
+    warr = (_Weights * L)(*[_Weights(*[_p(w[n]) for n in WEIGHT_NAMES]) for w in ws])
+    karr = (_dp * L)(*[_p(kc) for kc, _ in caches])
+    varr = (_dp * L)(*[_p(vc) for _, vc in caches])
+    g = _f64(final_norm)
+    y = np.zeros((B, S, d), dtype=np.float64)
+    hid = np.zeros((L, B, S, d), dtype=np.float64) if hidden else None
+    rc = lib().orc_stack_forward(ctypes.byref(c), L, B, S, int(start_pos), int(cap), _p(x), warr,
+                                 _p(g), karr, varr, _p(hid) if hidden else None, _p(y))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return y, hid
 
 
 def cfg_of(w) -> Dict:

@@ -284,3 +284,37 @@ int orc_block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, 
     free(need);
     return 0;
 }
+
+int orc_stack_forward(const orc_cfg* c, int n_layers, int B, int S, long start_pos, long cap,
+                      const double* x, const orc_weights* layers, const double* final_norm,
+                      double* const* k_caches, double* const* v_caches, double* hidden,
+                      double* y)
+{
+    if (n_layers < 1 || !layers || !final_norm || !k_caches || !v_caches) return -9;
+    int rc = check_cfg(c, B, S, start_pos, cap);
+    if (rc) return rc;
+    const int d = c->d;
+    const long M = (long)B * S;
+    const size_t n = (size_t)(M > 0 ? M : 1) * (size_t)d;
+    double* buf[2] = {NULL, NULL};
+    if (!hidden) {
+        buf[0] = (double*)malloc(sizeof(double) * n);
+        buf[1] = (double*)malloc(sizeof(double) * n);
+        if (!buf[0] || !buf[1]) { free(buf[0]); free(buf[1]); return -5; }
+    }
+    /* the residual stream: each block maps the previous block's output */
+    const double* stream = x;
+    for (int l = 0; l < n_layers && rc == 0; ++l) {
+        double* out = hidden ? hidden + (size_t)l * n : buf[l & 1];
+        rc = orc_block_forward(c, B, S, start_pos, cap, stream, &layers[l], k_caches[l], v_caches[l],
+                               out, NULL, 0, NULL);
+        stream = out;
+    }
+    if (rc == 0) {
+        for (long r = 0; r < M; ++r)
+            orc_rms_norm(stream + (size_t)r * d, final_norm, d, c->norm_eps, y + (size_t)r * d);
+    }
+    free(buf[0]);
+    free(buf[1]);
+    return rc;
+}

@@ -67,6 +67,20 @@ int orc_block_forward(const orc_cfg* cfg, int B, int S, long start_pos, long cap
                       const double* x, const orc_weights* w, double* k_cache, double* v_cache,
                       double* y, const int* rows, int n_rows, orc_stages* stages);
 
+/* A stack of n_layers blocks and the final RMSNorm: block l takes the output
+ * of block l-1 (block 0 takes x), and y = RMSNorm(output of the last block)
+ * with gain final_norm and the config's epsilon ("The Evolving Transformer 04
+ * LLaMA", 07 ASSEMBLE LLAMA; "Full Llama 3 transformer block", Overview: the
+ * block is the unit stacked L times; embedding and output projection are not
+ * part of this function).  layers, k_caches, v_caches: n_layers entries, block
+ * l reading and writing its own cache pair as orc_block_forward does.
+ * hidden (optional, may be NULL): [n_layers][B][S][d] receives each block's
+ * output.  Returns 0, or a negative code for an invalid argument. */
+int orc_stack_forward(const orc_cfg* cfg, int n_layers, int B, int S, long start_pos, long cap,
+                      const double* x, const orc_weights* layers, const double* final_norm,
+                      double* const* k_caches, double* const* v_caches, double* hidden,
+                      double* y);
+
 #ifdef __cplusplus
 }
 #endif

@@ -487,6 +487,98 @@ def test_workload_shapes_match_pages():
     assert wt.d_ff == 16 * math.ceil(8 * wt.d / 3 / 16)
 
 
+# ------------------------------------------------------------------ stack ----
+# "The Evolving Transformer 04 LLaMA", 07 ASSEMBLE LLAMA: N blocks, then a
+# final RMSNorm; "Full Llama 3 transformer block", Overview: the block is the
+# unit stacked L times.
+
+def _np_rms(v, g, eps):
+    return v / np.sqrt(np.mean(v * v, axis=-1, keepdims=True) + eps) * g
+
+
+def _stack_caches(w, L):
+    return [oracle.empty_cache(w) for _ in range(L)]
+
+
+def test_stack_of_identity_blocks_is_the_final_norm():
+    """Blocks with Wo = 0 and W_down = 0 pass the stream through unchanged, so
+    every block output is x and y is RMSNorm(x) * final gain (closed form)."""
+    w = _small("tiny_f32", B=2, S=5, seed=3)
+    st = workloads.generate_stack(w, 3)
+    layers = [dict(t, wo=torch.zeros_like(t["wo"]), w_down=torch.zeros_like(t["w_down"]))
+              for t in st["layers"]]
+    y, hid = oracle.stack_forward(oracle.cfg_of(w), st["x"], layers, st["final_norm"], 0,
+                                  _stack_caches(w, 3), hidden=True)
+    x = st["x"].double().numpy()
+    for l in range(3):
+        np.testing.assert_array_equal(hid[l], x)
+    want = _np_rms(x, st["final_norm"].double().numpy(), w.eps)
+    np.testing.assert_allclose(y, want, rtol=1e-14, atol=1e-15)
+
+
+def _diag_stack(d, consts, seed):
+    """Blocks whose output has a closed form: Wo = 0 (the attention branch adds
+    exactly zero), W_gate = b I, W_up = a I, W_down = c I with d_ff = d (so
+    FFN(n) = c SiLU(b n) (a n) per element), and Wk = k I with n_kv * d_head =
+    d (so the K row a token writes at position 0, where the rotation is the
+    identity, is k RMSNorm_1(input))."""
+    r = rng(seed)
+    I = np.eye(d)
+    layers = []
+    for (a, b, c, k) in consts:
+        layers.append({"attn_norm": r.uniform(0.5, 1.5, d), "wq": r.normal(0, 0.2, (d, d)),
+                       "wk": k * I, "wv": r.normal(0, 0.2, (d, d)), "wo": np.zeros((d, d)),
+                       "ffn_norm": r.uniform(0.5, 1.5, d), "w_gate": b * I, "w_up": a * I,
+                       "w_down": c * I})
+    return layers
+
+
+def test_stack_chains_blocks_in_order_closed_form():
+    """Three blocks with different closed-form maps, one token per sequence at
+    position 0: y and every block's K and V cache row follow from chaining
+    the closed forms in order (block l reads block l-1's output, each writes
+    its own cache, the final norm comes last)."""
+    d, eps = 16, 1e-5
+    cfg = {"d": d, "H": 2, "n_kv": 2, "d_head": 8, "d_ff": d, "theta": 1e4, "eps": eps}
+    consts = [(1.3, 0.7, 0.9, 1.1), (-0.6, 1.9, 1.4, 0.8), (2.1, -1.2, -0.5, 1.7)]
+    layers = _diag_stack(d, consts, 7)
+    r = rng(8)
+    x = r.normal(0, 1, (2, 1, d))
+    gf = r.uniform(0.5, 1.5, d)
+    caches = [(np.zeros((2, 2, 3, 8)), np.zeros((2, 2, 3, 8))) for _ in layers]
+    y, hid = oracle.stack_forward(cfg, x, layers, gf, 0, caches, hidden=True)
+    silu = lambda u: u / (1.0 + np.exp(-u))
+    v = x[:, 0, :]
+    for l, ((a, b, c, k), lw) in enumerate(zip(consts, layers)):
+        n1 = _np_rms(v, lw["attn_norm"], eps)
+        np.testing.assert_allclose(caches[l][0][:, :, 0, :].reshape(2, d), k * n1, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(caches[l][1][:, :, 0, :].reshape(2, d), n1 @ lw["wv"].T, rtol=1e-12,
+                                   atol=1e-13)
+        n2 = _np_rms(v, lw["ffn_norm"], eps)
+        v = v + c * silu(b * n2) * (a * n2)
+        np.testing.assert_allclose(hid[l][:, 0, :], v, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(y[:, 0, :], _np_rms(v, gf, eps), rtol=1e-13, atol=1e-14)
+
+
+def test_stack_prefill_equals_token_by_token_decode():
+    """"Full Llama 3 transformer block", How it works: with each block keeping
+    its own cache, S single-token steps of the stack give the rows of one
+    causal prefill of the stack, and leave the same caches."""
+    w = _small("tiny_f32", B=2, S=7, seed=12)
+    st = workloads.generate_stack(w, 3)
+    cfg = oracle.cfg_of(w)
+    full = _stack_caches(w, 3)
+    y_full, _ = oracle.stack_forward(cfg, st["x"], st["layers"], st["final_norm"], 0, full)
+    steps = _stack_caches(w, 3)
+    x = st["x"].double().numpy()
+    for s in range(w.S):
+        y_s, _ = oracle.stack_forward(cfg, x[:, s:s + 1, :].copy(), st["layers"], st["final_norm"], s, steps)
+        np.testing.assert_allclose(y_s[:, 0, :], y_full[:, s, :], rtol=0, atol=1e-13)
+    for (ka, va), (kb, vb) in zip(full, steps):
+        np.testing.assert_allclose(ka, kb, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(va, vb, rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------- planted mistakes are caught ----
 
 MUTANTS = [
@@ -521,6 +613,19 @@ MUTANTS = [
     ("blend weight reversed", "return (1.0 - t) * speed / c->rope_scale + t * speed;",
      "return t * speed / c->rope_scale + (1.0 - t) * speed;",
      ["test_rope_llama31_blend_meets_both_classes"]),
+    ("stack: every block reads x",
+     "rc = orc_block_forward(c, B, S, start_pos, cap, stream, &layers[l]",
+     "rc = orc_block_forward(c, B, S, start_pos, cap, x, &layers[l]",
+     ["test_stack_chains_blocks_in_order_closed_form"]),
+    ("stack: final norm left out",
+     "orc_rms_norm(stream + (size_t)r * d, final_norm, d, c->norm_eps, y + (size_t)r * d);",
+     "memcpy(y + (size_t)r * d, stream + (size_t)r * d, sizeof(double) * (size_t)d);",
+     ["test_stack_of_identity_blocks_is_the_final_norm", "test_stack_chains_blocks_in_order_closed_form"]),
+    ("stack: one cache for every block", "k_caches[l], v_caches[l]", "k_caches[0], v_caches[0]",
+     ["test_stack_chains_blocks_in_order_closed_form", "test_stack_prefill_equals_token_by_token_decode"]),
+    ("stack: last block dropped", "for (int l = 0; l < n_layers && rc == 0; ++l)",
+     "for (int l = 0; l < n_layers - 1 && rc == 0; ++l)",
+     ["test_stack_chains_blocks_in_order_closed_form"]),
 ]
 
 
@@ -549,7 +654,7 @@ def test_planted_mistake_is_caught(tmp_path, label, old, new, pins):
         import ctypes
         mut = ctypes.CDLL(str(so))
         for name in ("orc_rms_norm", "orc_linear", "orc_rope", "orc_rope_freq", "orc_rope_cfg",
-                     "orc_silu", "orc_attend", "orc_block_forward"):
+                     "orc_silu", "orc_attend", "orc_block_forward", "orc_stack_forward"):
             getattr(mut, name).argtypes = getattr(real, name).argtypes
             getattr(mut, name).restype = getattr(real, name).restype
         oracle._lib = mut

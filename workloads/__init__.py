@@ -34,7 +34,8 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["BlockWorkload", "WORKLOADS", "get", "generate", "param_count", "with_overrides"]
+__all__ = ["BlockWorkload", "WORKLOADS", "get", "generate", "generate_stack", "param_count",
+           "stack_layer_seed", "with_overrides"]
 
 
 @dataclass(frozen=True)
@@ -158,3 +159,34 @@ def generate(w: BlockWorkload, with_cache: bool = True) -> Dict[str, torch.Tenso
         out["k_prefix"] = _draw(gen, shape, 0.0, w.cache_std, dt)
         out["v_prefix"] = _draw(gen, shape, 0.0, w.cache_std, dt)
     return out
+
+
+def stack_layer_seed(seed: int, layer: int) -> int:
+    """Seed of block `layer` of a stack drawn from a workload with `seed`."""
+    return seed * 1_000_003 + 7919 * (layer + 1)
+
+
+def generate_stack(w: BlockWorkload, n_layers: int, with_cache: bool = True) -> Dict:
+    """Draw a stack of n_layers blocks of the workload's shape.
+
+    x [B][S][d] and the final RMSNorm gain final_norm [d] come from the
+    workload's own generator (x first, then the gain, drawn like the block's
+    gains).  Block l's tensors are those of generate() for the same workload
+    with seed stack_layer_seed(w.seed, l), without its x: its own weights and,
+    for start_pos > 0, its own pre-filled cache rows.  Returns {"x", "final_norm",
+    "layers": [dict per block]}.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed)
+    dt = w.torch_dtype
+    x = _draw(gen, (w.B, w.S, w.d), 0.0, w.x_std, dt)
+    if w.g_std is None:
+        final = torch.full((w.d,), w.g_mean, dtype=torch.float32).to(dt)
+    else:
+        final = _draw(gen, (w.d,), w.g_mean, w.g_std, dt)
+    layers = []
+    for l in range(n_layers):
+        t = generate(with_overrides(w, seed=stack_layer_seed(w.seed, l)), with_cache=with_cache)
+        del t["x"]
+        layers.append(t)
+    return {"x": x, "final_norm": final, "layers": layers}
