@@ -24,7 +24,11 @@ ELEM_NAMES = {0: "f32", 1: "bf16", 2: "f16"}
 MAX_RAGGED_BATCH = 64
 EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_forward_ragged", "llama_block_destroy",
            "llama_block_status_string", "llama_block_last_error", "llama_block_stage_info",
-           "llama_block_copy_stage", "llama_block_profile", "llama_block_profile_read")
+           "llama_block_copy_stage", "llama_block_profile", "llama_block_profile_read",
+           "llama_stack_init", "llama_stack_forward", "llama_stack_forward_device_pos",
+           "llama_stack_graph_create", "llama_stack_graph_launch", "llama_stack_graph_destroy",
+           "llama_stack_destroy", "llama_stack_num_layers", "llama_stack_last_error")
+MAX_STACK_LAYERS = 1024
 STAGE_NAMES = ("rmsnorm_1", "qkv_rope_append", "attention", "o_proj_residual", "rmsnorm_2",
                "gate_up_swiglu", "down_residual")
 
@@ -96,6 +100,27 @@ def lib() -> ctypes.CDLL:
         L.llama_block_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_int64)]
         L.llama_block_profile_read.restype = ctypes.c_int
+        kvp = ctypes.POINTER(LbKVCache)
+        L.llama_stack_init.argtypes = [ctypes.POINTER(LbConfig), i32, ctypes.POINTER(LbWeights), vp,
+                                       ctypes.POINTER(vp)]
+        L.llama_stack_init.restype = ctypes.c_int
+        L.llama_stack_forward.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(ctypes.c_int32), kvp,
+                                          vp, vp, vp]
+        L.llama_stack_forward.restype = ctypes.c_int
+        L.llama_stack_forward_device_pos.argtypes = [vp, vp, i32, i32, vp, i32, kvp, vp, vp, vp]
+        L.llama_stack_forward_device_pos.restype = ctypes.c_int
+        L.llama_stack_graph_create.argtypes = [vp, vp, i32, i32, vp, kvp, vp, ctypes.POINTER(vp)]
+        L.llama_stack_graph_create.restype = ctypes.c_int
+        L.llama_stack_graph_launch.argtypes = [vp, vp]
+        L.llama_stack_graph_launch.restype = ctypes.c_int
+        L.llama_stack_graph_destroy.argtypes = [vp]
+        L.llama_stack_graph_destroy.restype = None
+        L.llama_stack_destroy.argtypes = [vp]
+        L.llama_stack_destroy.restype = None
+        L.llama_stack_num_layers.argtypes = [vp]
+        L.llama_stack_num_layers.restype = i32
+        L.llama_stack_last_error.argtypes = [vp]
+        L.llama_stack_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -205,6 +230,91 @@ def llama_block_profile_read(handle: int) -> Tuple[Dict[str, float], int]:
     return {n: arr[i] for i, n in enumerate(STAGE_NAMES)}, calls.value
 
 
+def _check_stack(handle, status: int, what: str):
+    if status != LB_OK:
+        L = lib()
+        msg = L.llama_stack_last_error(handle).decode() or L.llama_block_status_string(status).decode()
+        raise LlamaBlockError(status, f"{what}: {msg}")
+
+
+def _kv_array(kv_list):
+    arr = (LbKVCache * len(kv_list))()
+    for i, (k, v) in enumerate(kv_list):
+        arr[i] = LbKVCache(_ptr(k), _ptr(v), int(k.shape[0]), int(k.shape[2]))
+    return arr
+
+
+def llama_stack_init(cfg: LbConfig, layers, final_norm) -> int:
+    """layers: one dict of device tensors per block (LbWeights names);
+    final_norm: device tensor [d_model].  Returns the handle.  Synchronous."""
+    n = len(layers)
+    arr = (LbWeights * max(n, 1))()
+    for i, w in enumerate(layers):
+        arr[i] = LbWeights(*[_ptr(w[nm]) for nm in WEIGHT_NAMES])
+    h = ctypes.c_void_p()
+    st = lib().llama_stack_init(ctypes.byref(cfg), n, arr, _ptr(final_norm), ctypes.byref(h))
+    _check_stack(None, st, "llama_stack_init")
+    return h.value
+
+
+def llama_stack_forward(handle: int, x, start_pos, kv_list, out, hidden=None, stream=None) -> None:
+    """start_pos: one int, or one per sequence; kv_list: one (k, v) per block;
+    hidden: optional device tensor [n_layers][B][S][d]."""
+    B, S = int(x.shape[0]), int(x.shape[1])
+    if hasattr(start_pos, "__len__"):
+        pos = [int(p) for p in start_pos]
+        if len(pos) != B:
+            raise ValueError(f"need one start position per sequence ({B}), got {len(pos)}")
+        starts, base = (ctypes.c_int32 * B)(*pos), 0
+    else:
+        starts, base = None, int(start_pos)
+    st = lib().llama_stack_forward(handle, _ptr(x), B, S, base, starts, _kv_array(kv_list), _ptr(out),
+                                   _ptr(hidden), _stream(stream))
+    _check_stack(handle, st, "llama_stack_forward")
+
+
+def llama_stack_forward_device_pos(handle: int, x, positions, advance: bool, kv_list, out, hidden=None,
+                                   stream=None) -> None:
+    """positions: int32 device tensor [B], read (and with advance, moved on by
+    S) by the kernels."""
+    B, S = int(x.shape[0]), int(x.shape[1])
+    st = lib().llama_stack_forward_device_pos(handle, _ptr(x), B, S, _ptr(positions), 1 if advance else 0,
+                                              _kv_array(kv_list), _ptr(out), _ptr(hidden), _stream(stream))
+    _check_stack(handle, st, "llama_stack_forward_device_pos")
+
+
+def llama_stack_graph_create(handle: int, x, positions, kv_list, out) -> int:
+    B, S = int(x.shape[0]), int(x.shape[1])
+    g = ctypes.c_void_p()
+    st = lib().llama_stack_graph_create(handle, _ptr(x), B, S, _ptr(positions), _kv_array(kv_list),
+                                        _ptr(out), ctypes.byref(g))
+    _check_stack(handle, st, "llama_stack_graph_create")
+    return g.value
+
+
+def llama_stack_graph_launch(graph: int, stream=None, handle=None) -> None:
+    st = lib().llama_stack_graph_launch(graph, _stream(stream))
+    _check_stack(handle, st, "llama_stack_graph_launch")
+
+
+def llama_stack_graph_destroy(graph: int) -> None:
+    if graph:
+        lib().llama_stack_graph_destroy(graph)
+
+
+def llama_stack_destroy(handle: int) -> None:
+    if handle:
+        lib().llama_stack_destroy(handle)
+
+
+def llama_stack_num_layers(handle: int) -> int:
+    return int(lib().llama_stack_num_layers(handle))
+
+
+def llama_stack_last_error(handle=None) -> str:
+    return lib().llama_stack_last_error(handle).decode()
+
+
 # ---- small conveniences (allocation / argument packing only) ----------------------------
 
 def make_config(d_model, n_heads, n_kv_heads, d_head, d_ff, max_tokens, max_seq_len, rope_theta,
@@ -264,3 +374,59 @@ class LlamaBlock:
             self.close()
         except Exception:
             pass
+
+
+class LlamaStack:
+    """Owns one stack handle (and the graphs made from it)."""
+
+    def __init__(self, cfg: LbConfig, layers, final_norm):
+        self.cfg = cfg
+        self.handle = llama_stack_init(cfg, layers, final_norm)
+        self.graphs = []
+
+    @property
+    def n_layers(self) -> int:
+        return llama_stack_num_layers(self.handle)
+
+    def forward(self, x, start_pos, kv_list, out, hidden=None, stream=None):
+        llama_stack_forward(self.handle, x, start_pos, kv_list, out, hidden, stream)
+        return out
+
+    def forward_device_pos(self, x, positions, kv_list, out, advance=True, hidden=None, stream=None):
+        llama_stack_forward_device_pos(self.handle, x, positions, advance, kv_list, out, hidden, stream)
+        return out
+
+    def capture(self, x, positions, kv_list, out) -> "StackGraph":
+        g = StackGraph(self, llama_stack_graph_create(self.handle, x, positions, kv_list, out))
+        self.graphs.append(g)
+        return g
+
+    def close(self):
+        for g in self.graphs:
+            g.close()
+        self.graphs = []
+        if self.handle:
+            llama_stack_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class StackGraph:
+    """A captured step of a stack: launch() replays it on a stream."""
+
+    def __init__(self, stack: LlamaStack, graph: int):
+        self.stack = stack
+        self.graph = graph
+
+    def launch(self, stream=None):
+        llama_stack_graph_launch(self.graph, stream, self.stack.handle)
+
+    def close(self):
+        if self.graph:
+            llama_stack_graph_destroy(self.graph)
+            self.graph = None

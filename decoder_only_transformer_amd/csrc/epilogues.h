@@ -46,7 +46,7 @@ struct EpiQKV {
     }
 
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
-        const int b = m / S, s = m - b * S, pos = (sp.ragged ? sp.pos[b] : sp.base) + s;
+        const int b = m / S, s = m - b * S, pos = LB_SEQ_START(sp, b) + s;
         const int kvd = nkv * dh;
         if (n < qd + kvd) {
             const int j = (n < qd ? n : n - qd) % dh;

@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(NW * 64) attn_prefill_kernel(
     const int hb = blockIdx.x % n_hb;
     const int bg = blockIdx.x / n_hb;
     const int g = bg % nkv, b = bg / nkv;
-    const int start_pos = sp.ragged ? sp.pos[b] : sp.base;
+    const int start_pos = LB_SEQ_START(sp, b);
     const int hl = hb * NW + wave;
     const bool head_ok = hl < n_rep;
     const int h = g * n_rep + (head_ok ? hl : n_rep - 1);
@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
     const int hb = blockIdx.x % n_hb;
     const int bg = blockIdx.x / n_hb;
     const int g = bg % nkv, b = bg / nkv;
-    const int start_pos = sp.ragged ? sp.pos[b] : sp.base;
+    const int start_pos = LB_SEQ_START(sp, b);
     const int hl = hb * NWH + hw;
     const bool head_ok = hl < n_rep;
     const int h = g * n_rep + (head_ok ? hl : n_rep - 1);
@@ -504,7 +504,7 @@ __global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int split = blockIdx.x, bg = blockIdx.y;
     const int b = bg / nkv, g = bg % nkv;
-    const int kv_len = (sp.ragged ? sp.pos[b] : sp.base) + 1;  // keys of this sequence, its new one included
+    const int kv_len = LB_SEQ_START(sp, b) + 1;  // keys of this sequence, its new one included
     const int hl = lane & 15, grp = lane >> 4;
     bf16* my_a = slab_a + wave * SLAB;
     bf16* my_b = slab_b + wave * SLAB;
@@ -737,7 +737,7 @@ __global__ void __launch_bounds__(64) attn_simple_kernel(const float* __restrict
     const int lane = threadIdx.x;
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int g = h / (H / nkv);
-    const int n = (sp.ragged ? sp.pos[b] : sp.base) + s + 1;
+    const int n = LB_SEQ_START(sp, b) + s + 1;
     const size_t bg = (size_t)b * nkv + g;
     const float* qp = q + ((size_t)b * S + s) * H * dh + (size_t)h * dh;
     for (int d = lane; d < dh; d += 64) qs[d] = qp[d];

@@ -271,4 +271,17 @@ hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const v
     return hipErrorInvalidValue;
 }
 
+// Device-held start positions move on by the tokens of the step that read
+// them; queued after that step's last kernel on the same stream.
+__global__ void __launch_bounds__(256) advance_positions_kernel(int* __restrict__ pos, int B, int S) {
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b < B) pos[b] += S;
+}
+
+hipError_t launch_advance_positions(int* pos, int B, int S, hipStream_t s) {
+    if (B <= 0) return hipSuccess;
+    advance_positions_kernel<<<(B + 255) / 256, 256, 0, s>>>(pos, B, S);
+    return hipGetLastError();
+}
+
 }  // namespace lb

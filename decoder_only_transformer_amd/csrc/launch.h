@@ -31,6 +31,8 @@ hipError_t launch_convert(Elem src_t, Elem dst_t, const void* src, void* dst, si
 // dst row 2i+1 <- src row i + perm_dh/2.
 hipError_t launch_convert_rows(Elem src_t, Elem dst_t, const void* src, void* dst, int rows, int K,
                                int perm_dh, hipStream_t s);
+// pos[b] += S for b < B (device array)
+hipError_t launch_advance_positions(int* pos, int B, int S, hipStream_t s);
 // dst [2*dff][d]: row groups of 8 = four gate rows then the same four up rows
 hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const void* up, void* dst,
                                int dff, int d, hipStream_t s);

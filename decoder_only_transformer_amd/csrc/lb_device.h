@@ -17,16 +17,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Start position of every sequence of one forward: all at `base`, or (ragged)
-// sequence b at pos[b], b < kMaxRagged.  Passed by value in kernel arguments;
-// device code reads `ragged ? pos[b] : base` from the argument itself (a
-// member function taking `this` would copy the argument to scratch memory).
+// Start position of every sequence of one forward: all at `base`, (ragged)
+// sequence b at pos[b], b < kMaxRagged, or (dev != nullptr) read at run time
+// from the device array dev[b] and clamped to [0, lim], so that no value in
+// that array can take an access out of the cache or the RoPE table.  Passed by
+// value in kernel arguments; device code reads it through LB_SEQ_START, which
+// names the members of the argument itself (a member function taking `this`
+// would copy the argument to scratch memory).
 constexpr int kMaxRagged = 64;
 struct SeqPos {
     int base;
     int ragged;
     int pos[kMaxRagged];
+    const int* dev;
+    int lim;
 };
+#define LB_SEQ_START(sp, b)                                                  \
+    ((sp).dev ? min(max((sp).dev[(b)], 0), (sp).lim)                        \
+              : ((sp).ragged ? (sp).pos[(b)] : (sp).base))
 
 // ---- scalar conversions (fp32 <-> storage types, round to nearest even) ----
 __device__ __forceinline__ float to_f32(float v) { return v; }

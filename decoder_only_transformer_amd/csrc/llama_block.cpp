@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -23,13 +24,8 @@
 
 using lb::Elem;
 
-struct lb_block {
-    lb_config cfg;
-    Elem dt = Elem::F32;  // dtype of x, out, cache
-    Elem op = Elem::F32;  // matrix-product operand type
-    int dev = 0;
-    int qd = 0, kvd = 0, nqkv = 0;
-    // packed weights
+// Packed weights of one block.
+struct LayerW {
     void* w_qkv = nullptr;
     void* w_o = nullptr;
     void* w_gu = nullptr;
@@ -41,6 +37,15 @@ struct lb_block {
     void* wt_down = nullptr;
     float* g1 = nullptr;
     float* g2 = nullptr;
+};
+
+struct lb_block {
+    lb_config cfg;
+    Elem dt = Elem::F32;  // dtype of x, out, cache
+    Elem op = Elem::F32;  // matrix-product operand type
+    int dev = 0;
+    int qd = 0, kvd = 0, nqkv = 0;
+    LayerW lw;  // this block's weights
     float2* rope = nullptr;
     // workspace
     void* n1 = nullptr;
@@ -200,14 +205,67 @@ static lb_status validate_config(const lb_config* c) {
     return LB_OK;
 }
 
-extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w, lb_block** out) {
-    g_init_error.clear();
-    if (!out) return fail(nullptr, LB_ERR_INVALID_ARG, "out is NULL");
-    *out = nullptr;
-    if (!cfg || !w) return fail(nullptr, LB_ERR_INVALID_ARG, "cfg or weights is NULL");
+// Allocate one block's packed weights (owned by blk's allocation list).
+static bool alloc_layer(lb_block* blk, LayerW* L) {
+    const lb_config& c = blk->cfg;
+    const int d = c.d_model, dff = c.d_ff;
+    const size_t eo = esz(blk->op);
+    bool ok = dalloc(blk, &L->w_qkv, (size_t)blk->nqkv * d * eo) &&
+              dalloc(blk, &L->w_o, (size_t)d * blk->qd * eo) &&
+              dalloc(blk, &L->w_gu, (size_t)2 * dff * d * eo) &&
+              dalloc(blk, &L->w_down, (size_t)d * dff * eo) && dalloc(blk, &L->g1, (size_t)d * 4) &&
+              dalloc(blk, &L->g2, (size_t)d * 4);
+    if (ok && blk->dt == Elem::BF16)
+        ok = dalloc(blk, &L->wt_qkv, (size_t)blk->nqkv * d * eo) &&
+             dalloc(blk, &L->wt_o, (size_t)d * blk->qd * eo) &&
+             dalloc(blk, &L->wt_gu, (size_t)2 * dff * d * eo) &&
+             dalloc(blk, &L->wt_down, (size_t)d * dff * eo);
+    return ok;
+}
+
+static bool weights_complete(const lb_weights* w) {
     const void* wp[9] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
     for (const void* p : wp)
-        if (!p) return fail(nullptr, LB_ERR_INVALID_ARG, "a weight pointer is NULL");
+        if (!p) return false;
+    return true;
+}
+
+// Enqueue the packing of one block's weights from the caller's tensors.
+static hipError_t pack_layer(const lb_block* blk, const lb_weights* w, const LayerW& L, hipStream_t s) {
+    const lb_config& c = blk->cfg;
+    const int d = c.d_model, dh = c.d_head, dff = c.d_ff;
+    const Elem op = blk->op, dt = blk->dt;
+    const size_t eo_row = (size_t)d * esz(op);
+    // rotate_half layout: the rows of each q and k head are reordered so that
+    // the projection puts dimensions i and i + d_head/2 side by side, where the
+    // epilogue turns adjacent pairs; it stores them back in natural order
+    const int perm_dh = c.rope_layout == LB_ROPE_HALF ? dh : 0;
+    hipError_t e = lb::launch_convert_rows(dt, op, w->wq, L.w_qkv, blk->qd, d, perm_dh, s);
+    if (e == hipSuccess)
+        e = lb::launch_convert_rows(dt, op, w->wk, (char*)L.w_qkv + (size_t)blk->qd * eo_row, blk->kvd, d,
+                                    perm_dh, s);
+    if (e == hipSuccess)
+        e = lb::launch_convert(dt, op, w->wv, (char*)L.w_qkv + (size_t)(blk->qd + blk->kvd) * eo_row,
+                               (size_t)blk->kvd * d, s);
+    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wo, L.w_o, (size_t)d * blk->qd, s);
+    if (e == hipSuccess) e = lb::launch_pack_gate_up(dt, op, w->w_gate, w->w_up, L.w_gu, dff, d, s);
+    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->w_down, L.w_down, (size_t)d * dff, s);
+    if (e == hipSuccess && dt == Elem::BF16) {
+        e = lb::launch_tile_weights(op, L.w_qkv, L.wt_qkv, blk->nqkv, d, s);
+        if (e == hipSuccess) e = lb::launch_tile_weights(op, L.w_o, L.wt_o, d, blk->qd, s);
+        if (e == hipSuccess) e = lb::launch_tile_weights(op, L.w_gu, L.wt_gu, 2 * dff, d, s);
+        if (e == hipSuccess) e = lb::launch_tile_weights(op, L.w_down, L.wt_down, d, dff, s);
+    }
+    if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->attn_norm, L.g1, (size_t)d, s);
+    if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->ffn_norm, L.g2, (size_t)d, s);
+    return e;
+}
+
+// A handle with the config, the RoPE table and the workspace, but no weights
+// yet.  Synchronous.  On error *out stays NULL and the message is in
+// g_init_error.
+static lb_status create_core(const lb_config* cfg, lb_block** out) {
+    *out = nullptr;
     lb_status st = validate_config(cfg);
     if (st != LB_OK) return st;
 
@@ -220,20 +278,15 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
         delete blk;
         return fail(nullptr, LB_ERR_HIP, "hipGetDevice failed");
     }
-    const int d = c.d_model, dh = c.d_head, nkv = c.n_kv_heads, dff = c.d_ff;
+    const int d = c.d_model, dh = c.d_head, dff = c.d_ff;
     blk->qd = c.n_heads * dh;
-    blk->kvd = nkv * dh;
+    blk->kvd = c.n_kv_heads * dh;
     blk->nqkv = blk->qd + 2 * blk->kvd;
     const size_t T = (size_t)c.max_tokens;
     const Elem op = blk->op, dt = blk->dt;
     const size_t eo = esz(op);
 
-    bool ok = dalloc(blk, &blk->w_qkv, (size_t)blk->nqkv * d * eo) &&
-              dalloc(blk, &blk->w_o, (size_t)d * blk->qd * eo) &&
-              dalloc(blk, &blk->w_gu, (size_t)2 * dff * d * eo) &&
-              dalloc(blk, &blk->w_down, (size_t)d * dff * eo) && dalloc(blk, &blk->g1, (size_t)d * 4) &&
-              dalloc(blk, &blk->g2, (size_t)d * 4) &&
-              dalloc(blk, &blk->rope, (size_t)c.max_seq_len * (dh / 2) * sizeof(float2)) &&
+    bool ok = dalloc(blk, &blk->rope, (size_t)c.max_seq_len * (dh / 2) * sizeof(float2)) &&
               dalloc(blk, &blk->n1, T * d * eo) && dalloc(blk, &blk->n2, T * d * eo) &&
               dalloc(blk, &blk->q, T * blk->qd * eo) && dalloc(blk, &blk->o, T * blk->qd * eo) &&
               dalloc(blk, &blk->z, T * dff * eo) && dalloc(blk, &blk->h, T * d * 4);
@@ -248,10 +301,6 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
              dalloc(blk, &blk->gpart, (blk->gpart_cap = lb::skinny_partials_floats(
                                            c.max_tokens < 64 ? c.max_tokens : 64,
                                            std::max(std::max(blk->nqkv, d), 2 * dff))) * sizeof(float)) &&
-             dalloc(blk, &blk->wt_qkv, (size_t)blk->nqkv * d * eo) &&
-             dalloc(blk, &blk->wt_o, (size_t)d * blk->qd * eo) &&
-             dalloc(blk, &blk->wt_gu, (size_t)2 * dff * d * eo) &&
-             dalloc(blk, &blk->wt_down, (size_t)d * dff * eo) &&
              dalloc(blk, &blk->at_n1, (size_t)kDecodeRows * d * eo) &&
              dalloc(blk, &blk->at_o, (size_t)kDecodeRows * blk->qd * eo) &&
              dalloc(blk, &blk->at_n2, (size_t)kDecodeRows * d * eo) &&
@@ -291,42 +340,53 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
     hipError_t e = hipStreamCreate(&s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(blk->rope, table.data(), table.size() * sizeof(float2), hipMemcpyHostToDevice, s);
-    const size_t eo_row = (size_t)d * eo;
-    // rotate_half layout: the rows of each q and k head are reordered so that
-    // the projection puts dimensions i and i + d_head/2 side by side, where the
-    // epilogue turns adjacent pairs; it stores them back in natural order
-    const int perm_dh = c.rope_layout == LB_ROPE_HALF ? dh : 0;
-    if (e == hipSuccess) e = lb::launch_convert_rows(dt, op, w->wq, blk->w_qkv, blk->qd, d, perm_dh, s);
-    if (e == hipSuccess)
-        e = lb::launch_convert_rows(dt, op, w->wk, (char*)blk->w_qkv + (size_t)blk->qd * eo_row, blk->kvd, d,
-                                    perm_dh, s);
-    if (e == hipSuccess)
-        e = lb::launch_convert(dt, op, w->wv, (char*)blk->w_qkv + (size_t)(blk->qd + blk->kvd) * eo_row,
-                               (size_t)blk->kvd * d, s);
-    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wo, blk->w_o, (size_t)d * blk->qd, s);
-    if (e == hipSuccess) e = lb::launch_pack_gate_up(dt, op, w->w_gate, w->w_up, blk->w_gu, dff, d, s);
-    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->w_down, blk->w_down, (size_t)d * dff, s);
     if (e == hipSuccess && dt == Elem::BF16) {
-        e = lb::launch_tile_weights(op, blk->w_qkv, blk->wt_qkv, blk->nqkv, d, s);
-        if (e == hipSuccess) e = lb::launch_tile_weights(op, blk->w_o, blk->wt_o, d, blk->qd, s);
-        if (e == hipSuccess) e = lb::launch_tile_weights(op, blk->w_gu, blk->wt_gu, 2 * dff, d, s);
-        if (e == hipSuccess) e = lb::launch_tile_weights(op, blk->w_down, blk->wt_down, d, dff, s);
         // rows past a decode batch are read by the GEMMs (their results are
         // dropped): start them at zero
-        if (e == hipSuccess) e = hipMemsetAsync(blk->at_n1, 0, (size_t)kDecodeRows * d * eo, s);
+        e = hipMemsetAsync(blk->at_n1, 0, (size_t)kDecodeRows * d * eo, s);
         if (e == hipSuccess) e = hipMemsetAsync(blk->at_o, 0, (size_t)kDecodeRows * blk->qd * eo, s);
         if (e == hipSuccess) e = hipMemsetAsync(blk->at_n2, 0, (size_t)kDecodeRows * d * eo, s);
         if (e == hipSuccess) e = hipMemsetAsync(blk->at_z, 0, (size_t)kDecodeRows * dff * eo, s);
     }
-    if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->attn_norm, blk->g1, (size_t)d, s);
-    if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->ffn_norm, blk->g2, (size_t)d, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (s) hipStreamDestroy(s);
     if (e != hipSuccess) {
         const char* msg = hipGetErrorString(e);
         free_all(blk);
         delete blk;
-        return fail(nullptr, LB_ERR_HIP, "weight packing failed: %s", msg);
+        return fail(nullptr, LB_ERR_HIP, "workspace set-up failed: %s", msg);
+    }
+    *out = blk;
+    return LB_OK;
+}
+
+// Allocate and pack n layers of weights into ls[0..n) (synchronous).
+static lb_status load_layers(lb_block* blk, const lb_weights* w, int n, LayerW* ls) {
+    for (int l = 0; l < n; ++l)
+        if (!alloc_layer(blk, &ls[l])) return fail(nullptr, LB_ERR_OOM, "device allocation failed (weights of block %d)", l);
+    hipStream_t s = nullptr;
+    hipError_t e = hipStreamCreate(&s);
+    for (int l = 0; l < n && e == hipSuccess; ++l) e = pack_layer(blk, &w[l], ls[l], s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (s) hipStreamDestroy(s);
+    if (e != hipSuccess) return fail(nullptr, LB_ERR_HIP, "weight packing failed: %s", hipGetErrorString(e));
+    return LB_OK;
+}
+
+extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w, lb_block** out) {
+    g_init_error.clear();
+    if (!out) return fail(nullptr, LB_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg || !w) return fail(nullptr, LB_ERR_INVALID_ARG, "cfg or weights is NULL");
+    if (!weights_complete(w)) return fail(nullptr, LB_ERR_INVALID_ARG, "a weight pointer is NULL");
+    lb_block* blk = nullptr;
+    lb_status st = create_core(cfg, &blk);
+    if (st != LB_OK) return st;
+    st = load_layers(blk, w, 1, &blk->lw);
+    if (st != LB_OK) {
+        free_all(blk);
+        delete blk;
+        return st;
     }
     *out = blk;
     return LB_OK;
@@ -351,8 +411,8 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 // sp: start position of every sequence (validated by the caller)
-static lb_status run_forward(lb_block* blk, const void* x, int B, int S, const lb::SeqPos& sp,
-                             const lb_kv_cache* kv, void* out, hipStream_t s) {
+static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int B, int S,
+                             const lb::SeqPos& sp, const lb_kv_cache* kv, void* out, hipStream_t s) {
     const lb_config& c = blk->cfg;
     const int M = B * S, d = c.d_model, dh = c.d_head, nkv = c.n_kv_heads, dff = c.d_ff;
     const int cap = kv->max_seq_len;
@@ -389,11 +449,13 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, const l
     void* z = dec ? blk->at_z : blk->z;
 
     mark(0);
-    e = lb::launch_rmsnorm(dt, op, x, blk->g1, n1, M, d, (float)c.norm_eps, mt, s);
+    e = lb::launch_rmsnorm(dt, op, x, L.g1, n1, M, d, (float)c.norm_eps, mt, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_1: %s", hipGetErrorString(e));
 
-    int max_start = sp.base, all_zero = sp.base == 0;
-    if (sp.ragged) {
+    // device-held positions: shape the launches for the largest start the
+    // kernels can read (they clamp to it)
+    int max_start = sp.dev ? sp.lim : sp.base, all_zero = !sp.dev && sp.base == 0;
+    if (!sp.dev && sp.ragged) {
         max_start = 0;
         all_zero = 1;
         for (int b = 0; b < B; ++b) {
@@ -419,8 +481,8 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, const l
     qe.qd = blk->qd;
     qe.rope_half = c.rope_layout == LB_ROPE_HALF;
     mark(1);
-    if (dec) e = lb::decode_qkv(op, dt, n1, blk->wt_qkv, M, blk->nqkv, d, qe, ws, s);
-    else e = lb::gemm_qkv(op, dt, n1, blk->w_qkv, M, blk->nqkv, d, qe, ws, s);
+    if (dec) e = lb::decode_qkv(op, dt, n1, L.wt_qkv, M, blk->nqkv, d, qe, ws, s);
+    else e = lb::gemm_qkv(op, dt, n1, L.w_qkv, M, blk->nqkv, d, qe, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "qkv projection: %s", hipGetErrorString(e));
 
     lb::AttnArgs a;
@@ -449,24 +511,90 @@ static lb_status run_forward(lb_block* blk, const void* x, int B, int S, const l
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "attention: %s", hipGetErrorString(e));
 
     mark(3);
-    if (dec) e = lb::decode_resid(op, dt, o, blk->wt_o, M, d, blk->qd, x, blk->h, ws, s);
-    else e = lb::gemm_resid(op, dt, o, blk->w_o, M, d, blk->qd, x, blk->h, ws, s);
+    if (dec) e = lb::decode_resid(op, dt, o, L.wt_o, M, d, blk->qd, x, blk->h, ws, s);
+    else e = lb::gemm_resid(op, dt, o, L.w_o, M, d, blk->qd, x, blk->h, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "o projection: %s", hipGetErrorString(e));
     mark(4);
-    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, blk->g2, n2, M, d, (float)c.norm_eps, mt, s);
+    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, L.g2, n2, M, d, (float)c.norm_eps, mt, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_2: %s", hipGetErrorString(e));
     mark(5);
-    if (dec) e = lb::decode_swiglu(op, n2, blk->wt_gu, M, 2 * dff, d, z, ws, s);
-    else e = lb::gemm_swiglu(op, n2, blk->w_gu, M, 2 * dff, d, z, ws, s);
+    if (dec) e = lb::decode_swiglu(op, n2, L.wt_gu, M, 2 * dff, d, z, ws, s);
+    else e = lb::gemm_swiglu(op, n2, L.w_gu, M, 2 * dff, d, z, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "gate/up projection: %s", hipGetErrorString(e));
     mark(6);
-    if (dec) e = lb::decode_out(op, dt, z, blk->wt_down, M, d, dff, blk->h, out, ws, s);
-    else e = lb::gemm_out(op, dt, z, blk->w_down, M, d, dff, blk->h, out, ws, s);
+    if (dec) e = lb::decode_out(op, dt, z, L.wt_down, M, d, dff, blk->h, out, ws, s);
+    else e = lb::gemm_out(op, dt, z, L.w_down, M, d, dff, blk->h, out, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "down projection: %s", hipGetErrorString(e));
     blk->last_mt = mt;
     blk->last_m = M;
     mark(7);
     return LB_OK;
+}
+
+// Checks every forward shares: pointers, sizes, the cache and overlap.
+static lb_status check_call(lb_block* blk, const void* x, int32_t batch, int32_t seq_len,
+                            const lb_kv_cache* kv, void* out) {
+    const lb_config& c = blk->cfg;
+    if (!x || !out || !kv || !kv->k || !kv->v)
+        return fail(blk, LB_ERR_INVALID_ARG, "x, out, kv, kv->k and kv->v must be non-NULL");
+    if (batch < 1 || seq_len < 1)
+        return fail(blk, LB_ERR_INVALID_ARG, "batch (%d) and seq_len (%d) must be >= 1", batch, seq_len);
+    if ((long)batch * seq_len > c.max_tokens)
+        return fail(blk, LB_ERR_INVALID_ARG, "batch*seq_len (%ld) exceeds max_tokens (%d)",
+                    (long)batch * seq_len, c.max_tokens);
+    if (batch > kv->batch)
+        return fail(blk, LB_ERR_INVALID_ARG, "batch (%d) exceeds the cache's batch (%d)", batch, kv->batch);
+    if (kv->max_seq_len < 1)
+        return fail(blk, LB_ERR_INVALID_ARG, "the cache's max_seq_len (%d) must be >= 1", kv->max_seq_len);
+    if (blk->dt == Elem::BF16 && kv->max_seq_len % 8 != 0)
+        return fail(blk, LB_ERR_UNSUPPORTED, "bf16 caches need max_seq_len % 8 == 0 (got %d)", kv->max_seq_len);
+    const size_t act = (size_t)batch * seq_len * c.d_model * esz(blk->dt);
+    if (overlap(x, act, out, act)) return fail(blk, LB_ERR_INVALID_ARG, "out overlaps x");
+    return LB_OK;
+}
+
+// Start positions of a call: host values (starts == nullptr: every sequence
+// at start_pos), each checked against cap (the smallest capacity of the
+// caches the call writes), or (dev != nullptr) a device array read by the
+// kernels, clamped there to the last start that fits.
+static lb_status make_positions(lb_block* blk, int32_t batch, int32_t seq_len, int32_t start_pos,
+                                const int32_t* starts, const int32_t* dev, int cap, lb::SeqPos* sp) {
+    const lb_config& c = blk->cfg;
+    sp->base = start_pos;
+    sp->ragged = starts != nullptr;
+    for (int b = 0; b < lb::kMaxRagged; ++b) sp->pos[b] = 0;
+    sp->dev = dev;
+    sp->lim = std::min(c.max_seq_len, cap) - seq_len;
+    if (dev) {
+        if (sp->lim < 0)
+            return fail(blk, LB_ERR_INVALID_ARG, "seq_len (%d) exceeds max_seq_len (config %d, cache %d)", seq_len,
+                        c.max_seq_len, cap);
+        return LB_OK;
+    }
+    if (starts && batch > lb::kMaxRagged)
+        return fail(blk, LB_ERR_INVALID_ARG, "a ragged forward takes at most %d sequences (got %d)",
+                    lb::kMaxRagged, batch);
+    for (int b = 0; b < (starts ? batch : 1); ++b) {
+        const int32_t p = starts ? starts[b] : start_pos;
+        if (p < 0) return fail(blk, LB_ERR_INVALID_ARG, "start_pos of sequence %d (%d) < 0", b, p);
+        if ((long)p + seq_len > c.max_seq_len || (long)p + seq_len > cap)
+            return fail(blk, LB_ERR_INVALID_ARG,
+                        "start_pos+seq_len of sequence %d (%ld) exceeds max_seq_len (config %d, cache %d)",
+                        b, (long)p + seq_len, c.max_seq_len, cap);
+        if (starts) sp->pos[b] = p;
+    }
+    return LB_OK;
+}
+
+// Runs fn() with blk's device current, restoring the caller's afterwards.
+template <typename F>
+static lb_status on_device(lb_block* blk, F fn) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(blk, LB_ERR_HIP, "hipGetDevice failed");
+    if (cur != blk->dev) hipSetDevice(blk->dev);
+    lb_status st = fn();
+    if (cur != blk->dev) hipSetDevice(cur);
+    return st;
 }
 
 // Validation and launch shared by the uniform and the ragged entry points;
@@ -476,43 +604,14 @@ static lb_status forward_checked(lb_block* blk, const void* x, int32_t batch, in
                                  void* out, void* stream) {
     if (!blk) return LB_ERR_INVALID_ARG;
     blk->err.clear();
-    const lb_config& c = blk->cfg;
-    if (!x || !out || !kv || !kv->k || !kv->v)
-        return fail(blk, LB_ERR_INVALID_ARG, "x, out, kv, kv->k and kv->v must be non-NULL");
-    if (batch < 1 || seq_len < 1)
-        return fail(blk, LB_ERR_INVALID_ARG, "batch (%d) and seq_len (%d) must be >= 1", batch, seq_len);
-    if ((long)batch * seq_len > c.max_tokens)
-        return fail(blk, LB_ERR_INVALID_ARG, "batch*seq_len (%ld) exceeds max_tokens (%d)",
-                    (long)batch * seq_len, c.max_tokens);
+    lb_status st = check_call(blk, x, batch, seq_len, kv, out);
+    if (st != LB_OK) return st;
     lb::SeqPos sp;
-    sp.base = start_pos;
-    sp.ragged = starts != nullptr;
-    for (int b = 0; b < lb::kMaxRagged; ++b) sp.pos[b] = 0;
-    if (starts && batch > lb::kMaxRagged)
-        return fail(blk, LB_ERR_INVALID_ARG, "a ragged forward takes at most %d sequences (got %d)",
-                    lb::kMaxRagged, batch);
-    for (int b = 0; b < (starts ? batch : 1); ++b) {
-        const int32_t p = starts ? starts[b] : start_pos;
-        if (p < 0) return fail(blk, LB_ERR_INVALID_ARG, "start_pos of sequence %d (%d) < 0", b, p);
-        if ((long)p + seq_len > c.max_seq_len || (long)p + seq_len > kv->max_seq_len)
-            return fail(blk, LB_ERR_INVALID_ARG,
-                        "start_pos+seq_len of sequence %d (%ld) exceeds max_seq_len (config %d, cache %d)",
-                        b, (long)p + seq_len, c.max_seq_len, kv->max_seq_len);
-        if (starts) sp.pos[b] = p;
-    }
-    if (batch > kv->batch)
-        return fail(blk, LB_ERR_INVALID_ARG, "batch (%d) exceeds the cache's batch (%d)", batch, kv->batch);
-    if (blk->dt == Elem::BF16 && kv->max_seq_len % 8 != 0)
-        return fail(blk, LB_ERR_UNSUPPORTED, "bf16 caches need max_seq_len % 8 == 0 (got %d)", kv->max_seq_len);
-    const size_t act = (size_t)batch * seq_len * c.d_model * esz(blk->dt);
-    if (overlap(x, act, out, act)) return fail(blk, LB_ERR_INVALID_ARG, "out overlaps x");
-
-    int cur = 0;
-    if (hipGetDevice(&cur) != hipSuccess) return fail(blk, LB_ERR_HIP, "hipGetDevice failed");
-    if (cur != blk->dev) hipSetDevice(blk->dev);
-    lb_status st = run_forward(blk, x, batch, seq_len, sp, kv, out, (hipStream_t)stream);
-    if (cur != blk->dev) hipSetDevice(cur);
-    return st;
+    st = make_positions(blk, batch, seq_len, start_pos, starts, nullptr, kv->max_seq_len, &sp);
+    if (st != LB_OK) return st;
+    return on_device(blk, [&] {
+        return run_forward(blk, blk->lw, x, batch, seq_len, sp, kv, out, (hipStream_t)stream);
+    });
 }
 
 extern "C" lb_status llama_block_forward(lb_block* blk, const void* x, int32_t batch, int32_t seq_len,
@@ -529,6 +628,227 @@ extern "C" lb_status llama_block_forward_ragged(lb_block* blk, const void* x, in
         return fail(blk, LB_ERR_INVALID_ARG, "start_pos must be non-NULL");
     }
     return forward_checked(blk, x, batch, seq_len, 0, start_pos, kv, out, stream);
+}
+
+// ---- stacks of blocks ------------------------------------------------------------
+// N blocks sharing one workspace and RoPE table, each with its own weights and
+// cache, then the final RMSNorm ("The Evolving Transformer 04 LLaMA", 07
+// ASSEMBLE LLAMA).  Block outputs pass between blocks in the config's dtype,
+// as the block's own interface hands them over.
+struct lb_stack {
+    lb_block* core = nullptr;  // config, workspace, RoPE table; owns every allocation
+    std::vector<LayerW> layers;
+    float* g_final = nullptr;
+    void* act[2] = {nullptr, nullptr};  // block outputs when the caller keeps none
+};
+
+struct lb_stack_graph {
+    lb_stack* st = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+extern "C" lb_status llama_stack_init(const lb_config* cfg, int32_t n_layers, const lb_weights* layers,
+                                      const void* final_norm, lb_stack** out) {
+    g_init_error.clear();
+    if (!out) return fail(nullptr, LB_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg || !layers || !final_norm) return fail(nullptr, LB_ERR_INVALID_ARG, "cfg, layers or final_norm is NULL");
+    if (n_layers < 1 || n_layers > LB_MAX_STACK_LAYERS)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "n_layers (%d) must be in [1, %d]", n_layers, LB_MAX_STACK_LAYERS);
+    for (int l = 0; l < n_layers; ++l)
+        if (!weights_complete(&layers[l]))
+            return fail(nullptr, LB_ERR_INVALID_ARG, "a weight pointer of block %d is NULL", l);
+    lb_block* blk = nullptr;
+    lb_status st = create_core(cfg, &blk);
+    if (st != LB_OK) return st;
+    lb_stack* sk = new lb_stack();
+    sk->core = blk;
+    sk->layers.resize((size_t)n_layers);
+    const size_t act = (size_t)blk->cfg.max_tokens * blk->cfg.d_model * esz(blk->dt);
+    bool ok = dalloc(blk, &sk->g_final, (size_t)blk->cfg.d_model * 4) && dalloc(blk, &sk->act[0], act) &&
+              dalloc(blk, &sk->act[1], act);
+    st = ok ? load_layers(blk, layers, n_layers, sk->layers.data())
+            : fail(nullptr, LB_ERR_OOM, "device allocation failed");
+    if (st == LB_OK) {
+        hipError_t e = lb::launch_convert(blk->dt, Elem::F32, final_norm, sk->g_final, (size_t)blk->cfg.d_model, nullptr);
+        if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) st = fail(nullptr, LB_ERR_HIP, "final norm gain: %s", hipGetErrorString(e));
+    }
+    if (st != LB_OK) {
+        free_all(blk);
+        delete blk;
+        delete sk;
+        return st;
+    }
+    *out = sk;
+    return LB_OK;
+}
+
+extern "C" void llama_stack_destroy(lb_stack* sk) {
+    if (!sk) return;
+    llama_block_destroy(sk->core);
+    delete sk;
+}
+
+extern "C" int32_t llama_stack_num_layers(const lb_stack* sk) { return sk ? (int32_t)sk->layers.size() : 0; }
+
+extern "C" const char* llama_stack_last_error(const lb_stack* sk) {
+    return llama_block_last_error(sk ? sk->core : nullptr);
+}
+
+// Checks of a stack call; *cap receives the smallest capacity of the caches.
+static lb_status check_stack_call(lb_stack* sk, const void* x, int32_t batch, int32_t seq_len,
+                                  const lb_kv_cache* kv, void* out, void* hidden, int* cap) {
+    lb_block* blk = sk->core;
+    if (!kv) return fail(blk, LB_ERR_INVALID_ARG, "kv must be non-NULL");
+    const int L = (int)sk->layers.size();
+    *cap = INT32_MAX;
+    for (int l = 0; l < L; ++l) {
+        lb_status st = check_call(blk, x, batch, seq_len, &kv[l], out);
+        if (st != LB_OK) return st;
+        *cap = std::min(*cap, kv[l].max_seq_len);
+    }
+    const size_t act = (size_t)batch * seq_len * blk->cfg.d_model * esz(blk->dt);
+    if (hidden && (overlap(hidden, act * L, x, act) || overlap(hidden, act * L, out, act)))
+        return fail(blk, LB_ERR_INVALID_ARG, "hidden overlaps x or out");
+    return LB_OK;
+}
+
+// Enqueue every block and the final norm (arguments validated).
+static lb_status stack_run(lb_stack* sk, const void* x, int B, int S, const lb::SeqPos& sp,
+                           const lb_kv_cache* kv, void* out, void* hidden, hipStream_t s) {
+    lb_block* blk = sk->core;
+    const lb_config& c = blk->cfg;
+    const size_t act = (size_t)B * S * c.d_model * esz(blk->dt);
+    const void* in = x;
+    for (size_t l = 0; l < sk->layers.size(); ++l) {
+        void* o = hidden ? (char*)hidden + l * act : sk->act[l & 1];
+        lb_status st = run_forward(blk, sk->layers[l], in, B, S, sp, &kv[l], o, s);
+        if (st != LB_OK) return st;
+        in = o;
+    }
+    hipError_t e = lb::launch_rmsnorm(blk->dt, blk->dt, in, sk->g_final, out, B * S, c.d_model,
+                                      (float)c.norm_eps, 0, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "final norm: %s", hipGetErrorString(e));
+    return LB_OK;
+}
+
+extern "C" lb_status llama_stack_forward(lb_stack* sk, const void* x, int32_t batch, int32_t seq_len,
+                                         int32_t start_pos, const int32_t* starts, const lb_kv_cache* kv,
+                                         void* out, void* hidden, void* stream) {
+    if (!sk) return LB_ERR_INVALID_ARG;
+    lb_block* blk = sk->core;
+    blk->err.clear();
+    int cap = 0;
+    lb_status st = check_stack_call(sk, x, batch, seq_len, kv, out, hidden, &cap);
+    if (st != LB_OK) return st;
+    lb::SeqPos sp;
+    st = make_positions(blk, batch, seq_len, start_pos, starts, nullptr, cap, &sp);
+    if (st != LB_OK) return st;
+    return on_device(blk, [&] { return stack_run(sk, x, batch, seq_len, sp, kv, out, hidden, (hipStream_t)stream); });
+}
+
+static lb_status stack_device_pos(lb_stack* sk, const void* x, int32_t batch, int32_t seq_len, int32_t* positions,
+                                  int32_t advance, const lb_kv_cache* kv, void* out, void* hidden, hipStream_t s) {
+    lb_block* blk = sk->core;
+    if (!positions) return fail(blk, LB_ERR_INVALID_ARG, "positions must be non-NULL");
+    int cap = 0;
+    lb_status st = check_stack_call(sk, x, batch, seq_len, kv, out, hidden, &cap);
+    if (st != LB_OK) return st;
+    lb::SeqPos sp;
+    st = make_positions(blk, batch, seq_len, 0, nullptr, positions, cap, &sp);
+    if (st != LB_OK) return st;
+    st = stack_run(sk, x, batch, seq_len, sp, kv, out, hidden, s);
+    if (st != LB_OK || !advance) return st;
+    hipError_t e = lb::launch_advance_positions(positions, batch, seq_len, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "advance positions: %s", hipGetErrorString(e));
+    return LB_OK;
+}
+
+extern "C" lb_status llama_stack_forward_device_pos(lb_stack* sk, const void* x, int32_t batch, int32_t seq_len,
+                                                    int32_t* positions, int32_t advance, const lb_kv_cache* kv,
+                                                    void* out, void* hidden, void* stream) {
+    if (!sk) return LB_ERR_INVALID_ARG;
+    sk->core->err.clear();
+    return on_device(sk->core, [&] {
+        return stack_device_pos(sk, x, batch, seq_len, positions, advance, kv, out, hidden, (hipStream_t)stream);
+    });
+}
+
+extern "C" lb_status llama_stack_graph_create(lb_stack* sk, const void* x, int32_t batch, int32_t seq_len,
+                                              int32_t* positions, const lb_kv_cache* kv, void* out,
+                                              lb_stack_graph** g) {
+    if (!sk) return LB_ERR_INVALID_ARG;
+    lb_block* blk = sk->core;
+    blk->err.clear();
+    if (!g) return fail(blk, LB_ERR_INVALID_ARG, "g is NULL");
+    *g = nullptr;
+    if (blk->profiling) return fail(blk, LB_ERR_INVALID_ARG, "stage profiling is on");
+    // the same checks the capture would run, before anything is captured
+    int cap = 0;
+    lb_status st = check_stack_call(sk, x, batch, seq_len, kv, out, nullptr, &cap);
+    if (st != LB_OK) return st;
+    if (!positions) return fail(blk, LB_ERR_INVALID_ARG, "positions must be non-NULL");
+    lb::SeqPos probe;
+    st = make_positions(blk, batch, seq_len, 0, nullptr, positions, cap, &probe);
+    if (st != LB_OK) return st;
+    return on_device(blk, [&]() -> lb_status {
+        hipStream_t s = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess)
+            return fail(blk, LB_ERR_HIP, "hipStreamCreate failed");
+        hipGraph_t graph = nullptr;
+        hipError_t e = hipStreamBeginCapture(s, hipStreamCaptureModeRelaxed);
+        lb_status rs = LB_OK;
+        if (e == hipSuccess) {
+            rs = stack_device_pos(sk, x, batch, seq_len, positions, 1, kv, out, nullptr, s);
+            e = hipStreamEndCapture(s, &graph);  // ends the capture whatever happened in it
+        }
+        hipStreamDestroy(s);
+        if (rs != LB_OK) {
+            if (graph) hipGraphDestroy(graph);
+            return rs;
+        }
+        if (e != hipSuccess) {
+            if (graph) hipGraphDestroy(graph);
+            return fail(blk, LB_ERR_HIP, "graph capture: %s", hipGetErrorString(e));
+        }
+        hipGraphExec_t exec = nullptr;
+        e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+        if (e != hipSuccess) {
+            hipGraphDestroy(graph);
+            return fail(blk, LB_ERR_HIP, "graph instantiate: %s", hipGetErrorString(e));
+        }
+        lb_stack_graph* sg = new lb_stack_graph();
+        sg->st = sk;
+        sg->graph = graph;
+        sg->exec = exec;
+        *g = sg;
+        return LB_OK;
+    });
+}
+
+extern "C" lb_status llama_stack_graph_launch(lb_stack_graph* g, void* stream) {
+    if (!g) return LB_ERR_INVALID_ARG;
+    lb_block* blk = g->st->core;
+    blk->err.clear();
+    return on_device(blk, [&]() -> lb_status {
+        hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "graph launch: %s", hipGetErrorString(e));
+        return LB_OK;
+    });
+}
+
+extern "C" void llama_stack_graph_destroy(lb_stack_graph* g) {
+    if (!g) return;
+    int cur = 0;
+    hipGetDevice(&cur);
+    hipSetDevice(g->st->core->dev);
+    hipDeviceSynchronize();
+    if (g->exec) hipGraphExecDestroy(g->exec);
+    if (g->graph) hipGraphDestroy(g->graph);
+    hipSetDevice(cur);
+    delete g;
 }
 
 static bool stage_buffer(const lb_block* blk, lb_stage which, const void** ptr, Elem* elem, int64_t* cols) {

@@ -163,6 +163,80 @@ lb_status llama_block_forward_ragged(lb_block* blk, const void* x, int32_t batch
 /* Free the handle and everything it owns (synchronises the device first). */
 void llama_block_destroy(lb_block* blk);
 
+/* ---- Stacks of blocks ------------------------------------------------------
+ * n_layers blocks of one config, each with its own weights and its own KV
+ * cache, followed by the final RMSNorm ("The Evolving Transformer 04 LLaMA",
+ * 07 ASSEMBLE LLAMA: token embedding, N blocks, final norm, output projection;
+ * "Full Llama 3 transformer block", Overview: the block is the unit stacked L
+ * times).  Block 0 maps x, block l maps block l-1's output, and
+ *     y = RMSNorm(output of the last block) * final_norm   (eps = cfg.norm_eps).
+ * The embedding and the output projection are not part of the stack.  Block
+ * outputs pass from block to block in cfg.dtype.  The blocks share one
+ * workspace, so one call per stack may be in flight. */
+#define LB_MAX_STACK_LAYERS 1024
+typedef struct lb_stack lb_stack;
+typedef struct lb_stack_graph lb_stack_graph;
+
+/* Create a stack on the current device: layers[0..n_layers) are the blocks'
+ * weights (device pointers as for llama_block_init), final_norm [d_model]
+ * the final gain in cfg.dtype.  Everything is copied; the caller may free its
+ * tensors when the call returns.  Checks as llama_block_init, plus 1 <=
+ * n_layers <= LB_MAX_STACK_LAYERS (LB_ERR_INVALID_ARG).  Synchronous. */
+lb_status llama_stack_init(const lb_config* cfg, int32_t n_layers, const lb_weights* layers,
+                           const void* final_norm, lb_stack** out);
+
+/* One forward of the whole stack, enqueued on `stream`.
+ *   x, out   [batch][seq_len][d_model] device, cfg.dtype; out must not overlap x
+ *   kv       HOST array of n_layers caches (block l reads and writes kv[l],
+ *            laid out as for llama_block_forward)
+ *   hidden   optional device buffer [n_layers][batch][seq_len][d_model] in
+ *            cfg.dtype that receives every block's output (NULL: kept in the
+ *            workspace); must not overlap x or out
+ *   starts   NULL: every sequence at start_pos; else a HOST array of batch
+ *            start positions (batch <= LB_MAX_RAGGED_BATCH), as in
+ *            llama_block_forward_ragged.
+ * Checks as llama_block_forward against every cache. */
+lb_status llama_stack_forward(lb_stack* st, const void* x, int32_t batch, int32_t seq_len,
+                              int32_t start_pos, const int32_t* starts, const lb_kv_cache* kv,
+                              void* out, void* hidden, void* stream);
+
+/* llama_stack_forward with the start positions in DEVICE memory: positions
+ * [batch] int32, read by the kernels when they run, so a captured graph of
+ * this call can be replayed while the positions move.  Each value is clamped
+ * to [0, min(cfg.max_seq_len, smallest cache max_seq_len) - seq_len] when it
+ * is read: a position past the end rewrites the last rows of the cache instead
+ * of leaving it, so callers stop before the capacity.  With advance != 0 a
+ * last kernel adds seq_len to every position, after every read of them.
+ * Launches are shaped for the largest start the clamp allows, which costs
+ * decode launches with few (sequence, KV head) pairs some idle blocks. */
+lb_status llama_stack_forward_device_pos(lb_stack* st, const void* x, int32_t batch,
+                                         int32_t seq_len, int32_t* positions, int32_t advance,
+                                         const lb_kv_cache* kv, void* out, void* hidden,
+                                         void* stream);
+
+/* Capture llama_stack_forward_device_pos(st, x, batch, seq_len, positions,
+ * advance = 1, kv, out, hidden = NULL) into a HIP graph: each launch runs one
+ * step of the stack at the current device positions and moves them on by
+ * seq_len, with no host work but the launch.  x, out, positions and the
+ * caches are bound at capture; the caller rewrites x (and, if it wishes,
+ * positions) between launches.  Arguments are checked as for the eager call
+ * before anything is captured.  Synchronous; the stack must outlive the
+ * graph, and graph launches count as calls on the stack. */
+lb_status llama_stack_graph_create(lb_stack* st, const void* x, int32_t batch, int32_t seq_len,
+                                   int32_t* positions, const lb_kv_cache* kv, void* out,
+                                   lb_stack_graph** g);
+/* Enqueue one replay of the graph on `stream`. */
+lb_status llama_stack_graph_launch(lb_stack_graph* g, void* stream);
+/* Free the graph (synchronises the device first). */
+void llama_stack_graph_destroy(lb_stack_graph* g);
+
+/* Free the stack and everything it owns (synchronises the device first). */
+void llama_stack_destroy(lb_stack* st);
+int32_t llama_stack_num_layers(const lb_stack* st);
+/* Last error text of the stack ("" if none); NULL: that of the last failed
+ * llama_stack_init or llama_block_init on this thread. */
+const char* llama_stack_last_error(const lb_stack* st);
+
 /* Static text for a status code. */
 const char* llama_block_status_string(lb_status s);
 

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "llama_block.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(llama_block_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(llama_(?:block|stack)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -103,3 +103,36 @@ def test_init_rejects_null_pointers():
 def test_status_strings():
     for s in range(5):
         assert lbmod.llama_block_status_string(s)
+
+
+def test_stack_init_rejects_bad_arguments_before_any_device_call():
+    L = lbmod.lib()
+    cfg = lbmod.make_config(64, 4, 2, 16, 176, 16, 16, 1e4, 1e-5, "f32")
+    arr = (lbmod.LbWeights * 3)(_fake_weights(), _fake_weights(), _fake_weights())
+    h = ctypes.c_void_p()
+    gain = ctypes.c_void_p(0x9000)
+    for n in (0, -1, lbmod.MAX_STACK_LAYERS + 1):
+        assert L.llama_stack_init(ctypes.byref(cfg), n, arr, gain, ctypes.byref(h)) == lbmod.LB_ERR_INVALID_ARG
+        assert h.value is None
+        assert "n_layers" in lbmod.llama_stack_last_error(None)
+    assert L.llama_stack_init(ctypes.byref(cfg), 3, arr, None, ctypes.byref(h)) == lbmod.LB_ERR_INVALID_ARG
+    arr[2].w_up = None
+    assert L.llama_stack_init(ctypes.byref(cfg), 3, arr, gain, ctypes.byref(h)) == lbmod.LB_ERR_INVALID_ARG
+    assert "block 2" in lbmod.llama_stack_last_error(None)
+    bad = lbmod.make_config(65, 4, 2, 16, 176, 16, 16, 1e4, 1e-5, "f32")
+    assert L.llama_stack_init(ctypes.byref(bad), 2, arr, gain, ctypes.byref(h)) == lbmod.LB_ERR_INVALID_ARG
+    assert h.value is None
+
+
+def test_stack_calls_reject_null_handles():
+    L = lbmod.lib()
+    assert L.llama_stack_forward(None, None, 1, 1, 0, None, None, None, None, None) == lbmod.LB_ERR_INVALID_ARG
+    assert L.llama_stack_forward_device_pos(None, None, 1, 1, None, 1, None, None, None, None) == \
+        lbmod.LB_ERR_INVALID_ARG
+    g = ctypes.c_void_p()
+    assert L.llama_stack_graph_create(None, None, 1, 1, None, None, None, ctypes.byref(g)) == \
+        lbmod.LB_ERR_INVALID_ARG
+    assert L.llama_stack_graph_launch(None, None) == lbmod.LB_ERR_INVALID_ARG
+    assert L.llama_stack_num_layers(None) == 0
+    L.llama_stack_destroy(None)
+    L.llama_stack_graph_destroy(None)
