@@ -147,6 +147,57 @@ def run_gpu(w, steps, warmup, positions=None):
     return ms, avg_all, dom, avg_dom[dom], ms_plain, ms_all, per_call
 
 
+def run_stack(w, n_layers, steps, warmup):
+    """Model-level decode: one step of a stack of n_layers blocks (each with
+    its own weights and cache) and the final RMSNorm, eagerly (host
+    positions) and as a replay of the captured step (device positions).
+    Returns (eager ms/step, graph ms/step)."""
+    import torch
+
+    import decoder_only_transformer_amd as lbmod
+    import workloads
+
+    cap = (w.capacity + 7) // 8 * 8
+    cfg = lbmod.make_config(w.d, w.H, w.n_kv, w.d_head, w.d_ff, w.M, cap, w.theta, w.eps, w.dtype)
+    t = workloads.generate_stack_on_device(w, n_layers)
+    stack = lbmod.LlamaStack(cfg, [{n: lt[n] for n in lbmod.WEIGHT_NAMES} for lt in t["layers"]],
+                             t["final_norm"])
+    kv = []
+    for lt in t["layers"]:
+        k, v = lbmod.new_kv_cache(w.B, w.n_kv, cap, w.d_head, w.torch_dtype, fill=None)
+        if w.start_pos > 0:
+            k[:, :, :w.start_pos] = lt.pop("k_prefix")
+            v[:, :, :w.start_pos] = lt.pop("v_prefix")
+        kv.append((k, v))
+    x = t["x"]
+    out = torch.empty_like(x)
+    del t
+    torch.cuda.empty_cache()
+
+    def clock(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    eager = lambda: stack.forward(x, w.start_pos, kv, out)
+    clock(eager, warmup)
+    ms_eager = clock(eager, steps)
+    # the captured step reads its positions from the device; at the end of the
+    # cache they stay clamped to the last start, so every replay does the work
+    # of the eager step at w.start_pos
+    positions = torch.full((w.B,), w.start_pos, dtype=torch.int32, device="cuda")
+    graph = stack.capture(x, positions, kv, out)
+    clock(graph.launch, warmup)
+    ms_graph = clock(graph.launch, steps)
+    stack.close()
+    del kv, x, out, positions
+    torch.cuda.empty_cache()
+    return ms_eager, ms_graph
+
+
 def roofline(w, avg_ms, dom, dom_ms, bound, positions=None):
     """Per-stage figures from the all-stage pass; the roofline entry from the
     dominant stage's own timed region."""
@@ -252,6 +303,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the model-level stack decode")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -343,6 +395,24 @@ def main():
             "roofline": rroof, "stages": rstages,
         }
         log(f"[bench] ragged decode {rms * 1e3:.1f} us/step")
+
+    if not args.no_stack:
+        # model-level decode: every block of the model, then the final norm
+        # (no embedding, no output projection)
+        result["stack_decode"] = []
+        for name, n_layers in (("llama3_8b_decode", 32), ("smollm2_135m_decode", 30),
+                               ("smollm2_135m_decode_b1", 30)):
+            ws = workloads.get(name)
+            log(f"[bench] stack decode {name} x {n_layers} blocks")
+            se, sg = run_stack(ws, n_layers, args.steps, args.warmup)
+            sbytes = n_layers * sum(v["bytes"] for v in stage_work(ws).values())
+            result["stack_decode"].append({
+                "workload": name, "blocks": n_layers, "B": ws.B, "start_pos": ws.start_pos,
+                "eager_ms_per_step": round(se, 4), "graph_ms_per_step": round(sg, 4),
+                "tokens_per_s": round(ws.B / (min(se, sg) * 1e-3), 1),
+                "gbs": round(sbytes / (min(se, sg) * 1e-3) / 1e9, 1),
+                "hbm_frac": round(sbytes / (min(se, sg) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+            log(f"[bench] stack decode {name}: eager {se:.3f} ms, graph {sg:.3f} ms")
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")

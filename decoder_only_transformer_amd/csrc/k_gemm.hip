@@ -44,6 +44,8 @@ static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const 
 // across blocks when there are fewer than 192 column tiles.
 int decode_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
+constexpr size_t kSplitMinBytes = size_t(4) << 20;
+
 template <typename T, int MT, class Epi>
 static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, const Epi& epi,
                                 const SplitWs& ws, hipStream_t s) {
@@ -71,7 +73,10 @@ static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, c
         return hipGetLastError();
     }
     int ks = 1;
-    if (tiles < 192) {
+    // narrow outputs: split K so that about 256 blocks stream the weights,
+    // unless the whole matrix is small enough (a few MB, the small-model
+    // widths) that the reduction's extra launch costs more than the split saves
+    if (tiles < 192 && (size_t)N * K * sizeof(T) >= kSplitMinBytes) {
         ks = (256 + tiles - 1) / tiles;
         if (ks > kSkinnyMaxSplit) ks = kSkinnyMaxSplit;
         if (ks > nks / 4) ks = nks / 4;  // at least one k-step per wavefront

@@ -144,6 +144,18 @@ def test_decode_llama3_width_batches(B):
     run.close()
 
 
+def test_decode_split_k_narrow_outputs():
+    """Decode at d 2048: the o and down products have fewer than 192 column
+    tiles and weights of several MB, so their K is split over several blocks
+    and a second kernel reduces the partials (at the 512 width of the other
+    decode tests the matrices are small enough to run unsplit)."""
+    w = workloads.BlockWorkload("decode_split", "bf16", B=5, S=1, start_pos=200, d=2048, H=16,
+                                n_kv=4, d_head=128, d_ff=5632, theta=5e5, eps=1e-5, w_std=0.02,
+                                g_mean=1.0, g_std=0.05, max_seq=256, seed=13)
+    run, *_ = _check_block(w)
+    run.close()
+
+
 def test_decode_stages_llama3_width():
     """Stage parity after a decode forward, whose activations live in the
     k-step tiled layout inside the library (copied out row-major).  Bar 2e-2

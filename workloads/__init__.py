@@ -34,8 +34,8 @@ from typing import Dict, Optional
 
 import torch
 
-__all__ = ["BlockWorkload", "WORKLOADS", "get", "generate", "generate_stack", "param_count",
-           "stack_layer_seed", "with_overrides"]
+__all__ = ["BlockWorkload", "WORKLOADS", "get", "generate", "generate_stack",
+           "generate_stack_on_device", "param_count", "stack_layer_seed", "with_overrides"]
 
 
 @dataclass(frozen=True)
@@ -94,6 +94,14 @@ WORKLOADS: Dict[str, BlockWorkload] = {
                                       d=4096, H=32, n_kv=8, d_head=128, d_ff=14336, theta=5e5,
                                       eps=1e-5, w_std=0.02, g_mean=1.0, g_std=0.05,
                                       cache_std=1.0, max_seq=8192),
+    # SmolLM2-135M decode at the end of a 1,024-token text (the length the
+    # page measures the model on), 32 sequences and a single one
+    "smollm2_135m_decode": BlockWorkload("smollm2_135m_decode", "bf16", B=32, S=1, start_pos=1023,
+                                         d=576, H=9, n_kv=3, d_head=64, d_ff=1536, theta=1e5,
+                                         eps=1e-5, w_std=0.02, max_seq=1024),
+    "smollm2_135m_decode_b1": BlockWorkload("smollm2_135m_decode_b1", "bf16", B=1, S=1, start_pos=1023,
+                                            d=576, H=9, n_kv=3, d_head=64, d_ff=1536, theta=1e5,
+                                            eps=1e-5, w_std=0.02, max_seq=1024),
     "llama3_70b_prefill": BlockWorkload("llama3_70b_prefill", "bf16", B=1, S=4096, start_pos=0,
                                         d=8192, H=64, n_kv=8, d_head=128, d_ff=28672, theta=5e5,
                                         eps=1e-5, w_std=0.01),
@@ -188,5 +196,51 @@ def generate_stack(w: BlockWorkload, n_layers: int, with_cache: bool = True) -> 
     for l in range(n_layers):
         t = generate(with_overrides(w, seed=stack_layer_seed(w.seed, l)), with_cache=with_cache)
         del t["x"]
+        layers.append(t)
+    return {"x": x, "final_norm": final, "layers": layers}
+
+
+def generate_stack_on_device(w: BlockWorkload, n_layers: int, device="cuda") -> Dict:
+    """A stack of the workload's shape drawn on the device with torch's device
+    generator (for model-sized stacks, whose weights would take minutes to draw
+    on the host).  Same distributions as generate_stack, other random streams:
+    one generator seeded stack_layer_seed(w.seed, l) per block, drawing that
+    block's tensors in the order of generate(); x and final_norm from a
+    generator seeded w.seed.  Pre-filled cache rows (start_pos > 0) are drawn
+    into the returned per-block "k_prefix" / "v_prefix" as in generate()."""
+    def draw(gen, shape, mean, std):
+        t = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+        if std != 1.0:
+            t.mul_(std)
+        if mean != 0.0:
+            t.add_(mean)
+        return t.to(w.torch_dtype)
+
+    def gain(gen):
+        if w.g_std is None:
+            return torch.full((w.d,), w.g_mean, dtype=torch.float32, device=device).to(w.torch_dtype)
+        return draw(gen, (w.d,), w.g_mean, w.g_std)
+
+    g0 = torch.Generator(device=device)
+    g0.manual_seed(w.seed)
+    x = draw(g0, (w.B, w.S, w.d), 0.0, w.x_std)
+    final = gain(g0)
+    layers = []
+    for l in range(n_layers):
+        gen = torch.Generator(device=device)
+        gen.manual_seed(stack_layer_seed(w.seed, l))
+        t = {"attn_norm": gain(gen),
+             "wq": draw(gen, (w.H * w.d_head, w.d), 0.0, w.w_std),
+             "wk": draw(gen, (w.n_kv * w.d_head, w.d), 0.0, w.w_std),
+             "wv": draw(gen, (w.n_kv * w.d_head, w.d), 0.0, w.w_std),
+             "wo": draw(gen, (w.d, w.H * w.d_head), 0.0, w.w_std),
+             "ffn_norm": gain(gen),
+             "w_gate": draw(gen, (w.d_ff, w.d), 0.0, w.w_std),
+             "w_up": draw(gen, (w.d_ff, w.d), 0.0, w.w_std),
+             "w_down": draw(gen, (w.d, w.d_ff), 0.0, w.w_std)}
+        if w.start_pos > 0:
+            shape = (w.B, w.n_kv, w.start_pos, w.d_head)
+            t["k_prefix"] = draw(gen, shape, 0.0, w.cache_std)
+            t["v_prefix"] = draw(gen, shape, 0.0, w.cache_std)
         layers.append(t)
     return {"x": x, "final_norm": final, "layers": layers}
