@@ -49,6 +49,17 @@ class _Weights(ctypes.Structure):
 STAGES = ("n1", "q", "k", "v", "o", "h", "n2", "z")
 
 
+class _MoeCfg(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int), ("top_k", ctypes.c_int), ("d_ff_expert", ctypes.c_int)]
+
+
+class _MoeWeights(ctypes.Structure):
+    _fields_ = [("router", _dp), ("w_gate", _dp), ("w_up", _dp), ("w_down", _dp)]
+
+
+MOE_WEIGHT_NAMES = ("router", "e_gate", "e_up", "e_down")
+
+
 class _Stages(ctypes.Structure):
     _fields_ = [(n, _dp) for n in STAGES]
 
@@ -81,6 +92,19 @@ def lib():
                                         ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp,
                                         ctypes.POINTER(_Weights), _dp, _pp, _pp, _dp, _dp]
         L.orc_stack_forward.restype = ctypes.c_int
+        _ip = ctypes.POINTER(ctypes.c_int)
+        L.orc_moe_route.argtypes = [ctypes.POINTER(_MoeCfg), ctypes.c_int, _dp, _dp, _ip, ctypes.c_int,
+                                    _dp, _dp]
+        L.orc_moe_route.restype = ctypes.c_int
+        L.orc_moe_ffn.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_MoeCfg), _dp,
+                                  ctypes.POINTER(_Weights), ctypes.POINTER(_MoeWeights), _ip,
+                                  ctypes.c_int, _dp, _dp, _dp]
+        L.orc_moe_ffn.restype = ctypes.c_int
+        L.orc_moe_block_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_MoeCfg), ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp,
+                                            ctypes.POINTER(_Weights), ctypes.POINTER(_MoeWeights), _dp,
+                                            _dp, _dp, _ip, ctypes.c_int, _ip, ctypes.c_int, _dp, _dp]
+        L.orc_moe_block_forward.restype = ctypes.c_int
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
@@ -225,6 +249,80 @@ def stack_forward(cfg: Dict, x, layers: Sequence[Dict], final_norm, start_pos: i
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return y, hid
+
+
+def _moe_struct(moe: Dict) -> "_MoeCfg":
+    return _MoeCfg(int(moe["n_experts"]), int(moe["top_k"]), int(moe["d_ff_expert"]))
+
+
+def moe_route(moe: Dict, n, router, force_sel=None):
+    """Routing of one normalised row: returns (sel, wts, logits)."""
+    n, r = _f64(n), _f64(router)
+    E, K = int(moe["n_experts"]), int(moe["top_k"])
+    sel = np.zeros(K, dtype=np.int32) if force_sel is None else np.array(force_sel, dtype=np.int32)
+    wts = np.zeros(K)
+    logits = np.zeros(E)
+    rc = lib().orc_moe_route(ctypes.byref(_moe_struct(moe)), n.shape[-1], _p(n), _p(r),
+                             sel.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), 0 if force_sel is None else 1,
+                             _p(wts), _p(logits))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return sel, wts, logits
+
+
+def moe_ffn(cfg: Dict, moe: Dict, n, weights: Dict, force_sel=None):
+    """MoE FFN of one normalised row n [d] (shared expert = weights' w_gate /
+    w_up / w_down).  Returns (out, sel, wts, logits)."""
+    n = _f64(n)
+    ws = {k: _f64(weights[k]) for k in ("w_gate", "w_up", "w_down") + MOE_WEIGHT_NAMES}
+    wstruct = _Weights(*[(_p(ws[k]) if k in ws else None) for k in WEIGHT_NAMES])
+    mstruct = _MoeWeights(*[_p(ws[k]) for k in MOE_WEIGHT_NAMES])
+    E, K = int(moe["n_experts"]), int(moe["top_k"])
+    sel = np.zeros(K, dtype=np.int32) if force_sel is None else np.array(force_sel, dtype=np.int32)
+    wts, logits, out = np.zeros(K), np.zeros(E), np.zeros(cfg["d"])
+    rc = lib().orc_moe_ffn(ctypes.byref(_cfg_struct(cfg)), ctypes.byref(_moe_struct(moe)), _p(n),
+                           ctypes.byref(wstruct), ctypes.byref(mstruct),
+                           sel.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), 0 if force_sel is None else 1,
+                           _p(wts), _p(logits), _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out, sel, wts, logits
+
+
+def moe_block_forward(cfg: Dict, moe: Dict, x, weights: Dict, start_pos: int, k_cache: np.ndarray,
+                      v_cache: np.ndarray, rows: Optional[Sequence[int]] = None, force_sel=None):
+    """The block with the MoE FFN.  weights: the block's (its FFN is the
+    shared expert) plus router / e_gate / e_up / e_down.  force_sel: optional
+    [B*S][k] experts to use per row.  Returns (y, sel, wts, logits), per flat
+    row; with `rows`, only those rows are meaningful."""
+    x = _f64(x)
+    B, S, d = x.shape
+    cap = k_cache.shape[2]
+    ws = {n: _f64(weights[n]) for n in WEIGHT_NAMES + MOE_WEIGHT_NAMES}
+    wstruct = _Weights(*[_p(ws[n]) for n in WEIGHT_NAMES])
+    mstruct = _MoeWeights(*[_p(ws[n]) for n in MOE_WEIGHT_NAMES])
+    E, K = int(moe["n_experts"]), int(moe["top_k"])
+    M = B * S
+    if force_sel is None:
+        sel = np.zeros((M, K), dtype=np.int32)
+    else:
+        sel = np.ascontiguousarray(np.asarray(force_sel, dtype=np.int32).reshape(M, K))
+    wts = np.zeros((M, K))
+    logits = np.zeros((M, E))
+    y = np.zeros((B, S, d))
+    if rows is not None:
+        rarr = (ctypes.c_int * len(rows))(*[int(r) for r in rows])
+        nrows = len(rows)
+    else:
+        rarr, nrows = None, 0
+    rc = lib().orc_moe_block_forward(ctypes.byref(_cfg_struct(cfg)), ctypes.byref(_moe_struct(moe)), B, S,
+                                     int(start_pos), int(cap), _p(x), ctypes.byref(wstruct),
+                                     ctypes.byref(mstruct), _p(k_cache), _p(v_cache), _p(y), rarr, nrows,
+                                     sel.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+                                     0 if force_sel is None else 1, _p(wts), _p(logits))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return y, sel, wts, logits
 
 
 def cfg_of(w) -> Dict:

@@ -157,6 +157,85 @@ void orc_attend(const double* q, const double* k_rows, const double* v_rows, lon
     }
 }
 
+/* One SwiGLU feed-forward of width f on n [L4 The idea; LL 04 SWIGLU]:
+ * out = down(SiLU(gate n) * up n), gate/up [f][d], down [d][f]. */
+static void swiglu(const double* n, const double* gate, const double* up, const double* down, int d,
+                   int f, double* out)
+{
+    double* a = (double*)malloc(sizeof(double) * (size_t)f * 2);
+    double* u = a + f;
+    orc_linear(n, gate, f, d, a);
+    orc_linear(n, up, f, d, u);
+    for (int j = 0; j < f; ++j) a[j] = orc_silu(a[j]) * u[j];
+    orc_linear(a, down, d, f, out);
+    free(a);
+}
+
+int orc_moe_route(const orc_moe_cfg* m, int d, const double* n, const double* router, int* sel,
+                  int force, double* wts, double* logits)
+{
+    const int E = m->n_experts, K = m->top_k;
+    if (E < 1 || K < 1 || K > E) return -10;
+    /* the router: a bias-free linear layer scoring every expert [L4 The idea] */
+    orc_linear(n, router, E, d, logits);
+    if (force) {
+        for (int j = 0; j < K; ++j) {
+            if (sel[j] < 0 || sel[j] >= E) return -11;
+            for (int i = 0; i < j; ++i)
+                if (sel[i] == sel[j]) return -11;
+        }
+    } else {
+        /* the top-k: repeatedly the largest logit not yet taken, the lower
+         * index first among equal logits */
+        for (int j = 0; j < K; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int i = 0; i < j; ++i) taken |= sel[i] == e;
+                if (!taken && (best < 0 || logits[e] > logits[best])) best = e;
+            }
+            sel[j] = best;
+        }
+    }
+    /* weights: softmax over the chosen experts' logits */
+    double mx = logits[sel[0]];
+    for (int j = 1; j < K; ++j) mx = logits[sel[j]] > mx ? logits[sel[j]] : mx;
+    double sum = 0.0;
+    for (int j = 0; j < K; ++j) {
+        wts[j] = exp(logits[sel[j]] - mx);
+        sum += wts[j];
+    }
+    for (int j = 0; j < K; ++j) wts[j] /= sum;
+    return 0;
+}
+
+/* out += sum_j wts[j] * expert_{sel[j]}(n), in the order of sel. */
+static void moe_add_routed(const orc_moe_cfg* m, int d, const double* n, const orc_moe_weights* mw,
+                           const int* sel, const double* wts, double* out)
+{
+    const int f = m->d_ff_expert;
+    double* t = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int j = 0; j < m->top_k; ++j) {
+        const size_t e = (size_t)sel[j];
+        swiglu(n, mw->w_gate + e * (size_t)f * d, mw->w_up + e * (size_t)f * d,
+               mw->w_down + e * (size_t)d * f, d, f, t);
+        for (int i = 0; i < d; ++i) out[i] += wts[j] * t[i];
+    }
+    free(t);
+}
+
+int orc_moe_ffn(const orc_cfg* c, const orc_moe_cfg* m, const double* n, const orc_weights* w,
+                const orc_moe_weights* mw, int* sel, int force, double* wts, double* logits,
+                double* out)
+{
+    const int d = c->d;
+    int rc = orc_moe_route(m, d, n, mw->router, sel, force, wts, logits);
+    if (rc) return rc;
+    swiglu(n, w->w_gate, w->w_up, w->w_down, d, c->d_ff, out); /* the shared expert */
+    moe_add_routed(m, d, n, mw, sel, wts, out);
+    return 0;
+}
+
 static int check_cfg(const orc_cfg* c, int B, int S, long start_pos, long cap)
 {
     if (!c || c->d <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->d_head <= 0 || c->d_ff <= 0)
@@ -181,12 +260,20 @@ static double* cache_row(double* cache, const orc_cfg* c, long cap, int b, int g
  * Attn: q, k, v projections, RoPE on q and k, cache write of k and v at
  * start_pos + s [L3], causal grouped-query attention, output projection;
  * FFN: down(SiLU(gate n) * up n) [LL 04]. */
-int orc_block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, const double* x,
-                      const orc_weights* w, double* k_cache, double* v_cache, double* y,
-                      const int* rows, int n_rows, orc_stages* st)
+/* The block, with a dense FFN (mc == NULL) or with the MoE FFN, whose
+ * shared expert is w's gate/up/down. */
+static int block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, const double* x,
+                         const orc_weights* w, double* k_cache, double* v_cache, double* y,
+                         const int* rows, int n_rows, orc_stages* st, const orc_moe_cfg* mc,
+                         const orc_moe_weights* mw, int* sel, int force, double* wts,
+                         double* logits)
 {
     int rc = check_cfg(c, B, S, start_pos, cap);
     if (rc) return rc;
+    if (mc && (mc->n_experts < 1 || mc->top_k < 1 || mc->top_k > mc->n_experts || mc->d_ff_expert < 1 ||
+               !mw || !sel || !wts || !logits))
+        return -10;
+    int moe_rc = 0;
     const int d = c->d, H = c->n_heads, G = c->n_kv_heads, dh = c->d_head, dff = c->d_ff;
     const int n_rep = H / G;
     const int qd = H * dh, kvd = G * dh;
@@ -270,6 +357,21 @@ int orc_block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, 
         orc_linear(n2, w->w_up, dff, d, u);
         for (int j = 0; j < dff; ++j) z[j] = orc_silu(a[j]) * u[j];
         orc_linear(z, w->w_down, d, dff, f);
+        if (mc) {
+            /* MoE: the FFN above is the always-on shared expert; add the
+             * chosen experts, weighted [L4 The idea] */
+            const int K = mc->top_k;
+            int* sr = sel + (size_t)r * K;
+            double* wr = wts + (size_t)r * K;
+            const int rr = orc_moe_route(mc, d, n2, mw->router, sr, force, wr,
+                                         logits + (size_t)r * mc->n_experts);
+            if (rr) {
+#pragma omp atomic write
+                moe_rc = rr;
+            } else {
+                moe_add_routed(mc, d, n2, mw, sr, wr, f);
+            }
+        }
         for (int i = 0; i < d; ++i) y[(size_t)r * d + i] = h[i] + f[i];
 
         if (st && st->q) memcpy(st->q + (size_t)r * qd, q, sizeof(double) * qd);
@@ -282,7 +384,25 @@ int orc_block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, 
     free(n1_all);
     free(want);
     free(need);
-    return 0;
+    return moe_rc;
+}
+
+int orc_block_forward(const orc_cfg* c, int B, int S, long start_pos, long cap, const double* x,
+                      const orc_weights* w, double* k_cache, double* v_cache, double* y,
+                      const int* rows, int n_rows, orc_stages* st)
+{
+    return block_forward(c, B, S, start_pos, cap, x, w, k_cache, v_cache, y, rows, n_rows, st, NULL,
+                         NULL, NULL, 0, NULL, NULL);
+}
+
+int orc_moe_block_forward(const orc_cfg* c, const orc_moe_cfg* m, int B, int S, long start_pos,
+                          long cap, const double* x, const orc_weights* w, const orc_moe_weights* mw,
+                          double* k_cache, double* v_cache, double* y, const int* rows, int n_rows,
+                          int* sel, int force, double* wts, double* logits)
+{
+    if (!m) return -10;
+    return block_forward(c, B, S, start_pos, cap, x, w, k_cache, v_cache, y, rows, n_rows, NULL, m,
+                         mw, sel, force, wts, logits);
 }
 
 int orc_stack_forward(const orc_cfg* c, int n_layers, int B, int S, long start_pos, long cap,

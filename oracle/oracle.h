@@ -67,6 +67,43 @@ int orc_block_forward(const orc_cfg* cfg, int B, int S, long start_pos, long cap
                       const double* x, const orc_weights* w, double* k_cache, double* v_cache,
                       double* y, const int* rows, int n_rows, orc_stages* stages);
 
+/* Mixture-of-experts FFN ("Llama 4 From Scratch", The idea: N expert FFNs,
+ * a router sending each token to the top k, one always-on shared expert).
+ * Readings where the page is silent: the router is a bias-free linear layer
+ * [E][d]; the top k are the k largest logits, larger first, the lower expert
+ * index first among equal logits; the chosen experts are weighted by the
+ * softmax of their logits; every expert, the shared one included, is a
+ * SwiGLU FFN.  The shared expert is the block's own FFN (orc_weights
+ * w_gate/w_up/w_down, width cfg.d_ff). */
+typedef struct {
+    int n_experts, top_k, d_ff_expert;
+} orc_moe_cfg;
+
+typedef struct {
+    const double* router;  /* [E][d] */
+    const double* w_gate;  /* [E][d_ff_expert][d] */
+    const double* w_up;    /* [E][d_ff_expert][d] */
+    const double* w_down;  /* [E][d][d_ff_expert] */
+} orc_moe_weights;
+
+/* Routing of one normalised row n [d]: logits [E] = n router^T; sel [k]
+ * receives the top k (or, with force != 0, holds the experts to use, which
+ * must be distinct and in range); wts [k] their softmax weights.  Returns 0
+ * or a negative code. */
+int orc_moe_route(const orc_moe_cfg* m, int d, const double* n, const double* router, int* sel,
+                  int force, double* wts, double* logits);
+/* out [d] = shared(n) + sum_j wts[j] * expert_{sel[j]}(n), routing as above. */
+int orc_moe_ffn(const orc_cfg* c, const orc_moe_cfg* m, const double* n, const orc_weights* w,
+                const orc_moe_weights* mw, int* sel, int force, double* wts, double* logits,
+                double* out);
+/* The block with the MoE FFN: y = h + MoE(RMSNorm_2(h)), everything else as
+ * orc_block_forward.  sel [B*S][k] (in with force, else out), wts [B*S][k],
+ * logits [B*S][E] per row. */
+int orc_moe_block_forward(const orc_cfg* c, const orc_moe_cfg* m, int B, int S, long start_pos,
+                          long cap, const double* x, const orc_weights* w, const orc_moe_weights* mw,
+                          double* k_cache, double* v_cache, double* y, const int* rows, int n_rows,
+                          int* sel, int force, double* wts, double* logits);
+
 /* A stack of n_layers blocks and the final RMSNorm: block l takes the output
  * of block l-1 (block 0 takes x), and y = RMSNorm(output of the last block)
  * with gain final_norm and the config's epsilon ("The Evolving Transformer 04

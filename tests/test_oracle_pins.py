@@ -579,6 +579,140 @@ def test_stack_prefill_equals_token_by_token_decode():
         np.testing.assert_allclose(va, vb, rtol=0, atol=1e-13)
 
 
+# -------------------------------------------------------------------- MoE ----
+# "Llama 4 From Scratch", The idea: N expert FFNs, a router sending each token
+# to the top k, one always-on shared expert.
+
+_MOE_W = workloads.BlockWorkload("moe_pin", "f32", B=2, S=5, start_pos=0, d=32, H=4, n_kv=2, d_head=8,
+                                 d_ff=48, theta=1e4, eps=1e-5, w_std=0.1, g_mean=1.0, g_std=0.1,
+                                 seed=9, n_experts=6, top_k=2, d_ff_expert=40)
+
+
+def _np_swiglu(n, gate, up, down):
+    a = n @ gate.T
+    return ((a / (1.0 + np.exp(-a))) * (n @ up.T)) @ down.T
+
+
+def test_moe_route_is_top_k_by_brute_force():
+    """Router logits are n . router^T (numpy); the chosen experts are the k
+    largest, in order, ties to the lower index (numpy stable argsort); the
+    weights are the softmax of the chosen logits (scipy)."""
+    r = rng(31)
+    for E, K in ((6, 2), (16, 1), (8, 8), (5, 3)):
+        moe = {"n_experts": E, "top_k": K, "d_ff_expert": 4}
+        for _ in range(20):
+            n = r.normal(0, 1, 24)
+            router = r.normal(0, 1, (E, 24))
+            if r.random() < 0.3:      # equal logits: duplicated router rows
+                i, j = r.choice(E, 2, replace=False)
+                router[j] = router[i]
+            sel, wts, logits = oracle.moe_route(moe, n, router)
+            want_logits = n @ router.T
+            np.testing.assert_allclose(logits, want_logits, rtol=1e-13, atol=1e-13)
+            order = np.argsort(-logits, kind="stable")[:K]
+            assert list(sel) == list(order)
+            np.testing.assert_allclose(wts, scipy.special.softmax(logits[order]), rtol=1e-13)
+
+
+def _moe_cfg(w):
+    return oracle.cfg_of(w), w.moe
+
+
+def _concat_ffn(t, parts):
+    """The block's weights with its FFN replaced by the concatenation of
+    several SwiGLU FFNs [(gate, up, down, scale)]: a SwiGLU of the
+    concatenated hidden width is the sum of the parts."""
+    g = np.concatenate([p[0] for p in parts], axis=0)
+    u = np.concatenate([p[1] for p in parts], axis=0)
+    dn = np.concatenate([p[2] * p[3] for p in parts], axis=1)
+    out = {k: t[k].double().numpy() for k in oracle.WEIGHT_NAMES}
+    out.update(w_gate=g, w_up=u, w_down=dn)
+    return out
+
+
+def test_moe_identical_experts_is_one_dense_ffn():
+    """With every routed expert equal, the weights of the k chosen ones sum to
+    1, so the MoE FFN is shared + expert: the dense block whose FFN is their
+    concatenation, whatever the router picks."""
+    w = _MOE_W
+    t = workloads.generate(w)
+    cfg, moe = _moe_cfg(w)
+    E = w.n_experts
+    for n in ("e_gate", "e_up", "e_down"):
+        t[n] = t[n][:1].expand_as(t[n]).contiguous()
+    kc, vc = oracle.empty_cache(w)
+    y, sel, wts, _ = oracle.moe_block_forward(cfg, moe, t["x"], t, 0, kc, vc)
+    assert len(set(sel.ravel().tolist())) > 1  # the router does spread the rows
+    np.testing.assert_allclose(wts.sum(axis=1), 1.0, rtol=1e-14)
+    sh = (t["w_gate"].double().numpy(), t["w_up"].double().numpy(), t["w_down"].double().numpy(), 1.0)
+    ex = (t["e_gate"][0].double().numpy(), t["e_up"][0].double().numpy(), t["e_down"][0].double().numpy(), 1.0)
+    dense = _concat_ffn(t, [sh, ex])
+    kd, vd = oracle.empty_cache(w)
+    yd, _ = oracle.block_forward(dict(cfg, d_ff=w.d_ff + w.d_ff_expert), t["x"], dense, 0, kd, vd)
+    np.testing.assert_allclose(y, yd, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(kc, kd)
+
+
+def test_moe_zero_router_takes_the_first_k_equally():
+    """A zero router gives every expert the same logit: the tie rule picks
+    experts 0 .. k-1, each weighted 1/k, so the block equals the dense block
+    whose FFN concatenates the shared expert and those experts scaled by 1/k."""
+    w = _MOE_W
+    t = workloads.generate(w)
+    t["router"] = torch.zeros_like(t["router"])
+    cfg, moe = _moe_cfg(w)
+    kc, vc = oracle.empty_cache(w)
+    y, sel, wts, _ = oracle.moe_block_forward(cfg, moe, t["x"], t, 0, kc, vc)
+    assert (sel == np.arange(w.top_k)).all()
+    np.testing.assert_array_equal(wts, 1.0 / w.top_k)
+    parts = [(t["w_gate"].double().numpy(), t["w_up"].double().numpy(), t["w_down"].double().numpy(), 1.0)]
+    for e in range(w.top_k):
+        parts.append((t["e_gate"][e].double().numpy(), t["e_up"][e].double().numpy(),
+                      t["e_down"][e].double().numpy(), 1.0 / w.top_k))
+    dense = _concat_ffn(t, parts)
+    kd, vd = oracle.empty_cache(w)
+    yd, _ = oracle.block_forward(dict(cfg, d_ff=w.d_ff + w.top_k * w.d_ff_expert), t["x"], dense, 0, kd, vd)
+    np.testing.assert_allclose(y, yd, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_ffn_row_closed_form():
+    """One row through orc_moe_ffn: shared SwiGLU plus the chosen experts'
+    SwiGLUs weighted by the softmax of their logits, each SwiGLU written out
+    in numpy; with forced experts the same formula over those experts."""
+    w = _MOE_W
+    t = workloads.generate(w)
+    cfg, moe = _moe_cfg(w)
+    r = rng(4)
+    T = {k: t[k].double().numpy() for k in ("w_gate", "w_up", "w_down") + oracle.MOE_WEIGHT_NAMES}
+    for force in (None, [3, 1], [5, 0]):
+        n = r.normal(0, 1, w.d)
+        out, sel, wts, logits = oracle.moe_ffn(cfg, moe, n, t, force_sel=force)
+        if force is not None:
+            assert list(sel) == force
+        want = _np_swiglu(n, T["w_gate"], T["w_up"], T["w_down"])
+        lg = n @ T["router"].T
+        p = scipy.special.softmax(lg[list(sel)])
+        for j, e in enumerate(sel):
+            want = want + p[j] * _np_swiglu(n, T["e_gate"][e], T["e_up"][e], T["e_down"][e])
+        np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-13)
+
+
+def test_moe_block_decode_token_by_token_equals_prefill():
+    """"Full Llama 3 transformer block", How it works: single-token steps give
+    the rows of one prefill, with the MoE FFN too (it acts row by row)."""
+    w = _MOE_W
+    t = workloads.generate(w)
+    cfg, moe = _moe_cfg(w)
+    kc, vc = oracle.empty_cache(w)
+    y_full, sel_full, _, _ = oracle.moe_block_forward(cfg, moe, t["x"], t, 0, kc, vc)
+    k2, v2 = oracle.empty_cache(w)
+    x = t["x"].double().numpy()
+    for s in range(w.S):
+        y_s, sel_s, _, _ = oracle.moe_block_forward(cfg, moe, x[:, s:s + 1].copy(), t, s, k2, v2)
+        np.testing.assert_allclose(y_s[:, 0], y_full[:, s], rtol=0, atol=1e-13)
+        assert (sel_s == sel_full.reshape(w.B, w.S, -1)[:, s]).all()
+
+
 # ------------------------------------------------- planted mistakes are caught ----
 
 MUTANTS = [
@@ -626,6 +760,21 @@ MUTANTS = [
     ("stack: last block dropped", "for (int l = 0; l < n_layers && rc == 0; ++l)",
      "for (int l = 0; l < n_layers - 1 && rc == 0; ++l)",
      ["test_stack_chains_blocks_in_order_closed_form"]),
+    ("MoE: top-k takes the smallest", "if (!taken && (best < 0 || logits[e] > logits[best])) best = e;",
+     "if (!taken && (best < 0 || logits[e] < logits[best])) best = e;",
+     ["test_moe_route_is_top_k_by_brute_force"]),
+    ("MoE: ties to the higher index", "if (!taken && (best < 0 || logits[e] > logits[best])) best = e;",
+     "if (!taken && (best < 0 || logits[e] >= logits[best])) best = e;",
+     ["test_moe_route_is_top_k_by_brute_force", "test_moe_zero_router_takes_the_first_k_equally"]),
+    ("MoE: weights not normalised", "    for (int j = 0; j < K; ++j) wts[j] /= sum;\n", "\n",
+     ["test_moe_identical_experts_is_one_dense_ffn", "test_moe_zero_router_takes_the_first_k_equally",
+      "test_moe_route_is_top_k_by_brute_force"]),
+    ("MoE: shared expert left out", "swiglu(n, w->w_gate, w->w_up, w->w_down, d, c->d_ff, out); /* the shared expert */",
+     "memset(out, 0, sizeof(double) * (size_t)d);", ["test_moe_ffn_row_closed_form"]),
+    ("MoE: up and gate swapped in the experts",
+     "swiglu(n, mw->w_gate + e * (size_t)f * d, mw->w_up + e * (size_t)f * d,",
+     "swiglu(n, mw->w_up + e * (size_t)f * d, mw->w_gate + e * (size_t)f * d,",
+     ["test_moe_ffn_row_closed_form", "test_moe_zero_router_takes_the_first_k_equally"]),
 ]
 
 
@@ -654,7 +803,8 @@ def test_planted_mistake_is_caught(tmp_path, label, old, new, pins):
         import ctypes
         mut = ctypes.CDLL(str(so))
         for name in ("orc_rms_norm", "orc_linear", "orc_rope", "orc_rope_freq", "orc_rope_cfg",
-                     "orc_silu", "orc_attend", "orc_block_forward", "orc_stack_forward"):
+                     "orc_silu", "orc_attend", "orc_block_forward", "orc_stack_forward", "orc_moe_route",
+                     "orc_moe_ffn", "orc_moe_block_forward"):
             getattr(mut, name).argtypes = getattr(real, name).argtypes
             getattr(mut, name).restype = getattr(real, name).restype
         oracle._lib = mut

@@ -17,7 +17,8 @@ Shapes follow the pages:
 
 Draw protocol (one torch CPU generator per workload, seeded):
   x, g1, Wq, Wk, Wv, Wo, g2, W_gate, W_up, W_down, then the pre-filled K and V
-  cache rows (decode workloads only).  Each draw is randn(shape, fp32) * std +
+  cache rows (decode workloads only), then for mixture-of-experts blocks the
+  router [E][d] and the experts' gate [E][f][d], up [E][f][d], down [E][d][f].  Each draw is randn(shape, fp32) * std +
   mean, then rounded to the workload dtype (round-to-nearest-even for bf16).
   Gains given as "ones" consume no draws.  The second parameter of N(mu, s) is
   the standard deviation.
@@ -61,6 +62,12 @@ class BlockWorkload:
     seed: int = 0
     rope_half: bool = False   # RoPE pairs (i, i + d_head/2) instead of (2i, 2i+1)
     rope_scaling: Optional[tuple] = None  # (scale, low, high, original length) or None
+    # mixture-of-experts FFN: n_experts > 0 adds a router and n_experts routed
+    # SwiGLU experts of width d_ff_expert, top_k per token; the block's own
+    # FFN (width d_ff) is then the always-on shared expert
+    n_experts: int = 0
+    top_k: int = 0
+    d_ff_expert: int = 0
 
     @property
     def capacity(self) -> int:
@@ -77,6 +84,12 @@ class BlockWorkload:
     @property
     def n_rep(self) -> int:
         return self.H // self.n_kv
+
+    @property
+    def moe(self) -> Optional[Dict]:
+        if self.n_experts <= 0:
+            return None
+        return {"n_experts": self.n_experts, "top_k": self.top_k, "d_ff_expert": self.d_ff_expert}
 
 
 WORKLOADS: Dict[str, BlockWorkload] = {
@@ -166,6 +179,14 @@ def generate(w: BlockWorkload, with_cache: bool = True) -> Dict[str, torch.Tenso
         shape = (w.B, w.n_kv, w.start_pos, w.d_head)
         out["k_prefix"] = _draw(gen, shape, 0.0, w.cache_std, dt)
         out["v_prefix"] = _draw(gen, shape, 0.0, w.cache_std, dt)
+    if w.n_experts > 0:
+        # after everything above, so a block's dense draws do not depend on
+        # whether it has experts
+        E, fe = w.n_experts, w.d_ff_expert
+        out["router"] = _draw(gen, (E, w.d), 0.0, w.w_std, dt)
+        out["e_gate"] = _draw(gen, (E, fe, w.d), 0.0, w.w_std, dt)
+        out["e_up"] = _draw(gen, (E, fe, w.d), 0.0, w.w_std, dt)
+        out["e_down"] = _draw(gen, (E, w.d, fe), 0.0, w.w_std, dt)
     return out
 
 
