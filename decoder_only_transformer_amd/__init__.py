@@ -27,7 +27,8 @@ EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_forward_ragge
            "llama_block_copy_stage", "llama_block_profile", "llama_block_profile_read",
            "llama_stack_init", "llama_stack_forward", "llama_stack_forward_device_pos",
            "llama_stack_graph_create", "llama_stack_graph_launch", "llama_stack_graph_destroy",
-           "llama_stack_destroy", "llama_stack_num_layers", "llama_stack_last_error")
+           "llama_stack_destroy", "llama_stack_num_layers", "llama_stack_last_error",
+           "llama_moe_block_init", "llama_block_copy_routing")
 MAX_STACK_LAYERS = 1024
 STAGE_NAMES = ("rmsnorm_1", "qkv_rope_append", "attention", "o_proj_residual", "rmsnorm_2",
                "gate_up_swiglu", "down_residual")
@@ -56,6 +57,19 @@ class LbKVCache(ctypes.Structure):
 
 
 WEIGHT_NAMES = [f[0] for f in LbWeights._fields_]
+
+
+class LbMoeConfig(ctypes.Structure):
+    _fields_ = [("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("d_ff_expert", ctypes.c_int32)]
+
+
+class LbMoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("router", "w_gate", "w_up", "w_down")]
+
+
+# names of the routed experts' tensors in weight dicts (the block's own FFN
+# tensors are the shared expert)
+MOE_WEIGHT_NAMES = {"router": "router", "w_gate": "e_gate", "w_up": "e_up", "w_down": "e_down"}
 
 
 class LlamaBlockError(RuntimeError):
@@ -100,6 +114,12 @@ def lib() -> ctypes.CDLL:
         L.llama_block_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_int64)]
         L.llama_block_profile_read.restype = ctypes.c_int
+        L.llama_moe_block_init.argtypes = [ctypes.POINTER(LbConfig), ctypes.POINTER(LbWeights),
+                                           ctypes.POINTER(LbMoeConfig), ctypes.POINTER(LbMoeWeights),
+                                           ctypes.POINTER(vp)]
+        L.llama_moe_block_init.restype = ctypes.c_int
+        L.llama_block_copy_routing.argtypes = [vp, vp, vp, vp, vp]
+        L.llama_block_copy_routing.restype = ctypes.c_int
         kvp = ctypes.POINTER(LbKVCache)
         L.llama_stack_init.argtypes = [ctypes.POINTER(LbConfig), i32, ctypes.POINTER(LbWeights), vp,
                                        ctypes.POINTER(vp)]
@@ -160,6 +180,27 @@ def llama_block_init(cfg: LbConfig, weights: Dict[str, "object"]) -> int:
     st = lib().llama_block_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
     _check(None, st, "llama_block_init")
     return h.value
+
+
+def llama_moe_block_init(cfg: LbConfig, weights: Dict[str, "object"], moe: Dict[str, int]) -> int:
+    """A MoE block: weights as for llama_block_init (its FFN is the shared
+    expert) plus the experts under the names of MOE_WEIGHT_NAMES' values;
+    moe: n_experts, top_k, d_ff_expert."""
+    w = LbWeights(*[_ptr(weights[n]) for n in WEIGHT_NAMES])
+    ew = LbMoeWeights(*[_ptr(weights[MOE_WEIGHT_NAMES[f]]) for f, _ in LbMoeWeights._fields_])
+    mc = LbMoeConfig(int(moe["n_experts"]), int(moe["top_k"]), int(moe["d_ff_expert"]))
+    h = ctypes.c_void_p()
+    st = lib().llama_moe_block_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(mc), ctypes.byref(ew),
+                                    ctypes.byref(h))
+    _check(None, st, "llama_moe_block_init")
+    return h.value
+
+
+def llama_block_copy_routing(handle: int, sel=None, weights=None, logits=None, stream=None) -> None:
+    """Copy the last forward's routing into the given tensors (any may be None):
+    sel int32 [rows][top_k], weights fp32 [rows][top_k], logits fp32 [rows][E]."""
+    st = lib().llama_block_copy_routing(handle, _ptr(sel), _ptr(weights), _ptr(logits), _stream(stream))
+    _check(handle, st, "llama_block_copy_routing")
 
 
 def llama_block_forward(handle: int, x, start_pos: int, kv: Tuple, out, stream=None) -> None:
@@ -430,3 +471,22 @@ class StackGraph:
         if self.graph:
             llama_stack_graph_destroy(self.graph)
             self.graph = None
+
+
+class LlamaMoeBlock(LlamaBlock):
+    """A block whose FFN is a mixture of experts with a shared expert."""
+
+    def __init__(self, cfg: LbConfig, weights: Dict[str, "object"], moe: Dict[str, int]):
+        self.cfg = cfg
+        self.moe = dict(moe)
+        self.handle = llama_moe_block_init(cfg, weights, moe)
+
+    def routing(self, rows: int):
+        """(sel, weights, logits) of the last forward's `rows` token rows, on the device."""
+        import torch
+        K, E = self.moe["top_k"], self.moe["n_experts"]
+        sel = torch.empty((rows, K), dtype=torch.int32, device="cuda")
+        wts = torch.empty((rows, K), dtype=torch.float32, device="cuda")
+        lg = torch.empty((rows, E), dtype=torch.float32, device="cuda")
+        llama_block_copy_routing(self.handle, sel, wts, lg)
+        return sel, wts, lg

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libllama_block.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["llama_block.cpp", "k_small.hip", "k_gemm.hip", "k_attn.hip"]
+SOURCES = ["llama_block.cpp", "k_small.hip", "k_gemm.hip", "k_attn.hip", "k_moe.hip"]
 
 FLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

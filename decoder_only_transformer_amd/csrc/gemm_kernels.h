@@ -32,10 +32,10 @@ namespace lb {
 // ------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// One BM x BN output tile at (m0, n0); lds holds 2 * (BM + BN) * 64 elements.
 template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi>
-__global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict__ A,
-                                                            const T* __restrict__ W, int M, int N,
-                                                            int K, Epi epi) {
+__device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T* __restrict__ W, int M,
+                                               int N, int K, Epi epi, int m0, int n0, T* lds) {
     typedef typename vec8<T>::type V8;
     constexpr int NT = NW * 64;
     constexpr int BK = 64;
@@ -48,23 +48,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
     constexpr int EPR = 64;                 // epilogue rows per pass
     constexpr int CPAD = BN + 8;            // fp32 row pitch of the epilogue stage
     static_assert(EPR * CPAD * 4 <= 2 * (BM + BN) * BK * (int)sizeof(T), "epilogue stage fits");
-    __shared__ __attribute__((aligned(16))) T lds[2 * (BM + BN) * BK];
-
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    // Workgroups are dealt round-robin to the 8 XCDs: renumber so that each
-    // XCD runs a contiguous range of tiles, then walk tiles in groups of 8
-    // tile-rows (column-major inside a group) so neighbours share A and W panels.
-    int bid = blockIdx.x;
-    const int nb = gridDim.x;
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-    constexpr int GM = 8;
-    const int per_group = GM * tiles_n;
-    const int first_m = (bid / per_group) * GM;
-    const int gsize = min(tiles_m - first_m, GM);
-    const int in_group = bid % per_group;
-    const int tm = first_m + in_group % gsize;
-    const int tn = in_group / gsize;
-    const int m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
@@ -169,6 +152,71 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
         }
         __syncthreads();
     }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi>
+__global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict__ A,
+                                                            const T* __restrict__ W, int M, int N,
+                                                            int K, Epi epi) {
+    __shared__ __attribute__((aligned(16))) T lds[2 * (BM + BN) * 64];
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    // Workgroups are dealt round-robin to the 8 XCDs: renumber so that each
+    // XCD runs a contiguous range of tiles, then walk tiles in groups of 8
+    // tile-rows (column-major inside a group) so neighbours share A and W panels.
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (bid / per_group) * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int in_group = bid % per_group;
+    const int tm = first_m + in_group % gsize;
+    const int tn = in_group / gsize;
+    gemm_mfma_tile<T, BM, BN, WM, WN, NW, Epi>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
+}
+
+// Any epilogue applied to rows counted from m_off (the tile sees row m, the
+// output row is m + m_off).
+template <class Epi>
+struct EpiRowOff {
+    Epi e;
+    int m_off;
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const { e.row8(m + m_off, n, v); }
+};
+
+// ------------------------------------------------------------------------------------
+// Grouped GEMM over experts: group e multiplies the rows [row_off[e],
+// row_off[e+1]) of A by its own W_e = W + e * N * K (N x K, the layout of
+// gemm_mfma_kernel).  The groups' BM-row tiles are numbered consecutively
+// (group e owns tiles [tile_off[e], tile_off[e+1])); the grid holds
+// tiles_m_max x tiles_n blocks, a bound the host knows without reading the
+// group sizes, and blocks past the last tile return at once.  Consecutive
+// blocks take consecutive row tiles of one column tile, so the tiles of a
+// group share its W panel.
+// ------------------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi>
+__global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restrict__ A,
+                                                               const T* __restrict__ W,
+                                                               const int* __restrict__ row_off,
+                                                               const int* __restrict__ tile_off, int E,
+                                                               int N, int K, int tiles_m_max, Epi epi) {
+    __shared__ __attribute__((aligned(16))) T lds[2 * (BM + BN) * 64];
+    const int bid = blockIdx.x;
+    const int tn = bid / tiles_m_max, tmg = bid - tn * tiles_m_max;
+    if (tmg >= tile_off[E]) return;
+    // the group of this row tile: the last e with tile_off[e] <= tmg (empty
+    // groups own no tile, so that e is the one whose range holds tmg)
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_off[mid] <= tmg) lo = mid;
+        else hi = mid - 1;
+    }
+    const int r0 = row_off[lo], rows = row_off[lo + 1] - r0;
+    gemm_mfma_tile<T, BM, BN, WM, WN, NW, EpiRowOff<Epi>>(A + (size_t)r0 * K, W + (size_t)lo * N * K, rows, N, K,
+                                                          EpiRowOff<Epi>{epi, r0}, (tmg - tile_off[lo]) * BM,
+                                                          tn * BN, lds);
 }
 
 // ------------------------------------------------------------------------------------

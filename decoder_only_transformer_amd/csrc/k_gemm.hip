@@ -200,6 +200,12 @@ hipError_t gemm_resid(Elem op, Elem resid_t, const void* A, const void* W, int M
         return run_gemm((const f16*)A, (const f16*)W, M, N, K, EpiResid<bf16>{(const bf16*)resid, out, N}, part, s);
     if (op == Elem::BF16 && resid_t == Elem::BF16)
         return run_gemm((const bf16*)A, (const bf16*)W, M, N, K, EpiResid<bf16>{(const bf16*)resid, out, N}, part, s);
+    // fp32 residual (out may be resid itself: each element is read, then
+    // written, by one thread)
+    if (op == Elem::F16 && resid_t == Elem::F32)
+        return run_gemm((const f16*)A, (const f16*)W, M, N, K, EpiResid<float>{(const float*)resid, out, N}, part, s);
+    if (op == Elem::BF16 && resid_t == Elem::F32)
+        return run_gemm((const bf16*)A, (const bf16*)W, M, N, K, EpiResid<float>{(const float*)resid, out, N}, part, s);
     return hipErrorInvalidValue;
 }
 

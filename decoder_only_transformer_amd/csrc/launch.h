@@ -106,4 +106,28 @@ hipError_t attn_decode(Elem op, Elem kv_t, const AttnArgs& a, float* part, int o
 // Plain fp32 attention (fp32 blocks, any seq_len).
 hipError_t attn_simple(const AttnArgs& a, hipStream_t s);
 
+// ---- mixture-of-experts FFN (k_moe.hip) --------------------------------------------
+constexpr int kMoeMaxExperts = 256;
+constexpr int kMoeMaxTopK = 8;
+constexpr int kMoeMaxWidth = 16384;  // d_model the router stages in LDS
+constexpr int kMoeTileM = 128;       // row tile of the grouped expert GEMMs
+// logits [M][E] fp32; sel / wts [M][K]: the top K experts, larger logit first
+// (lower index among equal logits), and the softmax of their logits
+hipError_t launch_moe_router(Elem op, const void* n, const void* wr, int M, int d, int E, int K,
+                             float* logits, int* sel, float* wts, hipStream_t s);
+// row_off / tile_off [E+1]; src [MK]: pair of each sorted row; slot [MK]:
+// sorted row of each pair (pair i = token i / K, choice i % K)
+hipError_t launch_moe_route(const int* sel, int MK, int E, int* row_off, int* tile_off, int* src, int* slot,
+                            hipStream_t s);
+hipError_t launch_moe_gather(Elem op, const void* n, const int* src, int MK, int K, int d, void* a,
+                             hipStream_t s);
+// expert e: z rows [row_off[e], row_off[e+1]) = SwiGLU(A rows . W_e^T), W_e = W + e*N*K (gate/up packed)
+hipError_t launch_moe_grouped_swiglu(Elem op, const void* A, const void* W, const int* row_off, const int* tile_off,
+                                     int E, int MK, int N, int K, void* z, hipStream_t s);
+// expert e: r rows = A rows . W_e^T in fp32
+hipError_t launch_moe_grouped_down(Elem op, const void* A, const void* W, const int* row_off, const int* tile_off,
+                                   int E, int MK, int N, int K, float* r, hipStream_t s);
+hipError_t launch_moe_combine(Elem out_t, const float* hs, const float* r, const int* slot, const float* wts,
+                              int M, int K, int d, void* y, hipStream_t s);
+
 }  // namespace lb

@@ -66,7 +66,24 @@ struct lb_block {
     void* at_n2 = nullptr;
     void* at_z = nullptr;
     int last_mt = 0;             // row tiles of the last forward's tiled activations (0: none)
+    int last_ffn_mt = 0;         // the same for n2 and z (MoE blocks keep them row-major)
     int last_m = 0;
+    // mixture-of-experts FFN (moe_E > 0); the dense FFN above is the shared expert
+    int moe_E = 0, moe_K = 0, moe_fe = 0;
+    void* w_router = nullptr;    // [E][d] operand type
+    void* w_egu = nullptr;       // [E][2 fe][d] gate/up packed per expert
+    void* w_edown = nullptr;     // [E][d][fe]
+    float* m_logits = nullptr;   // [T][E]
+    int* m_sel = nullptr;        // [T][K]
+    float* m_wts = nullptr;      // [T][K]
+    int* m_row_off = nullptr;    // [E+1]
+    int* m_tile_off = nullptr;   // [E+1]
+    int* m_src = nullptr;        // [T*K]
+    int* m_slot = nullptr;       // [T*K]
+    void* m_a = nullptr;         // [T*K][d] normalised rows in expert order
+    void* m_z = nullptr;         // [T*K][fe]
+    float* m_r = nullptr;        // [T*K][d] expert outputs
+    float* m_hs = nullptr;       // [T][d] h plus the shared expert
     std::vector<void*> allocs;
     std::string err;
     // per-stage timing: a ring of event sets, LB_NUM_STAGES + 1 events each
@@ -392,6 +409,86 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
     return LB_OK;
 }
 
+extern "C" lb_status llama_moe_block_init(const lb_config* cfg, const lb_weights* w, const lb_moe_config* moe,
+                                          const lb_moe_weights* ew, lb_block** out) {
+    g_init_error.clear();
+    if (!out) return fail(nullptr, LB_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!cfg || !w || !moe || !ew) return fail(nullptr, LB_ERR_INVALID_ARG, "cfg, weights, moe or experts is NULL");
+    if (!weights_complete(w) || !ew->router || !ew->w_gate || !ew->w_up || !ew->w_down)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "a weight pointer is NULL");
+    const int E = moe->n_experts, K = moe->top_k, fe = moe->d_ff_expert;
+    if (E < 1 || E > lb::kMoeMaxExperts)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "n_experts (%d) must be in [1, %d]", E, lb::kMoeMaxExperts);
+    if (K < 1 || K > E || K > lb::kMoeMaxTopK)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "top_k (%d) must be in [1, min(n_experts, %d)]", K, lb::kMoeMaxTopK);
+    if (fe < 1) return fail(nullptr, LB_ERR_INVALID_ARG, "d_ff_expert (%d) must be >= 1", fe);
+    lb_status st = validate_config(cfg);
+    if (st != LB_OK) return st;
+    if (cfg->dtype != LB_BF16) return fail(nullptr, LB_ERR_UNSUPPORTED, "MoE blocks run in bf16 only");
+    if (fe % 64 != 0) return fail(nullptr, LB_ERR_UNSUPPORTED, "d_ff_expert (%d) must be a multiple of 64", fe);
+    if ((long)cfg->max_tokens * K > (1L << 24))
+        return fail(nullptr, LB_ERR_UNSUPPORTED, "max_tokens * top_k exceeds 2^24");
+    lb_block* blk = nullptr;
+    st = create_core(cfg, &blk);
+    if (st != LB_OK) return st;
+    blk->moe_E = E;
+    blk->moe_K = K;
+    blk->moe_fe = fe;
+    const lb_config& c = blk->cfg;
+    const size_t d = (size_t)c.d_model, T = (size_t)c.max_tokens, eo = esz(blk->op);
+    bool ok = dalloc(blk, &blk->w_router, (size_t)E * d * eo) &&
+              dalloc(blk, &blk->w_egu, (size_t)E * 2 * fe * d * eo) &&
+              dalloc(blk, &blk->w_edown, (size_t)E * d * fe * eo) &&
+              dalloc(blk, &blk->m_logits, T * E * 4) && dalloc(blk, &blk->m_sel, T * K * 4) &&
+              dalloc(blk, &blk->m_wts, T * K * 4) && dalloc(blk, &blk->m_row_off, (size_t)(E + 1) * 4) &&
+              dalloc(blk, &blk->m_tile_off, (size_t)(E + 1) * 4) && dalloc(blk, &blk->m_src, T * K * 4) &&
+              dalloc(blk, &blk->m_slot, T * K * 4) && dalloc(blk, &blk->m_a, T * K * d * eo) &&
+              dalloc(blk, &blk->m_z, T * K * fe * eo) && dalloc(blk, &blk->m_r, T * K * d * 4) &&
+              dalloc(blk, &blk->m_hs, T * d * 4);
+    if (!ok) st = fail(nullptr, LB_ERR_OOM, "device allocation failed (experts)");
+    if (st == LB_OK) st = load_layers(blk, w, 1, &blk->lw);
+    if (st == LB_OK) {
+        hipStream_t s = nullptr;
+        hipError_t e = hipStreamCreate(&s);
+        const Elem dt = blk->dt, op = blk->op;
+        const size_t ebytes = esz(dt);
+        if (e == hipSuccess) e = lb::launch_convert(dt, op, ew->router, blk->w_router, (size_t)E * d, s);
+        for (int x = 0; x < E && e == hipSuccess; ++x) {
+            const size_t off = (size_t)x * fe * d;
+            e = lb::launch_pack_gate_up(dt, op, (const char*)ew->w_gate + off * ebytes,
+                                        (const char*)ew->w_up + off * ebytes,
+                                        (char*)blk->w_egu + 2 * off * eo, fe, (int)d, s);
+        }
+        if (e == hipSuccess) e = lb::launch_convert(dt, op, ew->w_down, blk->w_edown, (size_t)E * d * fe, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (s) hipStreamDestroy(s);
+        if (e != hipSuccess) st = fail(nullptr, LB_ERR_HIP, "expert weight packing failed: %s", hipGetErrorString(e));
+    }
+    if (st != LB_OK) {
+        free_all(blk);
+        delete blk;
+        return st;
+    }
+    *out = blk;
+    return LB_OK;
+}
+
+extern "C" lb_status llama_block_copy_routing(lb_block* blk, int32_t* sel, float* weights, float* logits,
+                                              void* stream) {
+    if (!blk) return LB_ERR_INVALID_ARG;
+    blk->err.clear();
+    if (blk->moe_E == 0) return fail(blk, LB_ERR_INVALID_ARG, "not a MoE block");
+    const size_t M = (size_t)blk->last_m, K = (size_t)blk->moe_K, E = (size_t)blk->moe_E;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (sel) e = hipMemcpyAsync(sel, blk->m_sel, M * K * 4, hipMemcpyDefault, s);
+    if (e == hipSuccess && weights) e = hipMemcpyAsync(weights, blk->m_wts, M * K * 4, hipMemcpyDefault, s);
+    if (e == hipSuccess && logits) e = hipMemcpyAsync(logits, blk->m_logits, M * E * 4, hipMemcpyDefault, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "copy_routing: %s", hipGetErrorString(e));
+    return LB_OK;
+}
+
 extern "C" void llama_block_destroy(lb_block* blk) {
     if (!blk) return;
     int cur = 0;
@@ -408,6 +505,37 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const char* pa = (const char*)a;
     const char* pb = (const char*)b;
     return pa < pb + nb && pb < pa + na;
+}
+
+// The MoE FFN after RMSNorm_2 ("Llama 4 From Scratch", The idea): the shared
+// expert (the block's dense FFN) adds into h, the router picks each row's
+// experts, the rows are grouped by expert, the experts run as grouped GEMMs,
+// and the combine writes y = h + shared + sum of weighted expert outputs.
+template <typename Mark>
+static lb_status run_moe_ffn(lb_block* blk, const LayerW& L, const void* n2, void* z, int M, void* out,
+                             const lb::SplitWs& ws, hipStream_t s, Mark& mark) {
+    const lb_config& c = blk->cfg;
+    const int d = c.d_model, dff = c.d_ff, E = blk->moe_E, K = blk->moe_K, fe = blk->moe_fe;
+    const Elem op = blk->op;
+    const int MK = M * K;
+    mark(5);
+    hipError_t e = lb::gemm_swiglu(op, n2, L.w_gu, M, 2 * dff, d, z, ws, s);
+    if (e == hipSuccess) e = lb::launch_moe_router(op, n2, blk->w_router, M, d, E, K, blk->m_logits, blk->m_sel,
+                                                   blk->m_wts, s);
+    if (e == hipSuccess) e = lb::launch_moe_route(blk->m_sel, MK, E, blk->m_row_off, blk->m_tile_off, blk->m_src,
+                                                  blk->m_slot, s);
+    if (e == hipSuccess) e = lb::launch_moe_gather(op, n2, blk->m_src, MK, K, d, blk->m_a, s);
+    if (e == hipSuccess) e = lb::launch_moe_grouped_swiglu(op, blk->m_a, blk->w_egu, blk->m_row_off,
+                                                           blk->m_tile_off, E, MK, 2 * fe, d, blk->m_z, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "MoE gate/up: %s", hipGetErrorString(e));
+    mark(6);
+    e = lb::gemm_resid(op, Elem::F32, z, L.w_down, M, d, dff, blk->h, blk->m_hs, ws, s);
+    if (e == hipSuccess) e = lb::launch_moe_grouped_down(op, blk->m_z, blk->w_edown, blk->m_row_off, blk->m_tile_off,
+                                                         E, MK, d, fe, blk->m_r, s);
+    if (e == hipSuccess) e = lb::launch_moe_combine(blk->dt, blk->m_hs, blk->m_r, blk->m_slot, blk->m_wts, M, K, d,
+                                                    out, s);
+    if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "MoE down: %s", hipGetErrorString(e));
+    return LB_OK;
 }
 
 // sp: start position of every sequence (validated by the caller)
@@ -445,8 +573,11 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     const lb::SplitWs ws{blk->gpart, blk->gpart_cap};
     void* n1 = dec ? blk->at_n1 : blk->n1;
     void* o = dec ? blk->at_o : blk->o;
-    void* n2 = dec ? blk->at_n2 : blk->n2;
-    void* z = dec ? blk->at_z : blk->z;
+    const bool moe = blk->moe_E > 0;
+    // MoE blocks keep n2 and z row-major: the router and the grouping read n2 by rows
+    const bool dec_ffn = dec && !moe;
+    void* n2 = dec_ffn ? blk->at_n2 : blk->n2;
+    void* z = dec_ffn ? blk->at_z : blk->z;
 
     mark(0);
     e = lb::launch_rmsnorm(dt, op, x, L.g1, n1, M, d, (float)c.norm_eps, mt, s);
@@ -515,8 +646,16 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     else e = lb::gemm_resid(op, dt, o, L.w_o, M, d, blk->qd, x, blk->h, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "o projection: %s", hipGetErrorString(e));
     mark(4);
-    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, L.g2, n2, M, d, (float)c.norm_eps, mt, s);
+    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, L.g2, n2, M, d, (float)c.norm_eps, dec_ffn ? mt : 0, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_2: %s", hipGetErrorString(e));
+    blk->last_mt = mt;
+    blk->last_ffn_mt = dec_ffn ? mt : 0;
+    blk->last_m = M;
+    if (moe) {
+        lb_status st = run_moe_ffn(blk, L, n2, z, B * S, out, ws, s, mark);
+        if (st == LB_OK) mark(7);
+        return st;
+    }
     mark(5);
     if (dec) e = lb::decode_swiglu(op, n2, L.wt_gu, M, 2 * dff, d, z, ws, s);
     else e = lb::gemm_swiglu(op, n2, L.w_gu, M, 2 * dff, d, z, ws, s);
@@ -525,8 +664,6 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     if (dec) e = lb::decode_out(op, dt, z, L.wt_down, M, d, dff, blk->h, out, ws, s);
     else e = lb::gemm_out(op, dt, z, L.w_down, M, d, dff, blk->h, out, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "down projection: %s", hipGetErrorString(e));
-    blk->last_mt = mt;
-    blk->last_m = M;
     mark(7);
     return LB_OK;
 }
@@ -886,13 +1023,14 @@ extern "C" lb_status llama_block_copy_stage(lb_block* blk, lb_stage which, void*
         return fail(blk, LB_ERR_INVALID_ARG, "bad stage or NULL destination");
     const size_t cap = (size_t)blk->cfg.max_tokens * (size_t)cols * esz(e);
     if (bytes > cap) return fail(blk, LB_ERR_INVALID_ARG, "%zu bytes exceed the stage buffer (%zu)", bytes, cap);
-    if (blk->last_mt > 0 && which != LB_STAGE_Q && which != LB_STAGE_H) {
+    const int tiled_mt = (which == LB_STAGE_N2 || which == LB_STAGE_Z) ? blk->last_ffn_mt : blk->last_mt;
+    if (tiled_mt > 0 && which != LB_STAGE_Q && which != LB_STAGE_H) {
         // the last forward was a decode: this stage lives in the tiled layout;
         // lay it out row-major in the (idle) prefill buffer first
         const void* t = which == LB_STAGE_N1 ? blk->at_n1
                         : which == LB_STAGE_O ? blk->at_o
                         : which == LB_STAGE_N2 ? blk->at_n2 : blk->at_z;
-        hipError_t err = lb::launch_untile(e, t, const_cast<void*>(p), blk->last_m, (int)cols, blk->last_mt,
+        hipError_t err = lb::launch_untile(e, t, const_cast<void*>(p), blk->last_m, (int)cols, tiled_mt,
                                            (hipStream_t)stream);
         if (err != hipSuccess) return fail(blk, LB_ERR_HIP, "copy_stage: %s", hipGetErrorString(err));
     }

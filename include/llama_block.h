@@ -160,6 +160,52 @@ lb_status llama_block_forward_ragged(lb_block* blk, const void* x, int32_t batch
                                      int32_t seq_len, const int32_t* start_pos,
                                      const lb_kv_cache* kv, void* out, void* stream);
 
+/* ---- Mixture-of-experts blocks ----------------------------------------------
+ * The FFN becomes a mixture of experts with a shared expert ("Llama 4 From
+ * Scratch", The idea: N expert FFNs, a router that sends each token to its
+ * top k, one always-on shared expert):
+ *     FFN(n) = shared(n) + sum_{j<k} w_j expert_{e_j}(n)
+ * where logits = n router^T (a bias-free linear layer), e_0..e_{k-1} are the
+ * k largest logits (larger first; the lower expert index among equal
+ * logits), w = softmax of those k logits, and every expert is a SwiGLU FFN
+ * like the dense one.  The shared expert IS the block's dense FFN: the
+ * lb_weights w_gate / w_up / w_down, width cfg.d_ff.  The page leaves the
+ * router, the choice among equal scores and the weighting open; the rules
+ * above are this library's reading.  Logits are fp32 dot products of the
+ * operand-type n and router weights, so near-equal logits may be ordered
+ * differently from an exact computation. */
+typedef struct {
+    int32_t n_experts;    /* routed experts E, 1..256 */
+    int32_t top_k;        /* experts per token, 1..min(E, 8) */
+    int32_t d_ff_expert;  /* width of each routed expert; a multiple of 64 */
+} lb_moe_config;
+
+/* Device pointers in cfg.dtype, experts stacked along the first index:
+ *   router [E][d_model]   w_gate, w_up [E][d_ff_expert][d_model]
+ *   w_down [E][d_model][d_ff_expert]
+ * Copied (and repacked) by init. */
+typedef struct {
+    const void *router, *w_gate, *w_up, *w_down;
+} lb_moe_weights;
+
+/* Create a MoE block: weights as for llama_block_init (its FFN is the shared
+ * expert) plus the routed experts.  bf16 blocks only (LB_ERR_UNSUPPORTED
+ * otherwise).  The handle is used with llama_block_forward /
+ * llama_block_forward_ragged / llama_block_destroy like any block; the
+ * profiler's gate/up stage then covers the shared gate/up, the router, the
+ * grouping and the experts' gate/up, and its down stage the shared and the
+ * experts' down projections and the combine. */
+lb_status llama_moe_block_init(const lb_config* cfg, const lb_weights* weights, const lb_moe_config* moe,
+                               const lb_moe_weights* experts, lb_block** out);
+
+/* Routing of the last forward of a MoE block, for its batch*seq_len token
+ * rows: sel [rows][top_k] expert indices, weights [rows][top_k], logits
+ * [rows][n_experts] (fp32).  Any pointer may be NULL; others receive a copy
+ * (device or host memory) ordered on `stream`.  LB_ERR_INVALID_ARG for a
+ * dense block. */
+lb_status llama_block_copy_routing(lb_block* blk, int32_t* sel, float* weights, float* logits,
+                                   void* stream);
+
 /* Free the handle and everything it owns (synchronises the device first). */
 void llama_block_destroy(lb_block* blk);
 

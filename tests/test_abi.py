@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "llama_block.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(llama_(?:block|stack)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(llama_(?:block|stack|moe)_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -136,3 +136,28 @@ def test_stack_calls_reject_null_handles():
     assert L.llama_stack_num_layers(None) == 0
     L.llama_stack_destroy(None)
     L.llama_stack_graph_destroy(None)
+
+
+def test_moe_init_rejects_bad_arguments_before_any_device_call():
+    L = lbmod.lib()
+    cfg = lbmod.make_config(512, 8, 2, 64, 1024, 16, 64, 1e4, 1e-5, "bf16")
+    w = _fake_weights()
+    ew = lbmod.LbMoeWeights(0x5000, 0x6000, 0x7000, 0x8000)
+    h = ctypes.c_void_p()
+    for (E, K, fe) in ((0, 1, 64), (257, 1, 64), (8, 0, 64), (8, 9, 64), (4, 5, 64), (8, 2, 0)):
+        mc = lbmod.LbMoeConfig(E, K, fe)
+        st = L.llama_moe_block_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(mc), ctypes.byref(ew),
+                                    ctypes.byref(h))
+        assert st == lbmod.LB_ERR_INVALID_ARG, (E, K, fe)
+        assert h.value is None
+    mc = lbmod.LbMoeConfig(8, 2, 96)   # d_ff_expert not a multiple of 64
+    assert L.llama_moe_block_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(mc), ctypes.byref(ew),
+                                  ctypes.byref(h)) == lbmod.LB_ERR_UNSUPPORTED
+    f32 = lbmod.make_config(64, 4, 2, 16, 176, 16, 16, 1e4, 1e-5, "f32")
+    mc = lbmod.LbMoeConfig(8, 2, 64)
+    assert L.llama_moe_block_init(ctypes.byref(f32), ctypes.byref(w), ctypes.byref(mc), ctypes.byref(ew),
+                                  ctypes.byref(h)) == lbmod.LB_ERR_UNSUPPORTED
+    ew.w_up = None
+    assert L.llama_moe_block_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(mc), ctypes.byref(ew),
+                                  ctypes.byref(h)) == lbmod.LB_ERR_INVALID_ARG
+    assert L.llama_block_copy_routing(None, None, None, None, None) == lbmod.LB_ERR_INVALID_ARG
