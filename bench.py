@@ -40,18 +40,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_work(w, positions=None):
+def stage_work(w, positions=None, active_experts=None):
     """Algorithmic work per forward, per profiled stage: flops (matrix products,
     causal attention over visible (query, key) pairs only) and HBM bytes (each
     operand read once, each result written once).  positions: the start
-    position of each sequence (default: w.start_pos for all)."""
+    position of each sequence (default: w.start_pos for all).  For a
+    mixture-of-experts block the FFN stages add the router and the routed
+    experts (M * top_k rows); their weights count once per expert that the
+    forward used (active_experts, default all)."""
     M, d, dh, H, G, dff = w.M, w.d, w.d_head, w.H, w.n_kv, w.d_ff
     qd, kvd = H * dh, G * dh
     e = 2  # bytes per bf16/fp16 element
     starts = list(positions) if positions is not None else [w.start_pos] * w.B
     vis = sum(p + s + 1 for p in starts for s in range(w.S))       # visible pairs per head
     kv_read = sum(G * (p + w.S) * dh * 2 * e for p in starts)       # K and V, every visible row
-    return {
+    out = {
         "rmsnorm_1": {"flops": 0, "bytes": M * d * (e + e)},
         "qkv_rope_append": {"flops": 2 * M * (qd + 2 * kvd) * d,
                             "bytes": (qd + 2 * kvd) * d * e + M * d * e + M * (qd + 4 * kvd) * e},
@@ -65,6 +68,18 @@ def stage_work(w, positions=None):
         "down_residual": {"flops": 2 * M * d * dff,
                           "bytes": d * dff * e + M * dff * e + M * d * (4 + e)},
     }
+    if w.n_experts > 0:
+        E, K, fe = w.n_experts, w.top_k, w.d_ff_expert
+        act = E if active_experts is None else active_experts
+        MK = M * K
+        gu, dn = out["gate_up_swiglu"], out["down_residual"]
+        # router, gathered rows, experts' gate/up, their z
+        gu["flops"] += 2 * M * E * d + 2 * MK * 2 * fe * d
+        gu["bytes"] += E * d * e + M * E * 4 + 2 * MK * d * e + act * 2 * fe * d * e + MK * fe * e
+        # experts' down into fp32 rows, the combine
+        dn["flops"] += 2 * MK * d * fe
+        dn["bytes"] += act * d * fe * e + MK * fe * e + 2 * MK * d * 4 + M * d * 4
+    return out
 
 
 PER_CALL = 50  # forwards timed one by one for the median / p10 / p90
@@ -76,10 +91,16 @@ def run_gpu(w, steps, warmup, positions=None):
     import decoder_only_transformer_amd as lbmod
     import workloads
 
-    t = workloads.generate(w)
     cap = (w.capacity + 7) // 8 * 8
     cfg = lbmod.make_config(w.d, w.H, w.n_kv, w.d_head, w.d_ff, w.M, cap, w.theta, w.eps, w.dtype)
-    blk = lbmod.LlamaBlock(cfg, {n: t[n].to("cuda") for n in lbmod.WEIGHT_NAMES})
+    if w.n_experts > 0:
+        # billions of expert weights: drawn on the device
+        g = workloads.generate_stack_on_device(w, 1)
+        t = dict(g["layers"][0], x=g["x"])
+        blk = lbmod.LlamaMoeBlock(cfg, t, w.moe)
+    else:
+        t = workloads.generate(w)
+        blk = lbmod.LlamaBlock(cfg, {n: t[n].to("cuda") for n in lbmod.WEIGHT_NAMES})
     k, v = lbmod.new_kv_cache(w.B, w.n_kv, cap, w.d_head, w.torch_dtype)
     if w.start_pos > 0:
         k[:, :, : w.start_pos, :] = t["k_prefix"].to("cuda")
@@ -141,6 +162,10 @@ def run_gpu(w, steps, warmup, positions=None):
         per_call.update({tag + "median_ms": round(q(0.5), 4), tag + "p10_ms": round(q(0.1), 4),
                          tag + "p90_ms": round(q(0.9), 4)})
     del scratch
+    active = None
+    if w.n_experts > 0:
+        active = int(torch.unique(blk.routing(w.M)[0]).numel())
+        per_call["active_experts"] = active
     blk.close()
     del k, v, x, out
     torch.cuda.empty_cache()
@@ -198,10 +223,10 @@ def run_stack(w, n_layers, steps, warmup):
     return ms_eager, ms_graph
 
 
-def roofline(w, avg_ms, dom, dom_ms, bound, positions=None):
+def roofline(w, avg_ms, dom, dom_ms, bound, positions=None, active_experts=None):
     """Per-stage figures from the all-stage pass; the roofline entry from the
     dominant stage's own timed region."""
-    work = stage_work(w, positions)
+    work = stage_work(w, positions, active_experts)
     stages = {}
     for n, ms in avg_ms.items():
         s = ms * 1e-3
@@ -304,6 +329,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the model-level stack decode")
+    ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts block")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -395,6 +421,32 @@ def main():
             "roofline": rroof, "stages": rstages,
         }
         log(f"[bench] ragged decode {rms * 1e3:.1f} us/step")
+
+    if not args.no_moe:
+        # mixture-of-experts block (shared expert + top-k routed experts)
+        result["moe"] = []
+        for name, bound in (("llama4_moe_prefill", "mfma"), ("llama4_moe_decode", "hbm")):
+            wm = workloads.get(name)
+            msteps = args.steps if bound == "mfma" else 5 * args.steps
+            log(f"[bench] moe {name}: warmup {args.warmup}, steps {msteps}")
+            mms, mavg, mdom, mdom_ms, mms_plain, _, mper = run_gpu(wm, msteps, args.warmup)
+            act = mper.get("active_experts")
+            mroof, mstages = roofline(wm, mavg, mdom, mdom_ms, bound, active_experts=act)
+            work = stage_work(wm, active_experts=act)
+            fl = sum(v["flops"] for v in work.values())
+            by = sum(v["bytes"] for v in work.values())
+            entry = {"workload": name, "B": wm.B, "S": wm.S, "start_pos": wm.start_pos, "n_experts": wm.n_experts,
+                     "top_k": wm.top_k, "d_ff_expert": wm.d_ff_expert, "d_ff_shared": wm.d_ff,
+                     "active_experts": act, "steps": msteps, "ms_per_step": round(mms, 4),
+                     "ms_per_step_without_events": round(mms_plain, 4),
+                     "tokens_per_s": round(wm.M / (mms * 1e-3), 1),
+                     "block_tflops": round(fl / (mms * 1e-3) / 1e12, 2),
+                     "block_mfma_frac": round(fl / (mms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                     "block_gbs": round(by / (mms * 1e-3) / 1e9, 1),
+                     "block_hbm_frac": round(by / (mms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "dominant_stage": mroof, "stages": mstages}
+            result["moe"].append(entry)
+            log(f"[bench] moe {name}: {mms:.3f} ms/step")
 
     if not args.no_stack:
         # model-level decode: every block of the model, then the final norm

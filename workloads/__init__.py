@@ -115,6 +115,17 @@ WORKLOADS: Dict[str, BlockWorkload] = {
     "smollm2_135m_decode_b1": BlockWorkload("smollm2_135m_decode_b1", "bf16", B=1, S=1, start_pos=1023,
                                             d=576, H=9, n_kv=3, d_head=64, d_ff=1536, theta=1e5,
                                             eps=1e-5, w_std=0.02, max_seq=1024),
+    # a mixture-of-experts block at the width of the Llama 4 page's
+    # representative block (d 4096, 32 heads of 128, 8 KV heads): 16 routed
+    # experts, top 1, expert and shared-expert width 8192 (the page gives no
+    # expert counts or widths; these are this library's choice)
+    "llama4_moe_prefill": BlockWorkload("llama4_moe_prefill", "bf16", B=2, S=2048, start_pos=0, d=4096, H=32,
+                                        n_kv=8, d_head=128, d_ff=8192, theta=5e5, eps=1e-5, w_std=0.02,
+                                        g_mean=1.0, g_std=0.05, n_experts=16, top_k=1, d_ff_expert=8192),
+    "llama4_moe_decode": BlockWorkload("llama4_moe_decode", "bf16", B=32, S=1, start_pos=8191, d=4096, H=32,
+                                       n_kv=8, d_head=128, d_ff=8192, theta=5e5, eps=1e-5, w_std=0.02,
+                                       g_mean=1.0, g_std=0.05, cache_std=1.0, max_seq=8192, n_experts=16,
+                                       top_k=1, d_ff_expert=8192),
     "llama3_70b_prefill": BlockWorkload("llama3_70b_prefill", "bf16", B=1, S=4096, start_pos=0,
                                         d=8192, H=64, n_kv=8, d_head=128, d_ff=28672, theta=5e5,
                                         eps=1e-5, w_std=0.01),
@@ -263,5 +274,11 @@ def generate_stack_on_device(w: BlockWorkload, n_layers: int, device="cuda") -> 
             shape = (w.B, w.n_kv, w.start_pos, w.d_head)
             t["k_prefix"] = draw(gen, shape, 0.0, w.cache_std)
             t["v_prefix"] = draw(gen, shape, 0.0, w.cache_std)
+        if w.n_experts > 0:
+            E, fe = w.n_experts, w.d_ff_expert
+            t["router"] = draw(gen, (E, w.d), 0.0, w.w_std)
+            t["e_gate"] = draw(gen, (E, fe, w.d), 0.0, w.w_std)
+            t["e_up"] = draw(gen, (E, fe, w.d), 0.0, w.w_std)
+            t["e_down"] = draw(gen, (E, w.d, fe), 0.0, w.w_std)
         layers.append(t)
     return {"x": x, "final_norm": final, "layers": layers}
