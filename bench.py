@@ -330,6 +330,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the model-level stack decode")
     ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts block")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged decode")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -403,6 +404,7 @@ def main():
         }
         log(f"[bench] decode {dms * 1e3:.1f} us/step")
 
+    if not args.no_decode and not args.no_ragged:
         # the same decode with every sequence at its own position (ragged
         # batch): positions spread evenly from 1024 to the workload's last one
         pos = [1024 + (wd.start_pos - 1024) * b // max(wd.B - 1, 1) for b in range(wd.B)]
