@@ -92,6 +92,21 @@ def test_llama3_70b_prefill_sampled():
     run.close()
 
 
+@pytest.mark.parametrize("B,S,start", [(1, 130, 0), (4, 1, 200)])
+def test_maximum_width_sampled(B, S, start):
+    """d_model 16384, the largest the library takes (the 405B width of "Full
+    Llama 3 transformer block", How it works: 128 heads of 128, 8 KV heads),
+    with a narrow FFN to keep the oracle quick: prefill rows sampled across
+    the 128-row tiles, and a decode of 4 sequences over drawn history.  The
+    norms take the general kernel here (rows wider than 8192)."""
+    w = workloads.BlockWorkload("max_width", "bf16", B=B, S=S, start_pos=start, d=16384, H=128, n_kv=8,
+                                d_head=128, d_ff=1024, theta=5e5, eps=1e-5, w_std=0.01, g_mean=1.0,
+                                g_std=0.05, max_seq=(start + S + 7) // 8 * 8, seed=16)
+    rows = None if S == 1 else sample_rows(w, [0, 1, 64, 127, 128, 129])
+    run, *_ = _check_block(w, rows=rows)
+    run.close()
+
+
 @pytest.mark.parametrize("B,S", [(3, 77), (1, 2), (5, 33)])
 def test_ragged_bf16(B, S):
     w = workloads.with_overrides(workloads.get("smollm2_135m_prefill"), B=B, S=S, seed=B * 100 + S)

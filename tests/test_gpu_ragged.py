@@ -82,6 +82,16 @@ def test_ragged_decode_split_attention():
     _check_ragged(w, pos)
 
 
+def test_ragged_decode_maximum_batch():
+    """64 sequences, the most a ragged call takes, each at its own position
+    from 0 to 250 (four 16-row token tiles in the decode GEMMs)."""
+    pos = [(53 * b) % 251 for b in range(64)]
+    w = workloads.BlockWorkload("ragged_max", "bf16", B=64, S=1, start_pos=max(pos), d=512, H=8,
+                                n_kv=2, d_head=64, d_ff=1024, theta=5e5, eps=1e-5, w_std=0.02,
+                                g_mean=1.0, g_std=0.05, max_seq=256, seed=64)
+    _check_ragged(w, pos)
+
+
 def test_ragged_prefill_chunks_dh64():
     """Prefill chunks of 24 tokens at three offsets, SmolLM2 width (d_head 64,
     three heads per KV group)."""
@@ -139,6 +149,18 @@ def test_ragged_rejects_bad_positions_without_writing():
     run.out.copy_(sentinel)
     k0, v0 = run.kv[0].clone(), run.kv[1].clone()
     bad = {"negative": [0, -1, 3], "past the cache": [0, 15, 3], "wrong count": [0, 1]}
+    # 65 sequences, one over the ragged maximum, on a block and cache that
+    # would take them
+    w65 = workloads.with_overrides(w, B=65, S=1, start_pos=0, max_seq=16)
+    run65 = GpuRun(w65, workloads.generate(w65))
+    o65 = torch.full_like(run65.x, 7.0)
+    with pytest.raises(lbmod.LlamaBlockError) as e:
+        run65.block.forward(run65.x, [0] * 65, run65.kv, o65)
+    log(f"    65 sequences: {e.value}")
+    assert "at most 64" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.all(o65 == 7.0)
+    run65.close()
     for name, pos in bad.items():
         with pytest.raises((lbmod.LlamaBlockError, ValueError)) as e:
             run.block.forward(run.x, pos, run.kv, run.out)
