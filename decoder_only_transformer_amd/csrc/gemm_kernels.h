@@ -8,6 +8,13 @@
 //  gemm_skinny_kernel decode (M <= 64): 16x16x32 MFMA, split-K over waves
 //                     and blocks, weights streamed from HBM straight into
 //                     MFMA operands (+ reduce_epilogue_kernel)
+//
+// The M <= 64 kernels read each weight byte once per call.  With NT their
+// weight loads carry the non-temporal hint (streamed reads of hundreds of MB
+// measured 7.0 TB/s with it against 6.3 TB/s without); the launchers set it
+// for matrices of 8 MB and more, so that the weights of a small model can
+// stay in the 256 MB MALL from one call to the next.  Activations, shared by
+// every block, are read plainly.
 //  gemm_simple_kernel fp32 blocks: plain LDS-tiled fp32 FMA
 #pragma once
 
@@ -409,7 +416,7 @@ __global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
 // reduce_epilogue_kernel adds the KS partials in order (deterministic).
 // K % 32 == 0.
 // ------------------------------------------------------------------------------------
-template <typename T, int MT, int KW, int U, int CT, bool PARTIAL, class Epi>
+template <typename T, int MT, int KW, int U, int CT, bool PARTIAL, class Epi, bool NT = false>
 __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restrict__ A,
                                                               const T* __restrict__ W, int M,
                                                               int N, int K, int KS,
@@ -448,7 +455,7 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
         for (int u = 0; u < U; ++u) {
             const int kstep = min(kfirst + wave + (chunk * U + u) * KW, nks - 1);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) bw[s][u][c] = *reinterpret_cast<const V8*>(wp[c] + kstep * 32);
+            for (int c = 0; c < CT; ++c) bw[s][u][c] = load_w<NT>(reinterpret_cast<const V8*>(wp[c] + kstep * 32));
 #pragma unroll
             for (int t = 0; t < MT; ++t) aa[s][u][t] = *reinterpret_cast<const V8*>(ap[t] + kstep * 32);
         }
@@ -513,7 +520,7 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
 // epilogue on rows < M, otherwise it stores an fp32 partial [ks][M][N] for
 // reduce_epilogue_kernel.  N % (16*CT) == 0, K % 32 == 0.
 // ------------------------------------------------------------------------------------
-template <typename T, int MT, int CT, int U, int NW, bool PARTIAL, class Epi>
+template <typename T, int MT, int CT, int U, int NW, bool PARTIAL, class Epi, bool NT = false>
 __global__ void __launch_bounds__(NW * 64) gemm_decode_kernel(const T* __restrict__ At,
                                                               const T* __restrict__ Wt, int M,
                                                               int N, int K, int KS,
@@ -544,7 +551,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_decode_kernel(const T* __restric
         for (int u = 0; u < U; ++u) {
             const int kstep = min(w0 + chunk * U + u, nks - 1);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) bw[s][u][c] = *reinterpret_cast<const V8*>(wp[c] + (size_t)kstep * 512);
+            for (int c = 0; c < CT; ++c) bw[s][u][c] = load_w<NT>(reinterpret_cast<const V8*>(wp[c] + (size_t)kstep * 512));
 #pragma unroll
             for (int t = 0; t < MT; ++t)
                 aa[s][u][t] = *reinterpret_cast<const V8*>(ap + ((size_t)kstep * MT + t) * 512);
@@ -609,7 +616,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_decode_kernel(const T* __restric
 // wavefront goes through LDS to form the 8-column chunks of the epilogue.
 // Grid N / (16*NW).  N % (16*NW) == 0, K % 32 == 0.
 // ------------------------------------------------------------------------------------
-template <typename T, int MT, int U, int NW, int AC, class Epi>
+template <typename T, int MT, int U, int NW, int AC, class Epi, bool NT = false>
 __global__ void __launch_bounds__(NW * 64) gemm_decode_wide_kernel(const T* __restrict__ At,
                                                                    const T* __restrict__ Wt, int M,
                                                                    int N, int K, Epi epi) {
@@ -639,7 +646,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_decode_wide_kernel(const T* __re
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     V8 bw[U];
-    auto wload = [&](int step, int slot) { bw[slot] = *reinterpret_cast<const V8*>(wp + (size_t)min(step, nks - 1) * 512); };
+    auto wload = [&](int step, int slot) {
+        bw[slot] = load_w<NT>(reinterpret_cast<const V8*>(wp + (size_t)min(step, nks - 1) * 512));
+    };
 #pragma unroll
     for (int u = 0; u < U; ++u) wload(u, u);
     dma_chunk(0);

@@ -482,6 +482,13 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
 // ------------------------------------------------------------------------------------
 template <int N> __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
+// Cache policy of the K/V streams: every cache byte is read once per step, so
+// the loads carry the non-temporal hint (the nt bit, cache-policy value 2 of
+// the direct-to-LDS builtin).  Measured on the 8B decode caches (two 537 MB
+// tensors): 7.0 TB/s for non-temporal grid-stride reads against 6.3 TB/s
+// plain, and 6.5 against 5.7 TB/s in this kernel's own read order.
+constexpr int kNonTemporal = 2;
+
 template <typename T, int DH, int NW, bool DIRECT>
 __global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
     const T* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
@@ -525,13 +532,14 @@ __global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
             const int key = kb0 + 8 * ((lane & 15) >> 2) + 4 * t + (lane & 3);
             const bf16* p = kp + (size_t)min(key, kv_len - 1) * DH + 8 * grp;
 #pragma unroll
-            for (int kk = 0; kk < DH / 32; ++kk) kf[t][kk] = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
+            for (int kk = 0; kk < DH / 32; ++kk)
+                kf[t][kk] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 32 * kk));
         }
 #pragma unroll
         for (int i = 0; i < VLOADS; ++i) {
             const int p = i * 64 + lane, row = p / KCH, pc = p % KCH, ch = pc ^ vswz(row);
             const bf16* src = vp + (size_t)min(kb0 + row, kv_len - 1) * DH + ch * 8;
-            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)(slab + i * 64 * 8), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_ptr)(slab + i * 64 * 8), 16, 0, kNonTemporal);
         }
     };
     // the first step's loads go out before q's, which the first step needs

@@ -9,13 +9,18 @@ size_t skinny_partials_floats(int max_m, int max_n) { return (size_t)kSkinnyMaxS
 
 // Decode GEMM launch: CT column tiles per wavefront, split-K over KS blocks
 // so that a launch has >= ~256 blocks even for narrow outputs.
-template <typename T, int MT, class Epi>
+// Weight matrices from this size up are streamed with the non-temporal hint;
+// smaller ones (a small model's whole weight set fits in the 256 MB MALL)
+// are read plainly so that they can stay there between calls.
+constexpr size_t kStreamMinBytes = size_t(8) << 20;
+
+template <typename T, int MT, bool NT, class Epi>
 static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const Epi& epi,
                              float* part, size_t part_cap, hipStream_t s) {
     if constexpr (MT <= 2) {
         if (N >= 128 * 192) {  // wide outputs: 128 columns per wavefront, no split
             const dim3 grid((N + 127) / 128, 1);
-            gemm_skinny_kernel<T, MT, 8, 1, 8, false, Epi><<<grid, 512, 0, s>>>(A, W, M, N, K, 1, part, epi);
+            gemm_skinny_kernel<T, MT, 8, 1, 8, false, Epi, NT><<<grid, 512, 0, s>>>(A, W, M, N, K, 1, part, epi);
             return hipGetLastError();
         }
     }
@@ -27,10 +32,10 @@ static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const 
     while (ks > 1 && (size_t)ks * M * N > part_cap) --ks;
     const dim3 grid(tiles, ks);
     if (ks == 1) {
-        gemm_skinny_kernel<T, MT, 4, 2, 4, false, Epi><<<grid, 256, 0, s>>>(A, W, M, N, K, 1, part, epi);
+        gemm_skinny_kernel<T, MT, 4, 2, 4, false, Epi, NT><<<grid, 256, 0, s>>>(A, W, M, N, K, 1, part, epi);
         return hipGetLastError();
     }
-    gemm_skinny_kernel<T, MT, 4, 2, 4, true, Epi><<<grid, 256, 0, s>>>(A, W, M, N, K, ks, part, epi);
+    gemm_skinny_kernel<T, MT, 4, 2, 4, true, Epi, NT><<<grid, 256, 0, s>>>(A, W, M, N, K, ks, part, epi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     reduce_epilogue_kernel<Epi><<<(M * (N / 8) + 255) / 256, 256, 0, s>>>(part, M, N, ks, epi);
@@ -46,7 +51,7 @@ int decode_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
 constexpr size_t kSplitMinBytes = size_t(4) << 20;
 
-template <typename T, int MT, class Epi>
+template <typename T, int MT, bool NT, class Epi>
 static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, const Epi& epi,
                                 const SplitWs& ws, hipStream_t s) {
     const int tiles = N / 16, nks = K / 32;
@@ -54,11 +59,11 @@ static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, c
     // activations through LDS
     if (tiles >= 8 * 192 && tiles % 8 == 0) {
         constexpr int AC = MT == 4 ? 8 : 16;
-        gemm_decode_wide_kernel<T, MT, 8, 8, AC, Epi><<<tiles / 8, 512, 0, s>>>(At, Wt, M, N, K, epi);
+        gemm_decode_wide_kernel<T, MT, 8, 8, AC, Epi, NT><<<tiles / 8, 512, 0, s>>>(At, Wt, M, N, K, epi);
         return hipGetLastError();
     }
     if (tiles >= 384 && tiles % 2 == 0) {
-        gemm_decode_kernel<T, MT, 2, 2, 4, false, Epi><<<dim3(tiles / 2, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
+        gemm_decode_kernel<T, MT, 2, 2, 4, false, Epi, NT><<<dim3(tiles / 2, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
         return hipGetLastError();
     }
     // long K at mid widths (the down projection): two column tiles per
@@ -66,7 +71,7 @@ static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, c
     // split keeps one block per CU (measured faster than one split, despite
     // the extra reduction launch, from K = 8192 up)
     if (tiles >= 192 && tiles % 2 == 0 && nks >= 256 && (size_t)2 * M * N <= ws.cap) {
-        gemm_decode_kernel<T, MT, 2, 2, 4, true, Epi><<<dim3(tiles / 2, 2), 256, 0, s>>>(At, Wt, M, N, K, 2, ws.part, epi);
+        gemm_decode_kernel<T, MT, 2, 2, 4, true, Epi, NT><<<dim3(tiles / 2, 2), 256, 0, s>>>(At, Wt, M, N, K, 2, ws.part, epi);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         reduce_epilogue_kernel<Epi><<<(M * (N / 8) + 255) / 256, 256, 0, s>>>(ws.part, M, N, 2, epi);
@@ -84,10 +89,10 @@ static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, c
         if (ks < 1) ks = 1;
     }
     if (ks == 1) {
-        gemm_decode_kernel<T, MT, 1, 4, 4, false, Epi><<<dim3(tiles, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
+        gemm_decode_kernel<T, MT, 1, 4, 4, false, Epi, NT><<<dim3(tiles, 1), 256, 0, s>>>(At, Wt, M, N, K, 1, ws.part, epi);
         return hipGetLastError();
     }
-    gemm_decode_kernel<T, MT, 1, 4, 4, true, Epi><<<dim3(tiles, ks), 256, 0, s>>>(At, Wt, M, N, K, ks, ws.part, epi);
+    gemm_decode_kernel<T, MT, 1, 4, 4, true, Epi, NT><<<dim3(tiles, ks), 256, 0, s>>>(At, Wt, M, N, K, ks, ws.part, epi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     reduce_epilogue_kernel<Epi><<<(M * (N / 8) + 255) / 256, 256, 0, s>>>(ws.part, M, N, ks, epi);
@@ -99,10 +104,14 @@ static hipError_t run_decode(const T* At, const T* Wt, int M, int N, int K, cons
                              const SplitWs& ws, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
     if (M > 64 || N % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
+    const bool nt = (size_t)N * K * sizeof(T) >= kStreamMinBytes;
     switch (decode_row_tiles(M)) {
-        case 1: return run_decode_mt<T, 1>(At, Wt, M, N, K, epi, ws, s);
-        case 2: return run_decode_mt<T, 2>(At, Wt, M, N, K, epi, ws, s);
-        default: return run_decode_mt<T, 4>(At, Wt, M, N, K, epi, ws, s);
+        case 1: return nt ? run_decode_mt<T, 1, true>(At, Wt, M, N, K, epi, ws, s)
+                          : run_decode_mt<T, 1, false>(At, Wt, M, N, K, epi, ws, s);
+        case 2: return nt ? run_decode_mt<T, 2, true>(At, Wt, M, N, K, epi, ws, s)
+                          : run_decode_mt<T, 2, false>(At, Wt, M, N, K, epi, ws, s);
+        default: return nt ? run_decode_mt<T, 4, true>(At, Wt, M, N, K, epi, ws, s)
+                           : run_decode_mt<T, 4, false>(At, Wt, M, N, K, epi, ws, s);
     }
 }
 
@@ -123,9 +132,15 @@ template <typename T, class Epi>
 static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Epi& epi,
                            const SplitWs& ws, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    if (M <= 16) return run_skinny<T, 1>(A, W, M, N, K, epi, ws.part, ws.cap, s);
-    if (M <= 32) return run_skinny<T, 2>(A, W, M, N, K, epi, ws.part, ws.cap, s);
-    if (M <= 64) return run_skinny<T, 4>(A, W, M, N, K, epi, ws.part, ws.cap, s);
+    if (M <= 64) {
+        const bool nt = (size_t)N * K * sizeof(T) >= kStreamMinBytes;
+        if (M <= 16) return nt ? run_skinny<T, 1, true>(A, W, M, N, K, epi, ws.part, ws.cap, s)
+                               : run_skinny<T, 1, false>(A, W, M, N, K, epi, ws.part, ws.cap, s);
+        if (M <= 32) return nt ? run_skinny<T, 2, true>(A, W, M, N, K, epi, ws.part, ws.cap, s)
+                               : run_skinny<T, 2, false>(A, W, M, N, K, epi, ws.part, ws.cap, s);
+        return nt ? run_skinny<T, 4, true>(A, W, M, N, K, epi, ws.part, ws.cap, s)
+                  : run_skinny<T, 4, false>(A, W, M, N, K, epi, ws.part, ws.cap, s);
+    }
     const long tm = (M + 255) / 256, tn = (N + 255) / 256, t256 = tm * tn;
     if (K % 64 == 0 && t256 >= 192) {
         // A CU runs one 256 x 256 tile at a time, so a launch takes

@@ -97,6 +97,14 @@ template <typename T> __device__ __forceinline__ void store4(T* p, const float* 
 // only ever meets a sum that is at least one: softmax weights and SiLU.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A 16-byte operand load, with the non-temporal hint when NT (data read once
+// per call that should not displace reusable lines).
+template <bool NT, typename V>
+__device__ __forceinline__ V load_w(const V* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 // ---- wavefront reductions (64 lanes, fixed butterfly order) ----------------
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
