@@ -40,7 +40,9 @@ namespace lb {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One BM x BN output tile at (m0, n0); lds holds 2 * (BM + BN) * 64 elements.
-template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi>
+// NTW: the W loads carry the non-temporal hint (weights read by one row
+// tile only).
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi, bool NTW = false>
 __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T* __restrict__ W, int M,
                                                int N, int K, Epi epi, int m0, int n0, T* lds) {
     typedef typename vec8<T>::type V8;
@@ -81,7 +83,7 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
 #pragma unroll
         for (int i = 0; i < BCH; ++i)
             __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + k0),
-                                             (lds_ptr_t)(lb + (i * NW + wave) * 64 * 8), 16, 0, 0);
+                                             (lds_ptr_t)(lb + (i * NW + wave) * 64 * 8), 16, 0, NTW ? 2 : 0);
     };
 
     f32x16 acc[TM][TN];
@@ -202,7 +204,7 @@ struct EpiRowOff {
 // blocks take consecutive row tiles of one column tile, so the tiles of a
 // group share its W panel.
 // ------------------------------------------------------------------------------------
-template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi>
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi, bool NTW = false>
 __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restrict__ A,
                                                                const T* __restrict__ W,
                                                                const int* __restrict__ row_off,
@@ -221,7 +223,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restri
         else hi = mid - 1;
     }
     const int r0 = row_off[lo], rows = row_off[lo + 1] - r0;
-    gemm_mfma_tile<T, BM, BN, WM, WN, NW, EpiRowOff<Epi>>(A + (size_t)r0 * K, W + (size_t)lo * N * K, rows, N, K,
+    gemm_mfma_tile<T, BM, BN, WM, WN, NW, EpiRowOff<Epi>, NTW>(A + (size_t)r0 * K, W + (size_t)lo * N * K, rows, N, K,
                                                           EpiRowOff<Epi>{epi, r0}, (tmg - tile_off[lo]) * BM,
                                                           tn * BN, lds);
 }

@@ -230,12 +230,21 @@ static int grouped_tiles_m(int MK, int E) {
     return (MK + kMoeTileM - 1) / kMoeTileM + (E < MK ? E : MK);
 }
 
+// At most one row tile per expert on average (decode-sized calls): each
+// expert's weights are read by one row tile, so they stream non-temporally.
+static bool stream_experts(int MK, int E) { return MK <= E * kMoeTileM; }
+
 template <typename T>
 static hipError_t grouped_swiglu_t(const void* A, const void* W, const int* row_off, const int* tile_off, int E,
                                    int MK, int N, int K, void* z, hipStream_t s) {
     const int tm = grouped_tiles_m(MK, E), tn = (N + 127) / 128;
-    gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiSwiGLU<T>><<<(unsigned)tm * tn, 256, 0, s>>>(
-        (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiSwiGLU<T>{(T*)z, N / 2, 0});
+    const EpiSwiGLU<T> epi{(T*)z, N / 2, 0};
+    if (stream_experts(MK, E))
+        gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiSwiGLU<T>, true><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, epi);
+    else
+        gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiSwiGLU<T>, false><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, epi);
     return hipGetLastError();
 }
 
@@ -252,8 +261,12 @@ template <typename T>
 static hipError_t grouped_down_t(const void* A, const void* W, const int* row_off, const int* tile_off, int E,
                                  int MK, int N, int K, float* r, hipStream_t s) {
     const int tm = grouped_tiles_m(MK, E), tn = (N + 127) / 128;
-    gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiStoreF32><<<(unsigned)tm * tn, 256, 0, s>>>(
-        (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});
+    if (stream_experts(MK, E))
+        gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiStoreF32, true><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});
+    else
+        gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiStoreF32, false><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});
     return hipGetLastError();
 }
 
