@@ -211,7 +211,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restri
                                                                const int* __restrict__ tile_off, int E,
                                                                int N, int K, int tiles_m_max, Epi epi) {
     __shared__ __attribute__((aligned(16))) T lds[2 * (BM + BN) * 64];
-    const int bid = blockIdx.x;
+    // workgroups are dealt round-robin to the 8 XCDs: renumber so that each
+    // XCD runs a contiguous range, whose row tiles of one column tile then
+    // share the expert's weight panel in that XCD's L2
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
     const int tn = bid / tiles_m_max, tmg = bid - tn * tiles_m_max;
     if (tmg >= tile_off[E]) return;
     // the group of this row tile: the last e with tile_off[e] <= tmg (empty
