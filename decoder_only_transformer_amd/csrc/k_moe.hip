@@ -116,10 +116,10 @@ __global__ void __launch_bounds__(256) moe_router_kernel(const T* __restrict__ n
 
 // ---- grouping ------------------------------------------------------------------------
 // One block: counts per expert (LDS atomics give each pair its rank inside its
-// expert), prefix sums into row_off / tile_off, then every pair's sorted row
-// (slot) and every sorted row's pair (src).  The same thread handles pair i in
-// both passes.
-__global__ void __launch_bounds__(1024) moe_route_kernel(const int* __restrict__ sel, int MK, int E,
+// expert), prefix sums into row_off / tile_off (row tiles of tile_m), then
+// every pair's sorted row (slot) and every sorted row's pair (src).  The same
+// thread handles pair i in both passes.
+__global__ void __launch_bounds__(1024) moe_route_kernel(const int* __restrict__ sel, int MK, int E, int tile_m,
                                                          int* __restrict__ row_off, int* __restrict__ tile_off,
                                                          int* __restrict__ src, int* __restrict__ slot) {
     __shared__ int cnt[kMoeMaxExperts];
@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(1024) moe_route_kernel(const int* __restrict__
             row_off[e] = r;
             tile_off[e] = tl;
             r += cnt[e];
-            tl += (cnt[e] + kMoeTileM - 1) / kMoeTileM;
+            tl += (cnt[e] + tile_m - 1) / tile_m;
         }
         row_off[E] = r;
         tile_off[E] = tl;
@@ -209,10 +209,14 @@ hipError_t launch_moe_router(Elem op, const void* n, const void* wr, int M, int 
     return hipGetLastError();
 }
 
+// Row-tile height of the grouped GEMMs: 256-row tiles of the large kernel
+// when the experts average at least one full such tile, else 128-row tiles.
+int moe_tile_m(int MK, int E) { return MK >= 256 * E ? 256 : kMoeTileM; }
+
 hipError_t launch_moe_route(const int* sel, int MK, int E, int* row_off, int* tile_off, int* src, int* slot,
                             hipStream_t s) {
     if (E < 1 || E > kMoeMaxExperts || MK < 0) return hipErrorInvalidValue;
-    moe_route_kernel<<<1, 1024, 0, s>>>(sel, MK, E, row_off, tile_off, src, slot);
+    moe_route_kernel<<<1, 1024, 0, s>>>(sel, MK, E, moe_tile_m(MK, E), row_off, tile_off, src, slot);
     return hipGetLastError();
 }
 
@@ -226,8 +230,8 @@ hipError_t launch_moe_gather(Elem op, const void* n, const int* src, int MK, int
 
 // Row-tile bound of the grouped GEMMs over MK sorted rows and E experts: each
 // expert's last tile is the only partial one.
-static int grouped_tiles_m(int MK, int E) {
-    return (MK + kMoeTileM - 1) / kMoeTileM + (E < MK ? E : MK);
+static int grouped_tiles_m(int MK, int E, int tile_m) {
+    return (MK + tile_m - 1) / tile_m + (E < MK ? E : MK);
 }
 
 // At most one row tile per expert on average (decode-sized calls): each
@@ -237,8 +241,14 @@ static bool stream_experts(int MK, int E) { return MK <= E * kMoeTileM; }
 template <typename T>
 static hipError_t grouped_swiglu_t(const void* A, const void* W, const int* row_off, const int* tile_off, int E,
                                    int MK, int N, int K, void* z, hipStream_t s) {
-    const int tm = grouped_tiles_m(MK, E), tn = (N + 127) / 128;
     const EpiSwiGLU<T> epi{(T*)z, N / 2, 0};
+    if (moe_tile_m(MK, E) == 256) {
+        const int tm = grouped_tiles_m(MK, E, 256), tn = (N + 255) / 256;
+        gemm_big_grouped_kernel<T, 256, 256, EpiSwiGLU<T>><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, epi);
+        return hipGetLastError();
+    }
+    const int tm = grouped_tiles_m(MK, E, kMoeTileM), tn = (N + 127) / 128;
     if (stream_experts(MK, E))
         gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiSwiGLU<T>, true><<<(unsigned)tm * tn, 256, 0, s>>>(
             (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, epi);
@@ -260,7 +270,13 @@ hipError_t launch_moe_grouped_swiglu(Elem op, const void* A, const void* W, cons
 template <typename T>
 static hipError_t grouped_down_t(const void* A, const void* W, const int* row_off, const int* tile_off, int E,
                                  int MK, int N, int K, float* r, hipStream_t s) {
-    const int tm = grouped_tiles_m(MK, E), tn = (N + 127) / 128;
+    if (moe_tile_m(MK, E) == 256) {
+        const int tm = grouped_tiles_m(MK, E, 256), tn = (N + 255) / 256;
+        gemm_big_grouped_kernel<T, 256, 256, EpiStoreF32><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});
+        return hipGetLastError();
+    }
+    const int tm = grouped_tiles_m(MK, E, kMoeTileM), tn = (N + 127) / 128;
     if (stream_experts(MK, E))
         gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiStoreF32, true><<<(unsigned)tm * tn, 256, 0, s>>>(
             (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});

@@ -154,6 +154,15 @@ def test_moe_large_groups():
     check_moe(_small(name="moe_large", B=2, S=300, n_experts=4, top_k=1, d_ff_expert=1024, seed=12))
 
 
+@pytest.mark.parametrize("E,k", [(2, 1), (4, 2)])
+def test_moe_256_row_tiles(E, k):
+    """600 tokens with at least 256 (token, choice) pairs per expert on
+    average: the experts run on the 256 x 256 grouped kernel, each group one
+    full tile plus a partial one."""
+    check_moe(_small(name=f"moe_big_tiles_{E}_{k}", B=2, S=300, n_experts=E, top_k=k, d_ff_expert=512,
+                     seed=20 + E))
+
+
 def test_moe_llama3_width_sampled():
     """The 8B-width attention with a MoE FFN (8 experts of width 4096, top 2,
     shared expert 4096) over 2 x 256 tokens; rows sampled at the ends of each
