@@ -10,9 +10,12 @@ size_t skinny_partials_floats(int max_m, int max_n) { return (size_t)kSkinnyMaxS
 // Decode GEMM launch: CT column tiles per wavefront, split-K over KS blocks
 // so that a launch has >= ~256 blocks even for narrow outputs.
 // Weight matrices from this size up are streamed with the non-temporal hint;
-// smaller ones (a small model's whole weight set fits in the 256 MB MALL)
-// are read plainly so that they can stay there between calls.
-constexpr size_t kStreamMinBytes = size_t(8) << 20;
+// smaller ones are read plainly.  Measured at 32 tokens with every call on
+// fresh weights: the hint wins from the 50 MB q/k/v matrix up (13.4 against
+// 13.7 us; down 24.4 against 25.3; gate/up 40 against 45) and loses on the
+// 34 MB o matrix (11.1 against 10.0 us); a small model's whole weight set
+// fits in the 256 MB MALL, where plain loads let it stay between calls.
+constexpr size_t kStreamMinBytes = size_t(40) << 20;
 
 template <typename T, int MT, bool NT, class Epi>
 static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const Epi& epi,
@@ -58,8 +61,11 @@ static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, c
     // very wide outputs (gate/up): blocks of 8 column tiles sharing the
     // activations through LDS
     if (tiles >= 8 * 192 && tiles % 8 == 0) {
-        constexpr int AC = MT == 4 ? 8 : 16;
-        gemm_decode_wide_kernel<T, MT, 8, 8, AC, Epi, NT><<<tiles / 8, 512, 0, s>>>(At, Wt, M, N, K, epi);
+        // k-steps in flight per wavefront and activation k-steps per LDS
+        // refill (measured at 32 tokens: U 4 with AC 16, 39.4 us, against
+        // 40.2 with U 8)
+        constexpr int AC = MT == 4 ? 8 : 16, U = MT == 4 ? 8 : 4;
+        gemm_decode_wide_kernel<T, MT, U, 8, AC, Epi, NT><<<tiles / 8, 512, 0, s>>>(At, Wt, M, N, K, epi);
         return hipGetLastError();
     }
     if (tiles >= 384 && tiles % 2 == 0) {
