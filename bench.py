@@ -405,6 +405,21 @@ def main():
         log(f"[bench] decode {dms * 1e3:.1f} us/step")
 
     if not args.no_decode and not args.no_ragged:
+        # one sequence: the per-token latency case
+        wb = workloads.get("llama3_8b_decode_b1")
+        log(f"[bench] decode {wb.name}: warmup {args.warmup}, steps {dsteps}")
+        bms, bavg, bdom, bdom_ms, bms_plain, _, bper = run_gpu(wb, dsteps, args.warmup)
+        broof, bstages = roofline(wb, bavg, bdom, bdom_ms, "hbm")
+        bbytes = sum(v["bytes"] for v in stage_work(wb).values())
+        result["decode_b1"] = {
+            "workload": wb.name, "B": wb.B, "start_pos": wb.start_pos, "steps": dsteps,
+            "us_per_step": round(bms * 1e3, 2), "us_per_step_without_events": round(bms_plain * 1e3, 2),
+            "block_gbs": round(bbytes / (bms * 1e-3) / 1e9, 1),
+            "block_hbm_frac": round(bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "dominant_stage": broof, "stages": bstages, "per_call": bper,
+        }
+        log(f"[bench] decode one sequence {bms * 1e3:.1f} us/step")
+
         # the same decode with every sequence at its own position (ragged
         # batch): positions spread evenly from 1024 to the workload's last one
         pos = [1024 + (wd.start_pos - 1024) * b // max(wd.B - 1, 1) for b in range(wd.B)]

@@ -126,6 +126,11 @@ WORKLOADS: Dict[str, BlockWorkload] = {
                                        n_kv=8, d_head=128, d_ff=8192, theta=5e5, eps=1e-5, w_std=0.02,
                                        g_mean=1.0, g_std=0.05, cache_std=1.0, max_seq=8192, n_experts=16,
                                        top_k=1, d_ff_expert=8192),
+    # one sequence decoding at the end of the 8B context: the per-token
+    # latency case, bound by streaming the block's 436 MB of weights
+    "llama3_8b_decode_b1": BlockWorkload("llama3_8b_decode_b1", "bf16", B=1, S=1, start_pos=8191, d=4096,
+                                         H=32, n_kv=8, d_head=128, d_ff=14336, theta=5e5, eps=1e-5,
+                                         w_std=0.02, g_mean=1.0, g_std=0.05, cache_std=1.0, max_seq=8192),
     "llama3_70b_prefill": BlockWorkload("llama3_70b_prefill", "bf16", B=1, S=4096, start_pos=0,
                                         d=8192, H=64, n_kv=8, d_head=128, d_ff=28672, theta=5e5,
                                         eps=1e-5, w_std=0.01),
