@@ -53,7 +53,7 @@ typedef enum { LB_OPERANDS_AUTO = 0, LB_OPERANDS_F16 = 1, LB_OPERANDS_BF16 = 2 }
 typedef enum {
     LB_OK = 0,
     LB_ERR_INVALID_ARG = 1,  /* a pointer, size or config value is invalid */
-    LB_ERR_UNSUPPORTED = 2,  /* valid, but a shape this build does not run */
+    LB_ERR_UNSUPPORTED = 2,  /* valid, but a shape this library does not run */
     LB_ERR_OOM = 3,          /* device allocation failed */
     LB_ERR_HIP = 4           /* a HIP runtime call failed */
 } lb_status;

@@ -46,7 +46,7 @@ def gpu_cache(w: workloads.BlockWorkload, tensors: Dict[str, torch.Tensor], fill
     return k, v
 
 
-class GpuRun:
+class BlockOnGpu:
     def __init__(self, w, tensors, operands="auto", max_tokens=None, fill=0.0, cap=None,
                  max_seq_len=None):
         self.w = w

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads
-from block_harness import (GpuRun, gpu_cache_rows, log, oracle_rows, rel_err, sample_rows,
+from block_harness import (BlockOnGpu, gpu_cache_rows, log, oracle_rows, rel_err, sample_rows,
                            tol_of)
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +24,7 @@ def _check_block(w, rows=None, operands="auto", stages=False, tol=None, fill=0.0
         f"n_kv={w.n_kv} dh={w.d_head} dff={w.d_ff} dtype={w.dtype} operands={operands} "
         f"rows={'all' if rows is None else len(rows)}")
     t = workloads.generate(w)
-    run = GpuRun(w, t, operands=operands, fill=fill)
+    run = BlockOnGpu(w, t, operands=operands, fill=fill)
     y_gpu = run.forward().double().cpu().numpy().reshape(w.M, w.d)
     y_orc, kc, vc, st = oracle_rows(w, t, rows=rows, stages=stages)
     y_orc = y_orc.reshape(w.M, w.d)
@@ -250,7 +250,7 @@ def test_decode_token_by_token_matches_prefill():
     base = workloads.with_overrides(workloads.get("smollm2_135m_prefill"), B=2, S=48, seed=9)
     log(f"[case] decode-after-prefill {base}")
     t = workloads.generate(base)
-    run = GpuRun(base, t, max_tokens=base.M, cap=48)
+    run = BlockOnGpu(base, t, max_tokens=base.M, cap=48)
     x = run.x
     o40 = torch.empty_like(x[:, :40].contiguous())
     run.forward(x=x[:, :40].contiguous(), start_pos=0, out=o40)
@@ -273,7 +273,7 @@ def test_cache_rows_outside_window_untouched():
                                  max_seq=64, seed=4)
     log(f"[case] canaries {w}")
     t = workloads.generate(w)
-    run = GpuRun(w, t, fill=float("nan"))
+    run = BlockOnGpu(w, t, fill=float("nan"))
     # prefix rows are real values; everything past start_pos+S stays NaN
     run.forward()
     k, v = run.kv
@@ -288,7 +288,7 @@ def test_deterministic_bitwise():
     w = workloads.with_overrides(workloads.get("smollm2_135m_prefill"), B=2, S=130, seed=2)
     log(f"[case] determinism {w}")
     t = workloads.generate(w)
-    run = GpuRun(w, t)
+    run = BlockOnGpu(w, t)
     a = run.forward().clone()
     b = run.forward().clone()
     assert torch.equal(a, b)
@@ -317,7 +317,7 @@ def test_bf16_operands_at_8b_width_lose_to_fp16():
     y_orc = y_orc.reshape(w.M, w.d)[rows]
     errs = {}
     for operands in ("auto", "bf16"):
-        run = GpuRun(w, t, operands=operands)
+        run = BlockOnGpu(w, t, operands=operands)
         y = run.forward().double().cpu().numpy().reshape(w.M, w.d)[rows]
         errs[operands] = rel_err(y, y_orc)
         log(f"    8B prefill operands={operands}: max|err|/rms = {errs[operands]:.3e}")
@@ -332,7 +332,7 @@ def test_forward_rejects_bad_arguments_without_writing():
     w = workloads.with_overrides(workloads.get("tiny_f32"), B=1, S=8)
     log("[case] argument checks")
     t = workloads.generate(w)
-    run = GpuRun(w, t, cap=8)
+    run = BlockOnGpu(w, t, cap=8)
     sentinel = torch.full_like(run.x, 7.0)
     with pytest.raises(lbmod.LlamaBlockError) as ei:
         run.block.forward(run.x, 1, run.kv, sentinel)  # 1 + 8 > capacity 8

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads
-from block_harness import GpuRun, gpu_cache_rows, log, oracle_rows, rel_err, tol_of
+from block_harness import BlockOnGpu, gpu_cache_rows, log, oracle_rows, rel_err, tol_of
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def _check_ragged(w, positions, operands="auto"):
     log(f"[case] ragged {w.name} B={w.B} S={w.S} positions={list(positions)} d={w.d} H={w.H} "
         f"n_kv={w.n_kv} dh={w.d_head} dtype={w.dtype} operands={operands}")
     t = workloads.generate(w)
-    run = GpuRun(w, t, operands=operands)
+    run = BlockOnGpu(w, t, operands=operands)
     k0 = run.kv[0].clone()
     v0 = run.kv[1].clone()
     y = run.forward(start_pos=list(positions)).double().cpu().numpy().reshape(w.B, w.S, w.d)
@@ -128,8 +128,8 @@ def test_ragged_with_equal_positions_is_the_uniform_forward(S):
                                 n_kv=2, d_head=64, d_ff=1024, theta=5e5, eps=1e-5, w_std=0.02,
                                 g_mean=1.0, g_std=0.05, max_seq=64, seed=21)
     t = workloads.generate(w)
-    a = GpuRun(w, t)
-    b = GpuRun(w, t)
+    a = BlockOnGpu(w, t)
+    b = BlockOnGpu(w, t)
     ya = a.forward(start_pos=w.start_pos).clone()
     yb = b.forward(start_pos=[w.start_pos] * w.B).clone()
     assert torch.equal(ya, yb)
@@ -144,7 +144,7 @@ def test_ragged_rejects_bad_positions_without_writing():
                                 d_head=64, d_ff=1024, theta=5e5, eps=1e-5, w_std=0.02, g_mean=1.0,
                                 g_std=0.05, max_seq=16, seed=1)
     t = workloads.generate(w)
-    run = GpuRun(w, t)
+    run = BlockOnGpu(w, t)
     sentinel = torch.full_like(run.x, 7.0)
     run.out.copy_(sentinel)
     k0, v0 = run.kv[0].clone(), run.kv[1].clone()
@@ -152,7 +152,7 @@ def test_ragged_rejects_bad_positions_without_writing():
     # 65 sequences, one over the ragged maximum, on a block and cache that
     # would take them
     w65 = workloads.with_overrides(w, B=65, S=1, start_pos=0, max_seq=16)
-    run65 = GpuRun(w65, workloads.generate(w65))
+    run65 = BlockOnGpu(w65, workloads.generate(w65))
     o65 = torch.full_like(run65.x, 7.0)
     with pytest.raises(lbmod.LlamaBlockError) as e:
         run65.block.forward(run65.x, [0] * 65, run65.kv, o65)
