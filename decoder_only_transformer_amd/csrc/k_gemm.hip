@@ -1,4 +1,6 @@
 // GEMM dispatch for the four projections of the block.
+#include <atomic>
+
 #include "epilogues.h"
 #include "gemm_kernels.h"
 #include "launch.h"
@@ -121,17 +123,18 @@ static hipError_t run_decode(const T* At, const T* Wt, int M, int N, int K, cons
     }
 }
 
-// compute units of the current device, cached per device
+// compute units of the current device, cached per device (threads that race
+// to fill an entry store the same value)
 static int device_cus() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <typename T, class Epi>
