@@ -521,12 +521,18 @@ __global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
     const int k_begin = (split * NW + wave) * CH;
     int nsteps = (kv_len - k_begin + 31) / 32;
     nsteps = nsteps < 0 ? 0 : (nsteps > CH / 32 ? CH / 32 : nsteps);
+    // Each wavefront walks its steps from its own starting step, wrapping
+    // around (the online softmax takes the keys in any order): with every
+    // stream at the same offset of its region the reads measured 6.6 TB/s,
+    // with the start rotated by block and by wavefront 7.0 TB/s.
+    const int rot = nsteps > 0 ? (7 * (int)(blockIdx.y * gridDim.x + blockIdx.x) + 3 * wave) % nsteps : 0;
+    auto key0 = [&](int st) { return k_begin + 32 * (st + rot < nsteps ? st + rot : st + rot - nsteps); };
     bf16x8 kf[2][DH / 32];
     // K operands of step st into kf; V rows of step st into slab (rows past
     // kv_len repeat the last valid row: finite values that meet zero
     // probabilities)
     auto issue = [&](int st, bf16* slab) {
-        const int kb0 = k_begin + 32 * st;
+        const int kb0 = key0(st);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int key = kb0 + 8 * ((lane & 15) >> 2) + 4 * t + (lane & 3);
@@ -572,7 +578,7 @@ __global__ void __launch_bounds__(NW * 64) attn_decode_kernel(
 
     // one 32-key step whose V rows are in cur; the next step goes to nxt
     auto step = [&](int st, const bf16* cur, bf16* nxt) {
-        const int kb0 = k_begin + 32 * st;
+        const int kb0 = key0(st);
         f32x4 sc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
