@@ -174,6 +174,15 @@ def test_moe_llama3_width_sampled():
     check_moe(w, rows=rows)
 
 
+def test_moe_benchmark_shape_sampled():
+    """The benchmark's MoE prefill shape and launch path (16 experts of 8192,
+    top 1, shared expert 8192, d 4096, 2 x 2048 tokens: 256-row grouped
+    tiles), rows sampled at both ends of each sequence and across tiles."""
+    w = workloads.get("llama4_moe_prefill")
+    rows = sorted({b * w.S + s for b in range(w.B) for s in (0, 1, 255, 256, 1023, 2047)})
+    check_moe(w, rows=rows)
+
+
 def test_moe_zero_router_takes_the_first_experts():
     """A zero router scores every expert 0: the library takes experts 0 and 1,
     each weighted 1/2, exactly as the tie rule says."""
