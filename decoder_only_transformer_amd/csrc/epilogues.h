@@ -2,6 +2,14 @@
 // an epilogue in chunks of 8 consecutive output columns of one token row:
 // row8(m, n, v) with n % 8 == 0.  The epilogue owns the fusion that follows
 // the product and the stores.
+//
+// What an epilogue reads from memory besides the product (a residual) it
+// can fetch ahead: load(m, n, aux) fills an Aux for the chunk,
+// row8(m, n, v, aux) finishes it.  The tiled GEMMs issue the loads of all of
+// a thread's chunks of an epilogue pass first and then finish them, so the
+// loads overlap one another; the compiler cannot do that reordering itself,
+// since the stores of one chunk might alias the loads of the next.
+// row8(m, n, v) is load and finish of one chunk.
 #pragma once
 
 #include "lb_device.h"
@@ -45,6 +53,11 @@ struct EpiQKV {
         store4(head + j / 2 + dh / 2, hi);
     }
 
+    // RoPE angles are read in the finishing step: fetching them ahead for a
+    // whole pass measured slower (the registers outweigh the overlap).
+    struct Aux {};
+    __device__ __forceinline__ void load(int, int, Aux&) const {}
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8], const Aux&) const { row8(m, n, v); }
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
         const int b = m / S, s = m - b * S, pos = LB_SEQ_START(sp, b) + s;
         const int kvd = nkv * dh;
@@ -82,12 +95,19 @@ struct EpiResid {
     const TR* resid;  // [M][N]
     float* out;       // [M][N]
     int N;
-    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+    using Aux = Raw8<TR>;
+    __device__ __forceinline__ void load(int m, int n, Aux& a) const { fetch8(resid + (size_t)m * N + n, a); }
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8], const Aux& a) const {
         float r[8];
-        load8(resid + (size_t)m * N + n, r);
+        widen8(a, r);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = r[e] + v[e];
         store8(out + (size_t)m * N + n, v);
+    }
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+        Aux a;
+        load(m, n, a);
+        row8(m, n, v, a);
     }
 };
 
@@ -100,6 +120,9 @@ struct EpiSwiGLU {
     TO* z;    // [M][dff], or k-step tiled with mt row tiles when mt > 0
     int dff;
     int mt;
+    struct Aux {};
+    __device__ __forceinline__ void load(int, int, Aux&) const {}
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8], const Aux&) const { row8(m, n, v); }
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
         float r[4];
 #pragma unroll
@@ -119,12 +142,19 @@ struct EpiOut {
     const float* h;  // [M][N]
     TY* y;           // [M][N]
     int N;
-    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+    using Aux = Raw8<float>;
+    __device__ __forceinline__ void load(int m, int n, Aux& a) const { fetch8(h + (size_t)m * N + n, a); }
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8], const Aux& a) const {
         float r[8];
-        load8(h + (size_t)m * N + n, r);
+        widen8(a, r);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = r[e] + v[e];
         store8(y + (size_t)m * N + n, v);
+    }
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const {
+        Aux a;
+        load(m, n, a);
+        row8(m, n, v, a);
     }
 };
 
@@ -134,6 +164,9 @@ template <class Epi>
 struct EpiShift {
     Epi e;
     int n_off;
+    using Aux = typename Epi::Aux;
+    __device__ __forceinline__ void load(int m, int n, Aux& a) const { e.load(m, n + n_off, a); }
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8], const Aux& a) const { e.row8(m, n + n_off, v, a); }
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const { e.row8(m, n + n_off, v); }
 };
 

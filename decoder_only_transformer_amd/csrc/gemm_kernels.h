@@ -12,15 +12,69 @@
 // The M <= 64 kernels read each weight byte once per call.  With NT their
 // weight loads carry the non-temporal hint (streamed reads of hundreds of MB
 // measured 7.0 TB/s with it against 6.3 TB/s without); the launchers set it
-// for matrices of 8 MB and more, so that the weights of a small model can
+// for matrices of 40 MB and more, so that the weights of a small model can
 // stay in the 256 MB MALL from one call to the next.  Activations, shared by
 // every block, are read plainly.
 //  gemm_simple_kernel fp32 blocks: plain LDS-tiled fp32 FMA
 #pragma once
 
+#include <type_traits>
+
 #include "lb_device.h"
 
 namespace lb {
+
+// One epilogue pass of a tiled GEMM: rows [mp, mp + EPR) x columns
+// [n0, n0 + BN) of the tile, staged in LDS (row stride CPAD floats), handed
+// to the epilogue as 8-column chunks, chunk c = tid + i * NT of the pass to
+// thread tid.  When the epilogue reads memory (a non-empty Aux), fetch()
+// issues those loads for all of the thread's chunks before the staging, so
+// that they overlap one another and it; the loads are not predicated (a
+// branch would keep each load's wait beside it): a chunk past the tile's edge
+// loads the last chunk inside it, unused.  Epilogues that read nothing run
+// the plain strided loop.
+template <class Epi, int EPR, int BN, int NT, int CPAD>
+struct EpiPass {
+    static constexpr int IT = EPR * (BN / 8) / NT;
+    static_assert(IT * NT == EPR * (BN / 8), "whole chunks per thread");
+    static constexpr bool kReads = !std::is_empty<typename Epi::Aux>::value;
+    typename Epi::Aux aux[kReads ? IT : 1];
+
+    __device__ __forceinline__ void fetch(const Epi& epi, int tid, int mp, int n0, int M, int N) {
+        if constexpr (kReads) {
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int c = tid + it * NT, row = c / (BN / 8), c8 = c % (BN / 8);
+                epi.load(min(mp + row, M - 1), min(n0 + c8 * 8, N - 8), aux[it]);
+            }
+        }
+    }
+    __device__ __forceinline__ static void chunk(const Epi& epi, const float* cst, int c, int mp, int n0, int M,
+                                                 int N, const typename Epi::Aux& a) {
+        const int row = c / (BN / 8), c8 = c % (BN / 8);
+        const int m = mp + row, n = n0 + c8 * 8;
+        if (m < M && n < N) {
+            float v[8];
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = lo[e];
+                v[4 + e] = hi[e];
+            }
+            epi.row8(m, n, v, a);
+        }
+    }
+    __device__ __forceinline__ void finish(const Epi& epi, const float* cst, int tid, int mp, int n0, int M,
+                                           int N) const {
+        if constexpr (kReads) {
+#pragma unroll
+            for (int it = 0; it < IT; ++it) chunk(epi, cst, tid + it * NT, mp, n0, M, N, aux[it]);
+        } else {
+            for (int c = tid; c < EPR * (BN / 8); c += NT) chunk(epi, cst, c, mp, n0, M, N, aux[0]);
+        }
+    }
+};
 
 // ------------------------------------------------------------------------------------
 // Prefill GEMM.  Block tile BM x BN x 64, NW wavefronts in a (BM/WM) x (BN/WN)
@@ -131,6 +185,8 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
     float* cst = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int p = 0; p < BM / EPR; ++p) {
+        EpiPass<Epi, EPR, BN, NT, CPAD> pass;
+        pass.fetch(epi, tid, m0 + p * EPR, n0, M, N);
         if (wm == (p * EPR) / WM) {
             constexpr int IPP = EPR / 32;
 #pragma unroll
@@ -147,18 +203,7 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
             }
         }
         __syncthreads();
-        for (int c = tid; c < EPR * (BN / 8); c += NT) {
-            const int row = c / (BN / 8), c8 = c % (BN / 8);
-            const int m = m0 + p * EPR + row, n = n0 + c8 * 8;
-            if (m < M && n < N) {
-                float v[8];
-                const f32x4 a = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8 + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
-                epi.row8(m, n, v);
-            }
-        }
+        pass.finish(epi, cst, tid, m0 + p * EPR, n0, M, N);
         __syncthreads();
     }
 }
@@ -191,6 +236,9 @@ template <class Epi>
 struct EpiRowOff {
     Epi e;
     int m_off;
+    using Aux = typename Epi::Aux;
+    __device__ __forceinline__ void load(int m, int n, Aux& a) const { e.load(m + m_off, n, a); }
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8], const Aux& a) const { e.row8(m + m_off, n, v, a); }
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const { e.row8(m + m_off, n, v); }
 };
 
@@ -370,6 +418,8 @@ __device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* 
     float* cst = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int p = 0; p < BM / EPR; ++p) {
+        EpiPass<Epi, EPR, BN, NT, CPAD> pass;
+        pass.fetch(epi, tid, m0 + p * EPR, n0, M, N);
         if (wm == (p * EPR) / WM) {
 #pragma unroll
             for (int ii = 0; ii < EPR / 16; ++ii) {
@@ -382,21 +432,7 @@ __device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* 
             }
         }
         __syncthreads();
-        for (int c = tid; c < EPR * (BN / 8); c += NT) {
-            const int row = c / (BN / 8), c8 = c % (BN / 8);
-            const int m = m0 + p * EPR + row, n = n0 + c8 * 8;
-            if (m < M && n < N) {
-                float v[8];
-                const f32x4 a = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(cst + row * CPAD + c8 * 8 + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] = a[e];
-                    v[4 + e] = b[e];
-                }
-                epi.row8(m, n, v);
-            }
-        }
+        pass.finish(epi, cst, tid, m0 + p * EPR, n0, M, N);
         __syncthreads();
     }
 }

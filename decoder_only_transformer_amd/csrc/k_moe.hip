@@ -190,6 +190,9 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(const float* __restric
 struct EpiStoreF32 {
     float* out;
     int N;
+    struct Aux {};
+    __device__ __forceinline__ void load(int, int, Aux&) const {}
+    __device__ __forceinline__ void row8(int m, int n, float (&v)[8], const Aux&) const { row8(m, n, v); }
     __device__ __forceinline__ void row8(int m, int n, float (&v)[8]) const { store8(out + (size_t)m * N + n, v); }
 };
 

@@ -66,6 +66,28 @@ __device__ __forceinline__ void load8(const bf16* p, float (&v)[8]) {
     for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
 }
 
+// The same loads split in two: fetch8 issues the access into a Raw8 holding
+// the stored type, widen8 converts it once the data is needed, so that several
+// fetches can be in flight before the first conversion waits on one.
+template <typename T> struct Raw8;
+template <> struct Raw8<float> { f32x4 a, b; };
+template <> struct Raw8<f16> { f16x8 a; };
+template <> struct Raw8<bf16> { bf16x8 a; };
+__device__ __forceinline__ void fetch8(const float* p, Raw8<float>& r) {
+    r.a = *reinterpret_cast<const f32x4*>(p);
+    r.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void fetch8(const f16* p, Raw8<f16>& r) { r.a = *reinterpret_cast<const f16x8*>(p); }
+__device__ __forceinline__ void fetch8(const bf16* p, Raw8<bf16>& r) { r.a = *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void widen8(const Raw8<float>& r, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = r.a[i]; v[4 + i] = r.b[i]; }
+}
+template <typename T> __device__ __forceinline__ void widen8(const Raw8<T>& r, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)r.a[i];
+}
+
 __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
     f32x4 a, b;
 #pragma unroll
