@@ -80,6 +80,17 @@ def test_llama3_8b_prefill_sampled():
     run.close()
 
 
+def test_llama3_8b_width_ragged_rows_sampled():
+    """8B width with 4000 token rows: the last row tile of every prefill GEMM
+    is partial (160 of 256 rows), among them the 256 x 256 tiles of o and
+    down, whose epilogues fetch the residual rows of the partial tile clamped.
+    A narrow FFN keeps the oracle quick."""
+    w = workloads.with_overrides(workloads.get("llama3_8b_prefill"), B=1, S=4000, d_ff=1024, seed=21)
+    rows = sample_rows(w, [0, 191, 192, 3839, 3840, 3903, 3999])
+    run, *_ = _check_block(w, rows=rows)
+    run.close()
+
+
 def test_llama3_8b_decode_full():
     run, *_ = _check_block(workloads.get("llama3_8b_decode"))
     run.close()
