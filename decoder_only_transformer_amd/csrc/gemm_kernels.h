@@ -323,24 +323,28 @@ __device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     // load d of a stage: instruction (d % NA or d - NA) of this wavefront fills
-    // 64 consecutive 16-byte slots; lane l the slot l
-    const T* gsrc[ND];
-    unsigned ldst[ND];
+    // 64 consecutive 16-byte slots; lane l the slot l.  Addresses are the
+    // tile's first A (or W) row, wave-uniform, plus a per-lane byte offset
+    // (below 256 rows x K elements, far inside 32 bits for any K taken)
+    unsigned voff[ND], ldst[ND];
     const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)lds;
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
         const bool isa = d < NA;
         const int slot0 = ((isa ? d : d - NA) * NW + wave) * 64;
         const int p = slot0 + lane, row = p >> 2, c = (p & 3) ^ ((row >> 1) & 3);
-        gsrc[d] = isa ? A + (size_t)min(m0 + row, M - 1) * K + c * 8
-                      : W + (size_t)min(n0 + row, N - 1) * K + c * 8;
+        const int r = isa ? min(m0 + row, M - 1) - m0 : min(n0 + row, N - 1) - n0;
+        voff[d] = (unsigned)(((size_t)r * K + c * 8) * sizeof(T));
         ldst[d] = lds0 + (unsigned)(((isa ? 0 : SA) + slot0 * 8) * (int)sizeof(T));
     }
+    const T* abase = A + (size_t)m0 * K;
+    const T* wbase = W + (size_t)n0 * K;
     const int nk = K / BK;
     // k-steps past the end reload the last one into a stage nobody reads
     auto dma = [&](int kstep, int d) {
         const int ks = kstep < nk ? kstep : nk - 1;
-        lds_dma16(gsrc[d] + ks * BK, ldst[d] + (unsigned)((kstep % STAGES) * STG * (int)sizeof(T)));
+        lds_dma16_s((d < NA ? abase : wbase) + ks * BK, voff[d],
+                    ldst[d] + (unsigned)((kstep % STAGES) * STG * (int)sizeof(T)));
     };
     f32x4 acc[TI][TJ];
 #pragma unroll
