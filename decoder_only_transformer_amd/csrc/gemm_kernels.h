@@ -290,10 +290,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restri
 // SIMD).  A four-stage
 // LDS ring is filled by direct-to-LDS loads issued from inline assembly (so
 // the compiler's counters for LDS reads stay exact; the kernel waits for
-// the loads itself).  Each k-step runs its MFMAs in two halves with the one
-// barrier of the step between them: after it, stage k+1 is complete for
-// every wavefront and the second half reads the next step's operands under
-// its MFMAs; the loads of stage k+3 are spread over both halves.  LDS rows
+// the loads itself).  One barrier opens each k-step: after it, stage k+1 is
+// complete for every wavefront, and the step's eight MFMA groups each take
+// one A row and about one B fragment of stage k+1 and one load of stage k+3
+// (A single-buffered in registers, B double-buffered).  LDS rows
 // are 64 bytes (4 chunks) with chunk index XORed by (row / 2) & 3, the
 // pattern measured free of bank conflicts for this operand read (16 rows at
 // each of the 4 chunks of a 64-byte row per instruction).
@@ -313,7 +313,7 @@ __device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* 
     constexpr int TI = WM / 16, TJ = WN / 16;
     constexpr int SA = BM * BK, SB = BN * BK, STG = SA + SB;  // elements per stage
     constexpr int NA = BM * BK / 8 / NT, NB = BN * BK / 8 / NT; // loads per thread per stage
-    constexpr int ND = NA + NB, H0 = (ND + 1) / 2;
+    constexpr int ND = NA + NB;
     constexpr int EPR = 64, CPAD = BN + 4;  // rows r, r+4, r+8, r+12 of a store on distinct banks
     static_assert(NA * NT * 8 == SA && NB * NT * 8 == SB, "whole load instructions");
     static_assert(EPR * CPAD * 4 <= STAGES * STG * (int)sizeof(T), "epilogue stage fits");
@@ -351,7 +351,7 @@ __device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* 
     for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    V8 af[2][TI], bf[2][TJ];
+    V8 af[1][TI], bf[2][TJ];
     // 16x16x32 operand: lane l holds row l % 16 and logical chunk l / 16
     auto rd_a = [&](int kstep, int fb, int i) {
         const T* la = lds + (kstep % STAGES) * STG;
@@ -368,44 +368,38 @@ __device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* 
     for (int st = 0; st < STAGES - 1; ++st)
 #pragma unroll
         for (int d = 0; d < ND; ++d) dma(st, d);
-    wait_vm<2 * ND>();  // stage 0 has landed
+    wait_vm<(STAGES - 2) * ND>();  // stage 0 has landed
     lds_barrier();
 #pragma unroll
-    for (int i = 0; i < TI; ++i) rd_a(0, 0, i);
+    for (int i = 0; i < TI - 1; ++i) rd_a(0, 0, i);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) rd_b(0, 0, j);
 
-    // one k-step; fb (the operand buffer) is a constant after inlining
+    // one k-step; fb (the B operand buffer) is a constant after inlining.
+    // The barrier opens the step: stage kt+1 has landed everywhere and every
+    // wavefront is done with stage kt-1, which the step's loads refill.
+    // After MFMA group i, A row i of the next step is read into the same
+    // registers (their last use has issued) and the next step's B fragments
+    // go to the other buffer, spread over the groups with the loads, so the
+    // LDS sees a steady stream of reads rather than a burst after a barrier.
+    // The last group reads nothing (its A row for the next step is read in
+    // that step's first group), so the step's end waits on no fresh read.
     auto step = [&](const int kt, const int fb) {
         const int kd = kt + STAGES - 1;
-#pragma unroll
-        for (int i = 0; i < TI / 2; ++i) {
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[fb][i], bf[fb][j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = i; d < H0; d += TI / 2) dma(kd, d);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // stage kt+1 complete: only stage kt+2 and the first loads of kd may fly
-        wait_vm<ND + H0>();
+        wait_vm<(STAGES - 3) * ND>();  // only stage kt+2 may still fly
         lds_barrier();
-        // the next step's operands in the order its first half uses them:
-        // every B fragment and the first A rows early, the last A rows late
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) rd_b(kt + 1, fb ^ 1, j);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < TI; ++i) {
 #pragma unroll
-        for (int i = TI / 2; i < TI; ++i) {
-            const int g = i - TI / 2;
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[fb][i], bf[fb][j], acc[i][j]);
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[0][i], bf[fb][j], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int d = H0 + g; d < ND; d += TI / 2) dma(kd, d);
-            if (g < 2) {
+            for (int d = i; d < ND; d += TI) dma(kd, d);
+            if (i == 0) rd_a(kt, 0, TI - 1);
+            if (i < TI - 1) {
+                rd_a(kt + 1, 0, i);
 #pragma unroll
-                for (int q = 0; q < TI / 2; ++q) rd_a(kt + 1, fb ^ 1, g * (TI / 2) + q);
+                for (int j = i * TJ / (TI - 1); j < (i + 1) * TJ / (TI - 1); ++j) rd_b(kt + 1, fb ^ 1, j);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
