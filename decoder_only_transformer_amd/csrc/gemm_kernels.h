@@ -86,17 +86,21 @@ struct EpiPass {
 // straight from global memory into LDS (global_load_lds_dwordx4, no VGPR
 // staging): instruction i of wavefront w fills the 64 consecutive 16-byte
 // LDS slots starting at (i*NW + w)*64, lane l the slot l, so every lane loads
-// the global chunk whose swizzled home is that slot.  Two LDS stages: the
-// loads for step k+1 are issued before the MFMAs of step k; one barrier per
-// step.  Rows of A beyond M and of W beyond N are clamped to the last valid
+// the global chunk whose swizzled home is that slot.  An LDS ring of STAGES
+// k-steps (two for prefill, where two blocks share a CU; four for the
+// weight-streaming expert GEMM): the loads for step k + STAGES - 1 are
+// issued before the MFMAs of step k, the kernel waits for its own loads
+// (vmcnt) and one barrier closes each step.  Rows of A beyond M and of W
+// beyond N are clamped to the last valid
 // row (they only feed outputs that the epilogue discards).  K % 64 == 0.
 // ------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// One BM x BN output tile at (m0, n0); lds holds 2 * (BM + BN) * 64 elements.
+// One BM x BN output tile at (m0, n0); lds holds STAGES * (BM + BN) * 64
+// elements.
 // NTW: the W loads carry the non-temporal hint (weights read by one row
 // tile only).
-template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi, bool NTW = false>
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi, bool NTW = false, int STAGES = 2>
 __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T* __restrict__ W, int M,
                                                int N, int K, Epi epi, int m0, int n0, T* lds) {
     typedef typename vec8<T>::type V8;
@@ -112,32 +116,40 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
     constexpr int CPAD = BN + 8;            // fp32 row pitch of the epilogue stage
     static_assert(EPR * CPAD * 4 <= 2 * (BM + BN) * BK * (int)sizeof(T), "epilogue stage fits");
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / NWN, wn = wave % NWN;
 
-    const T* abase[ACH];
-    const T* bbase[BCH];
+    // load i of a stage fills the 64 consecutive 16-byte slots from
+    // (i*NW + wave)*64; lane l the slot l.  Addresses are the tile's first A
+    // (or W) row, wave-uniform, plus a per-lane byte offset.
+    constexpr int ND = ACH + BCH;
+    unsigned aoff[ACH], boff[BCH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
         const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-        abase[i] = A + (size_t)min(m0 + row, M - 1) * K + c * 8;
+        aoff[i] = (unsigned)(((size_t)(min(m0 + row, M - 1) - m0) * K + c * 8) * sizeof(T));
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
         const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-        bbase[i] = W + (size_t)min(n0 + row, N - 1) * K + c * 8;
+        boff[i] = (unsigned)(((size_t)(min(n0 + row, N - 1) - n0) * K + c * 8) * sizeof(T));
     }
-    auto gload = [&](int k0, int buf) {
-        T* la = lds + buf * (BM + BN) * BK;
-        T* lb = la + BM * BK;
+    const T* a0 = A + (size_t)m0 * K;
+    const T* w0 = W + (size_t)n0 * K;
+    const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)lds;
+    const int nk = K / BK;
+    // k-steps past the end reload the last one into a stage nobody reads
+    auto gload = [&](int kstep) {
+        const int ks = kstep < nk ? kstep : nk - 1;
+        const unsigned la = lds0 + (unsigned)((kstep % STAGES) * (BM + BN) * BK * (int)sizeof(T));
+        const unsigned lb = la + (unsigned)(BM * BK * (int)sizeof(T));
 #pragma unroll
         for (int i = 0; i < ACH; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(abase[i] + k0),
-                                             (lds_ptr_t)(la + (i * NW + wave) * 64 * 8), 16, 0, 0);
+            lds_dma16_s(a0 + ks * BK, aoff[i], la + (unsigned)((i * NW + wave) * 64 * 8 * (int)sizeof(T)));
 #pragma unroll
         for (int i = 0; i < BCH; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(bbase[i] + k0),
-                                             (lds_ptr_t)(lb + (i * NW + wave) * 64 * 8), 16, 0, NTW ? 2 : 0);
+            lds_dma16_s<NTW>(w0 + ks * BK, boff[i], lb + (unsigned)((i * NW + wave) * 64 * 8 * (int)sizeof(T)));
     };
 
     f32x16 acc[TM][TN];
@@ -148,13 +160,16 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = K / BK;
-    gload(0, 0);
-    __syncthreads();
+    // an LDS ring of STAGES k-steps: the loads of step k + STAGES - 1 go out
+    // as step k starts, into the stage of step k - 1, which every wavefront
+    // finished reading before the barrier that closed step k - 1
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) gload(st);
+    wait_vm<(STAGES - 2) * ND>();  // step 0 has landed
+    lds_barrier();
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK, buf ^ 1);
-        const T* la = lds + buf * (BM + BN) * BK;
+        gload(kt + STAGES - 1);
+        const T* la = lds + (kt % STAGES) * (BM + BN) * BK;
         const T* lb = la + BM * BK;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
@@ -175,10 +190,13 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
-        // the barrier waits for this wavefront's loads of step k+1 (vmcnt) and
-        // for every wavefront to finish reading stage k
-        __syncthreads();
+        // step k+1 has landed for this wavefront (later steps may fly); the
+        // barrier makes it so for all and closes the reads of step k
+        wait_vm<(STAGES - 2) * ND>();
+        lds_barrier();
     }
+    wait_vm<0>();
+    __syncthreads();
 
     // Epilogue: stage EPR rows of the fp32 tile through LDS, then hand
     // contiguous 8-column chunks to the epilogue.
@@ -258,7 +276,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restri
                                                                const int* __restrict__ row_off,
                                                                const int* __restrict__ tile_off, int E,
                                                                int N, int K, int tiles_m_max, Epi epi) {
-    __shared__ __attribute__((aligned(16))) T lds[2 * (BM + BN) * 64];
+    // decode-sized calls (NTW) stream the expert weights: a four-step LDS
+    // ring keeps three steps of loads in flight per block
+    constexpr int STAGES = NTW ? 4 : 2;
+    __shared__ __attribute__((aligned(16))) T lds[STAGES * (BM + BN) * 64];
     // workgroups are dealt round-robin to the 8 XCDs: renumber so that each
     // XCD runs a contiguous range, whose row tiles of one column tile then
     // share the expert's weight panel in that XCD's L2.  With NTW every panel
@@ -278,9 +299,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restri
         else hi = mid - 1;
     }
     const int r0 = row_off[lo], rows = row_off[lo + 1] - r0;
-    gemm_mfma_tile<T, BM, BN, WM, WN, NW, EpiRowOff<Epi>, NTW>(A + (size_t)r0 * K, W + (size_t)lo * N * K, rows, N, K,
-                                                          EpiRowOff<Epi>{epi, r0}, (tmg - tile_off[lo]) * BM,
-                                                          tn * BN, lds);
+    gemm_mfma_tile<T, BM, BN, WM, WN, NW, EpiRowOff<Epi>, NTW, STAGES>(
+        A + (size_t)r0 * K, W + (size_t)lo * N * K, rows, N, K, EpiRowOff<Epi>{epi, r0}, (tmg - tile_off[lo]) * BM,
+        tn * BN, lds);
 }
 
 // ------------------------------------------------------------------------------------

@@ -189,11 +189,18 @@ __device__ __forceinline__ void lds_dma16(const void* g, unsigned lds_byte_addr)
                  : "memory", "m0");
 }
 // The same load from a wave-uniform base address (in SGPRs) plus a per-lane
-// 32-bit byte offset: no per-lane 64-bit address arithmetic.
+// 32-bit byte offset: no per-lane 64-bit address arithmetic.  NT adds the
+// non-temporal hint (data read once).
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, unsigned lds_byte_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-                 "s"(lds_byte_addr)
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase),
+                     "s"(lds_byte_addr)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                     "s"(lds_byte_addr)
+                     : "memory", "m0");
 }
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
