@@ -112,7 +112,7 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
     constexpr int ACH = BM * BK / 8 / NT;   // direct-load instructions per thread and stage
     constexpr int BCH = BN * BK / 8 / NT;
     static_assert(ACH * NT * 8 == BM * BK && BCH * NT * 8 == BN * BK, "whole instructions");
-    constexpr int EPR = 64;                 // epilogue rows per pass
+    constexpr int EPR = BM < 64 ? BM : 64;  // epilogue rows per pass
     constexpr int CPAD = BN + 8;            // fp32 row pitch of the epilogue stage
     static_assert(EPR * CPAD * 4 <= 2 * (BM + BN) * BK * (int)sizeof(T), "epilogue stage fits");
 

@@ -213,8 +213,13 @@ hipError_t launch_moe_router(Elem op, const void* n, const void* wr, int M, int 
 }
 
 // Row-tile height of the grouped GEMMs: 256-row tiles of the large kernel
-// when the experts average at least one full such tile, else 128-row tiles.
-int moe_tile_m(int MK, int E) { return MK >= 256 * E ? 256 : kMoeTileM; }
+// when the experts average at least one full such tile; 32-row tiles when
+// they average at most 32 rows (decode: the A tile is then mostly real rows
+// and the LDS ring small enough for two blocks per CU); else 128-row tiles.
+constexpr int kMoeSmallTileM = 32;
+int moe_tile_m(int MK, int E) {
+    return MK >= 256 * E ? 256 : (MK <= kMoeSmallTileM * E ? kMoeSmallTileM : kMoeTileM);
+}
 
 hipError_t launch_moe_route(const int* sel, int MK, int E, int* row_off, int* tile_off, int* src, int* slot,
                             hipStream_t s) {
@@ -251,6 +256,12 @@ static hipError_t grouped_swiglu_t(const void* A, const void* W, const int* row_
             (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, epi);
         return hipGetLastError();
     }
+    if (moe_tile_m(MK, E) == kMoeSmallTileM) {
+        const int tm = grouped_tiles_m(MK, E, kMoeSmallTileM), tn = (N + 127) / 128;
+        gemm_grouped_kernel<T, kMoeSmallTileM, 128, 32, 32, 4, EpiSwiGLU<T>, true><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, epi);
+        return hipGetLastError();
+    }
     const int tm = grouped_tiles_m(MK, E, kMoeTileM), tn = (N + 127) / 128;
     if (stream_experts(MK, E))
         gemm_grouped_kernel<T, kMoeTileM, 128, 64, 64, 4, EpiSwiGLU<T>, true><<<(unsigned)tm * tn, 256, 0, s>>>(
@@ -276,6 +287,12 @@ static hipError_t grouped_down_t(const void* A, const void* W, const int* row_of
     if (moe_tile_m(MK, E) == 256) {
         const int tm = grouped_tiles_m(MK, E, 256), tn = (N + 255) / 256;
         gemm_big_grouped_kernel<T, 256, 256, EpiStoreF32><<<(unsigned)tm * tn, 256, 0, s>>>(
+            (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});
+        return hipGetLastError();
+    }
+    if (moe_tile_m(MK, E) == kMoeSmallTileM) {
+        const int tm = grouped_tiles_m(MK, E, kMoeSmallTileM), tn = (N + 127) / 128;
+        gemm_grouped_kernel<T, kMoeSmallTileM, 128, 32, 32, 4, EpiStoreF32, true><<<(unsigned)tm * tn, 256, 0, s>>>(
             (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});
         return hipGetLastError();
     }
