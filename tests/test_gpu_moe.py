@@ -183,6 +183,13 @@ def test_moe_benchmark_shape_sampled():
     check_moe(w, rows=rows)
 
 
+def test_moe_decode_benchmark_shape():
+    """The benchmark's MoE decode shape and launch path (32 sequences at
+    position 8191 over a drawn cache, 16 experts of 8192, top 1, shared expert
+    8192, d 4096: 32-row expert tiles streamed non-temporally), every row."""
+    check_moe(workloads.get("llama4_moe_decode"))
+
+
 def test_moe_zero_router_takes_the_first_experts():
     """A zero router scores every expert 0: the library takes experts 0 and 1,
     each weighted 1/2, exactly as the tie rule says."""
