@@ -96,6 +96,13 @@ def test_llama3_8b_decode_full():
     run.close()
 
 
+def test_llama3_8b_decode_one_sequence():
+    """The benchmark's single-sequence decode: one token at position 8191 of
+    an 8B-width block, the attention split over many blocks per KV group."""
+    run, *_ = _check_block(workloads.get("llama3_8b_decode_b1"))
+    run.close()
+
+
 def test_llama3_70b_prefill_sampled():
     w = workloads.get("llama3_70b_prefill")
     rows = sample_rows(w, [0, 1, 33, 127, 128, 1000, 2047, 4095])
