@@ -829,10 +829,10 @@ template <typename T, typename KVT, int DH>
 static hipError_t prefill_nw(const AttnArgs& a, hipStream_t s) {
     const int n_rep = a.H / a.nkv;
     if constexpr (DH == 128 && std::is_same<T, KVT>::value) {
-        // eight wavefronts per block: heads of the group x query blocks share
-        // every staged K / V tile.  With 4 heads per group, 2 heads x 4 query
-        // blocks measured 3 % faster than 4 x 2 (8B prefill attention)
-        if (n_rep % 8 == 0) return prefill_fa_t<T, 8, 1>(a, s);
+        // eight wavefronts per block, 2 heads of the group x 4 query blocks,
+        // share every staged K / V tile: measured 2.5-3 % faster than 4 x 2
+        // heads x blocks with 4 heads per group (8B) and 2 % faster than 8 x 1
+        // with 8 (70B)
         if (n_rep % 2 == 0) return prefill_fa_t<T, 2, 4>(a, s);
     }
     if (n_rep % 8 == 0) return prefill_t<T, KVT, DH, 8>(a, s);
