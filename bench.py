@@ -297,6 +297,35 @@ def copy_only(mib):
           flush=True)
 
 
+def vendor_gemm(w, reps=20):
+    """The vendor GEMM library (torch.mm on ROCm, hipBLASLt) on the four
+    prefill products of workload w, fp16 operands, fp32 accumulation: A [M][K]
+    times W[N][K]^T, timed with events over `reps` calls after 3 warm-ups.
+    Context for the library's own GEMM kernels, not part of the step."""
+    import torch
+    M, d, qd, kvd, dff = w.M, w.d, w.H * w.d_head, w.n_kv * w.d_head, w.d_ff
+    shapes = {"qkv": (qd + 2 * kvd, d), "o": (d, qd), "gate_up": (2 * dff, d), "down": (d, dff)}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for name, (N, K) in shapes.items():
+        a = torch.randn(M, K, device="cuda", generator=g).mul_(1.0).half()
+        b = (torch.randn(N, K, device="cuda", generator=g) * 0.02).half()
+        for _ in range(3):
+            c = torch.mm(a, b.t())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            c = torch.mm(a, b.t())
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 4),
+                     "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, tokens):
     """The fp64 oracle, as it stands, on the host: the first `tokens` tokens of
     one sequence of workload w (full block weights)."""
@@ -331,6 +360,7 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the model-level stack decode")
     ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts block")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged decode")
+    ap.add_argument("--no-vendor", action="store_true", help="skip the vendor-library GEMM figures")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -383,6 +413,9 @@ def main():
         "per_call": per_call,
     }
     log(f"[bench] prefill {ms:.3f} ms/step, {result['value']:.0f} tokens/s")
+    if not args.no_vendor:
+        result["vendor_gemm"] = vendor_gemm(w)
+        log(f"[bench] vendor GEMM: {result['vendor_gemm']}")
 
     if not args.no_decode:
         wd = workloads.get(args.decode_workload)

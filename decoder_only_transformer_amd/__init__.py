@@ -28,7 +28,8 @@ EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_forward_ragge
            "llama_stack_init", "llama_stack_forward", "llama_stack_forward_device_pos",
            "llama_stack_graph_create", "llama_stack_graph_launch", "llama_stack_graph_destroy",
            "llama_stack_destroy", "llama_stack_num_layers", "llama_stack_last_error",
-           "llama_moe_block_init", "llama_block_copy_routing")
+           "llama_moe_block_init", "llama_block_copy_routing", "llama_block_operand_type",
+           "llama_stack_operand_type")
 MAX_STACK_LAYERS = 1024
 STAGE_NAMES = ("rmsnorm_1", "qkv_rope_append", "attention", "o_proj_residual", "rmsnorm_2",
                "gate_up_swiglu", "down_residual")
@@ -139,6 +140,10 @@ def lib() -> ctypes.CDLL:
         L.llama_stack_destroy.restype = None
         L.llama_stack_num_layers.argtypes = [vp]
         L.llama_stack_num_layers.restype = i32
+        L.llama_block_operand_type.argtypes = [vp]
+        L.llama_block_operand_type.restype = ctypes.c_int
+        L.llama_stack_operand_type.argtypes = [vp]
+        L.llama_stack_operand_type.restype = ctypes.c_int
         L.llama_stack_last_error.argtypes = [vp]
         L.llama_stack_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -233,6 +238,15 @@ def llama_block_forward_ragged(handle: int, x, start_pos, kv: Tuple, out, stream
 def llama_block_destroy(handle: int) -> None:
     if handle:
         lib().llama_block_destroy(handle)
+
+
+def llama_block_operand_type(handle: int) -> str:
+    """Operand type of the handle's matrix products: "f32", "f16" or "bf16"."""
+    return ELEM_NAMES[lib().llama_block_operand_type(handle)]
+
+
+def llama_stack_operand_type(handle: int) -> str:
+    return ELEM_NAMES[lib().llama_stack_operand_type(handle)]
 
 
 def llama_block_stage_info(handle: int, stage: str) -> Tuple[str, int]:
@@ -396,6 +410,10 @@ class LlamaBlock:
         else:
             llama_block_forward_ragged(self.handle, x, start_pos, kv, out, stream)
         return out
+
+    @property
+    def operand_type(self) -> str:
+        return llama_block_operand_type(self.handle)
 
     def stage(self, name: str, rows: int):
         import torch

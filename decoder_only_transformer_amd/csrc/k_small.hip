@@ -271,6 +271,52 @@ hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const v
     return hipErrorInvalidValue;
 }
 
+// Per-row statistics of a bf16 weight [rows][K] for the range check of the
+// fp16 operand path: out[row] = (sum_k (g_k w_k)^2, sum_k (w_k - fp16(w_k))^2,
+// max_k |w_k|, sum_k w_k^2), with g_k = 1 when g is null.  One wavefront per
+// row, four rows per block; K % 8 == 0.
+__global__ void __launch_bounds__(256) weight_row_stats_kernel(const bf16* __restrict__ w,
+                                                               const bf16* __restrict__ g, int rows,
+                                                               int K, f32x4* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const bf16* wr = w + (size_t)row * K;
+    float sg = 0.0f, se = 0.0f, mx = 0.0f, sw = 0.0f;
+    for (int c = lane * 8; c < K; c += 512) {
+        float v[8], gg[8];
+        load8(wr + c, v);
+        if (g) {
+            load8(g + c, gg);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gg[e] = 1.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float gw = gg[e] * v[e];
+            const float dv = v[e] - (float)(f16)v[e];
+            sg += gw * gw;
+            se += dv * dv;
+            mx = fmaxf(mx, fabsf(v[e]));
+            sw += v[e] * v[e];
+        }
+    }
+    sg = wave_sum(sg);
+    se = wave_sum(se);
+    sw = wave_sum(sw);
+    mx = wave_max(mx);
+    if (lane == 0) out[row] = f32x4{sg, se, mx, sw};
+}
+
+hipError_t launch_weight_row_stats(const void* w, const void* g, int rows, int K, float* out, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (K % 8 != 0) return hipErrorInvalidValue;
+    weight_row_stats_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>((const bf16*)w, (const bf16*)g, rows, K,
+                                                                      (f32x4*)out);
+    return hipGetLastError();
+}
+
 // Device-held start positions move on by the tokens of the step that read
 // them; queued after that step's last kernel on the same stream.
 __global__ void __launch_bounds__(256) advance_positions_kernel(int* __restrict__ pos, int B, int S) {

@@ -31,6 +31,10 @@ hipError_t launch_convert(Elem src_t, Elem dst_t, const void* src, void* dst, si
 // dst row 2i+1 <- src row i + perm_dh/2.
 hipError_t launch_convert_rows(Elem src_t, Elem dst_t, const void* src, void* dst, int rows, int K,
                                int perm_dh, hipStream_t s);
+// Per-row statistics of a bf16 weight w [rows][K] (gain g [K] or null for
+// ones), four floats per row into out [rows][4]: sum (g w)^2, sum of the
+// squared change of a bf16 -> fp16 conversion, max |w|, sum w^2.  K % 8 == 0.
+hipError_t launch_weight_row_stats(const void* w, const void* g, int rows, int K, float* out, hipStream_t s);
 // pos[b] += S for b < B (device array)
 hipError_t launch_advance_positions(int* pos, int B, int S, hipStream_t s);
 // dst [2*dff][d]: row groups of 8 = four gate rows then the same four up rows

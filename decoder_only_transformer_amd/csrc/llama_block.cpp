@@ -281,7 +281,7 @@ static hipError_t pack_layer(const lb_block* blk, const lb_weights* w, const Lay
 // A handle with the config, the RoPE table and the workspace, but no weights
 // yet.  Synchronous.  On error *out stays NULL and the message is in
 // g_init_error.
-static lb_status create_core(const lb_config* cfg, lb_block** out) {
+static lb_status create_core(const lb_config* cfg, Elem op_type, lb_block** out) {
     *out = nullptr;
     lb_status st = validate_config(cfg);
     if (st != LB_OK) return st;
@@ -290,7 +290,7 @@ static lb_status create_core(const lb_config* cfg, lb_block** out) {
     blk->cfg = *cfg;
     const lb_config& c = blk->cfg;
     blk->dt = c.dtype == LB_BF16 ? Elem::BF16 : Elem::F32;
-    blk->op = c.dtype == LB_F32 ? Elem::F32 : (c.operands == LB_OPERANDS_BF16 ? Elem::BF16 : Elem::F16);
+    blk->op = op_type;
     if (hipGetDevice(&blk->dev) != hipSuccess) {
         delete blk;
         return fail(nullptr, LB_ERR_HIP, "hipGetDevice failed");
@@ -377,6 +377,148 @@ static lb_status create_core(const lb_config* cfg, lb_block** out) {
     return LB_OK;
 }
 
+// ---- range of the fp16 operand path ----------------------------------------------
+// A bf16 weight widens to fp16 exactly from 2^-17 up to 65504 in magnitude
+// (8 significant bits fit fp16's subnormal spacing 2^-24 from 2^-17 up), and
+// every activation that a bf16 block rounds to an fp16 operand is bounded by
+// its weights and gains:
+//   |n1_k| <= sqrt(d) max|g1|, |n2_k| <= sqrt(d) max|g2|: the row divided by
+//     its root mean square has Euclidean norm at most sqrt(d);
+//   |q_j|, |k_j| <= sqrt(2) sqrt(d) ||g1 . Wq_j||: Cauchy-Schwarz, and RoPE
+//     turns each pair within its norm; |v_j| <= sqrt(d) ||g1 . Wv_j||;
+//   |o| <= max |v|: each output is a convex combination of value rows;
+//   |z_j| <= |a_j| |u_j| <= d ||g2 . Wgate_j|| ||g2 . Wup_j||, as |SiLU(a)| <= |a|
+//     (the same for every routed expert of a MoE block).
+// AUTO and F16 take fp16 operands when every bound and every |w| stays below
+// fp16's largest finite value and each weight row changes by at most 2^-11 of
+// its norm in the conversion (fp16's own relative rounding); otherwise AUTO
+// takes bf16 operands and F16 is refused.
+static hipError_t row_stats(float* dev, const void* w, const void* g, int rows, int K, std::vector<float>& out) {
+    out.assign((size_t)rows * 4, 0.0f);
+    hipError_t e = lb::launch_weight_row_stats(w, g, rows, K, dev, nullptr);
+    if (e == hipSuccess) e = hipMemcpy(out.data(), dev, out.size() * sizeof(float), hipMemcpyDeviceToHost);
+    return e;
+}
+
+struct RangeCheck {
+    bool fits = true;
+    char why[256] = {0};
+    void fail(const char* fmt, ...) {
+        if (!fits) return;
+        fits = false;
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(why, sizeof(why), fmt, ap);
+        va_end(ap);
+    }
+    // fp16 limit with a margin for the rounding of the bounds themselves
+    static constexpr double kLimit = 65504.0 * (1.0 - 1.0 / 256.0);
+    void bound(const char* what, int layer, double v) {
+        if (!(v <= kLimit)) fail("block %d: %s can reach %.6g, beyond fp16's range", layer, what, v);
+    }
+    // every weight in fp16 range and every row widened closely enough
+    void weights(const char* name, int layer, const std::vector<float>& st, int rows) {
+        for (int r = 0; r < rows && fits; ++r) {
+            const float* p = &st[(size_t)r * 4];
+            if (!(p[2] <= 65504.0f)) fail("block %d: |%s| reaches %.6g, beyond fp16's range", layer, name, p[2]);
+            else if (!(p[1] <= std::ldexp(p[3], -22)))
+                fail("block %d: row %d of %s loses more than 2^-11 of its norm in fp16", layer, r, name);
+        }
+    }
+    // max over rows of sqrt(sum (g w)^2)
+    static double max_gnorm(const std::vector<float>& st, int rows) {
+        double m = 0.0;
+        for (int r = 0; r < rows; ++r) m = std::max(m, std::sqrt((double)st[(size_t)r * 4]));
+        return m;
+    }
+};
+
+static lb_status check_f16_range(const lb_config& c, const lb_weights* ws, int n_layers, const lb_moe_config* moe,
+                                 const lb_moe_weights* ew, RangeCheck* rc) {
+    const int d = c.d_model, dh = c.d_head, dff = c.d_ff, qd = c.n_heads * dh, kvd = c.n_kv_heads * dh;
+    long rows_max = std::max(std::max(qd, d), std::max(dff, 1));
+    if (moe) rows_max = std::max(rows_max, (long)moe->n_experts * std::max(moe->d_ff_expert, d));
+    float* dev = nullptr;
+    if (hipMalloc(&dev, (size_t)rows_max * 4 * sizeof(float)) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(nullptr, LB_ERR_OOM, "device allocation failed (range check)");
+    }
+    const double sd = std::sqrt((double)d);
+    std::vector<float> g1, g2, a, b;
+    hipError_t e = hipSuccess;
+    for (int l = 0; l < n_layers && e == hipSuccess && rc->fits; ++l) {
+        const lb_weights& w = ws[l];
+        e = row_stats(dev, w.attn_norm, nullptr, 1, d, g1);
+        if (e == hipSuccess) e = row_stats(dev, w.ffn_norm, nullptr, 1, d, g2);
+        if (e != hipSuccess) break;
+        rc->bound("RMSNorm_1 output", l, sd * g1[2]);
+        rc->bound("RMSNorm_2 output", l, sd * g2[2]);
+        const struct { const char* name; const void* w; int rows; double f; } proj[3] = {
+            {"wq", w.wq, qd, std::sqrt(2.0)}, {"wk", w.wk, kvd, std::sqrt(2.0)}, {"wv", w.wv, kvd, 1.0}};
+        for (const auto& p : proj) {
+            if ((e = row_stats(dev, p.w, w.attn_norm, p.rows, d, a)) != hipSuccess) break;
+            rc->weights(p.name, l, a, p.rows);
+            rc->bound(p.name[1] == 'q' ? "q" : (p.name[1] == 'k' ? "k" : "v (and the attention output)"), l,
+                      p.f * sd * RangeCheck::max_gnorm(a, p.rows));
+        }
+        if (e != hipSuccess) break;
+        if ((e = row_stats(dev, w.wo, nullptr, d, qd, a)) != hipSuccess) break;
+        rc->weights("wo", l, a, d);
+        if ((e = row_stats(dev, w.w_down, nullptr, d, dff, a)) != hipSuccess) break;
+        rc->weights("w_down", l, a, d);
+        // gate and up rows pair up in z
+        auto ffn = [&](const char* what, const void* gate, const void* up, int rows) -> hipError_t {
+            hipError_t er = row_stats(dev, gate, w.ffn_norm, rows, d, a);
+            if (er == hipSuccess) er = row_stats(dev, up, w.ffn_norm, rows, d, b);
+            if (er != hipSuccess) return er;
+            rc->weights(what, l, a, rows);
+            rc->weights(what, l, b, rows);
+            double m = 0.0;
+            for (int r = 0; r < rows; ++r)
+                m = std::max(m, std::sqrt((double)a[(size_t)r * 4]) * std::sqrt((double)b[(size_t)r * 4]));
+            rc->bound(what, l, (double)d * m);
+            return hipSuccess;
+        };
+        if ((e = ffn("SwiGLU output z (w_gate, w_up)", w.w_gate, w.w_up, dff)) != hipSuccess) break;
+        if (moe) {
+            const int E = moe->n_experts, fe = moe->d_ff_expert;
+            if ((e = row_stats(dev, ew->router, nullptr, E, d, a)) != hipSuccess) break;
+            rc->weights("router", l, a, E);
+            if ((e = ffn("expert SwiGLU output z", ew->w_gate, ew->w_up, E * fe)) != hipSuccess) break;
+            if ((e = row_stats(dev, ew->w_down, nullptr, E * d, fe, a)) != hipSuccess) break;
+            rc->weights("expert w_down", l, a, E * d);
+        }
+    }
+    hipFree(dev);
+    if (e != hipSuccess) return fail(nullptr, LB_ERR_HIP, "range check: %s", hipGetErrorString(e));
+    return LB_OK;
+}
+
+// Operand type of the matrix products of a new handle (see above).
+static lb_status choose_operands(const lb_config* cfg, const lb_weights* ws, int n_layers, const lb_moe_config* moe,
+                                 const lb_moe_weights* ew, Elem* op) {
+    lb_status st = validate_config(cfg);
+    if (st != LB_OK) return st;
+    if (cfg->dtype == LB_F32) {
+        *op = Elem::F32;
+        return LB_OK;
+    }
+    if (cfg->operands == LB_OPERANDS_BF16) {
+        *op = Elem::BF16;
+        return LB_OK;
+    }
+    RangeCheck rc;
+    st = check_f16_range(*cfg, ws, n_layers, moe, ew, &rc);
+    if (st != LB_OK) return st;
+    if (rc.fits) {
+        *op = Elem::F16;
+        return LB_OK;
+    }
+    if (cfg->operands == LB_OPERANDS_F16) return fail(nullptr, LB_ERR_UNSUPPORTED, "fp16 operands: %s", rc.why);
+    *op = Elem::BF16;
+    return LB_OK;
+}
+
 // Allocate and pack n layers of weights into ls[0..n) (synchronous).
 static lb_status load_layers(lb_block* blk, const lb_weights* w, int n, LayerW* ls) {
     for (int l = 0; l < n; ++l)
@@ -396,8 +538,11 @@ extern "C" lb_status llama_block_init(const lb_config* cfg, const lb_weights* w,
     *out = nullptr;
     if (!cfg || !w) return fail(nullptr, LB_ERR_INVALID_ARG, "cfg or weights is NULL");
     if (!weights_complete(w)) return fail(nullptr, LB_ERR_INVALID_ARG, "a weight pointer is NULL");
+    Elem op = Elem::F32;
+    lb_status st = choose_operands(cfg, w, 1, nullptr, nullptr, &op);
+    if (st != LB_OK) return st;
     lb_block* blk = nullptr;
-    lb_status st = create_core(cfg, &blk);
+    st = create_core(cfg, op, &blk);
     if (st != LB_OK) return st;
     st = load_layers(blk, w, 1, &blk->lw);
     if (st != LB_OK) {
@@ -429,8 +574,11 @@ extern "C" lb_status llama_moe_block_init(const lb_config* cfg, const lb_weights
     if (fe % 64 != 0) return fail(nullptr, LB_ERR_UNSUPPORTED, "d_ff_expert (%d) must be a multiple of 64", fe);
     if ((long)cfg->max_tokens * K > (1L << 24))
         return fail(nullptr, LB_ERR_UNSUPPORTED, "max_tokens * top_k exceeds 2^24");
+    Elem op = Elem::F32;
+    st = choose_operands(cfg, w, 1, moe, ew, &op);
+    if (st != LB_OK) return st;
     lb_block* blk = nullptr;
-    st = create_core(cfg, &blk);
+    st = create_core(cfg, op, &blk);
     if (st != LB_OK) return st;
     blk->moe_E = E;
     blk->moe_K = K;
@@ -796,8 +944,11 @@ extern "C" lb_status llama_stack_init(const lb_config* cfg, int32_t n_layers, co
     for (int l = 0; l < n_layers; ++l)
         if (!weights_complete(&layers[l]))
             return fail(nullptr, LB_ERR_INVALID_ARG, "a weight pointer of block %d is NULL", l);
+    Elem op = Elem::F32;
+    lb_status st = choose_operands(cfg, layers, n_layers, nullptr, nullptr, &op);
+    if (st != LB_OK) return st;
     lb_block* blk = nullptr;
-    lb_status st = create_core(cfg, &blk);
+    st = create_core(cfg, op, &blk);
     if (st != LB_OK) return st;
     lb_stack* sk = new lb_stack();
     sk->core = blk;
@@ -1003,6 +1154,14 @@ static bool stage_buffer(const lb_block* blk, lb_stage which, const void** ptr, 
 
 static lb_elem to_abi(Elem e) {
     return e == Elem::F32 ? LB_ELEM_F32 : (e == Elem::BF16 ? LB_ELEM_BF16 : LB_ELEM_F16);
+}
+
+extern "C" lb_elem llama_block_operand_type(const lb_block* blk) {
+    return blk ? to_abi(blk->op) : LB_ELEM_F32;
+}
+
+extern "C" lb_elem llama_stack_operand_type(const lb_stack* sk) {
+    return sk ? to_abi(sk->core->op) : LB_ELEM_F32;
 }
 
 extern "C" lb_status llama_block_stage_info(const lb_block* blk, lb_stage which, lb_elem* elem, int64_t* cols) {

@@ -28,9 +28,13 @@
  *    on request, bf16) MFMA operands and fp32 accumulation; the residual
  *    stream h is kept in fp32.
  *  - Errors: every function validates its arguments before touching device
- *    memory; on any error nothing is launched and nothing is written.  The
- *    text of the last error of a handle is available from
- *    llama_block_last_error().
+ *    memory, and an argument error (LB_ERR_INVALID_ARG, LB_ERR_UNSUPPORTED)
+ *    launches nothing and writes nothing.  A forward that fails with
+ *    LB_ERR_HIP (a launch refused by the runtime) stops at the failing
+ *    kernel: the kernels before it have run, so `out`, the workspace and the
+ *    cache rows [start_pos, start_pos + seq_len) of that call may be partly
+ *    written; no other cache row is touched.  The text of the last error of a
+ *    handle is available from llama_block_last_error().
  */
 #ifndef LLAMA_BLOCK_H
 #define LLAMA_BLOCK_H
@@ -45,9 +49,27 @@ extern "C" {
 typedef enum { LB_F32 = 0, LB_BF16 = 1 } lb_dtype;
 
 /* Operand type of the matrix-core products for bf16 blocks (ignored for fp32
- * blocks, which run in fp32 throughout).  AUTO = F16: bf16 weights are widened
- * to fp16 at init and activations are rounded to fp16, three more mantissa
- * bits than bf16 at the same MFMA rate.  BF16 keeps every operand in bf16. */
+ * blocks, which run in fp32 throughout).
+ *   F16: bf16 weights are widened to fp16 at init and the activations that
+ *     feed matrix products (RMSNorm outputs, q, k, v, the attention output
+ *     and SiLU(gate)*up) are rounded to fp16: three more mantissa bits than
+ *     bf16 at the same MFMA rate.  The residual stream stays fp32.  fp16's
+ *     range is narrower than bf16's, so init checks, from the weights and
+ *     gains on the device, bounds that hold for ANY input x: |RMSNorm out|
+ *     <= sqrt(d_model) max|gain|; |q|, |k| <= sqrt(2) sqrt(d_model)
+ *     max_j ||gain * W_j|| (RoPE turns pairs within their norm), |v| and the
+ *     attention output <= sqrt(d_model) max_j ||gain * Wv_j||; |SiLU(gate)*up|
+ *     <= d_model max_j ||g2 * Wgate_j|| ||g2 * Wup_j||.  Every bound and every
+ *     |weight| must stay below 65504 (with a 2^-8 margin), and no weight row
+ *     may change by more than 2^-11 of its norm when widened (bf16 values
+ *     below 2^-17 lose bits in fp16).  Otherwise init returns
+ *     LB_ERR_UNSUPPORTED.
+ *   AUTO: F16 when that check passes, else BF16 (llama_block_operand_type
+ *     tells which was taken).
+ *   BF16: every operand in bf16 (8 significant bits).  An experimental mode:
+ *     at the 8B width its operand rounding, amplified by the FFN, reaches
+ *     about 2e-2 of rms(y) against an fp64 reference, so it is not held to
+ *     the 2e-2 bar that F16 meets; its tests hold it to 4e-2. */
 typedef enum { LB_OPERANDS_AUTO = 0, LB_OPERANDS_F16 = 1, LB_OPERANDS_BF16 = 2 } lb_operands;
 
 typedef enum {
@@ -117,7 +139,11 @@ typedef struct {
 
 typedef struct lb_block lb_block;
 
-/* Create a block on the current HIP device.  Validates cfg: d_model ==
+/* Create a block on the current HIP device: the set-up half of the pages'
+ * block module ("Full Llama 3 transformer block", How it works: the block
+ * holds the q/k/v/o projections, the two RMSNorm gains and the gate/up/down
+ * FFN; the RoPE table freqs_cis is computed once, "The Evolving Transformer
+ * 04 LLaMA", 02 RoPE).  Validates cfg: d_model ==
  * n_heads*d_head, n_heads % n_kv_heads == 0, d_head even, d_ff, max_tokens,
  * max_seq_len, rope_theta, norm_eps > 0 (LB_ERR_INVALID_ARG).  Supported
  * shapes (else LB_ERR_UNSUPPORTED): d_model <= 16384; bf16 blocks need d_head
@@ -128,8 +154,11 @@ typedef struct lb_block lb_block;
  * workspace.  Synchronous.  *out receives the handle (NULL on error). */
 lb_status llama_block_init(const lb_config* cfg, const lb_weights* weights, lb_block** out);
 
-/* One forward pass, enqueued on `stream` (a hipStream_t; NULL = the null
- * stream) and asynchronous to the host.
+/* One forward pass, the pages' forward(x, start_pos, freqs_cis, mask) ("Full
+ * Llama 3 transformer block", How it works): freqs_cis is the handle's table
+ * and the mask is the causal rule (key t is visible to the query at position
+ * start_pos + s iff t <= start_pos + s), so neither is passed.  Enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream), asynchronous to the host.
  *   x   [batch][seq_len][d_model], device, cfg.dtype
  *   out [batch][seq_len][d_model], device, cfg.dtype; must not overlap x
  * seq_len == 1 runs the decode kernels, seq_len > 1 the prefill kernels; one
@@ -300,6 +329,12 @@ const char* llama_block_last_error(const lb_block* blk);
 typedef enum { LB_STAGE_N1 = 0, LB_STAGE_Q = 1, LB_STAGE_O = 2, LB_STAGE_H = 3,
                LB_STAGE_N2 = 4, LB_STAGE_Z = 5 } lb_stage;
 typedef enum { LB_ELEM_F32 = 0, LB_ELEM_BF16 = 1, LB_ELEM_F16 = 2 } lb_elem;
+
+/* Operand type the handle's matrix products run in: LB_ELEM_F32 for fp32
+ * blocks, else LB_ELEM_F16 or LB_ELEM_BF16 as chosen by cfg.operands and the
+ * range check of init (see lb_operands).  LB_ELEM_F32 for a NULL handle. */
+lb_elem llama_block_operand_type(const lb_block* blk);
+lb_elem llama_stack_operand_type(const lb_stack* st);
 
 /* Describe a stage buffer: element type and columns per token row. */
 lb_status llama_block_stage_info(const lb_block* blk, lb_stage which, lb_elem* elem,

@@ -412,6 +412,34 @@ def test_decode_token_by_token_equals_prefill():
     np.testing.assert_allclose(vc, vc_full, rtol=0, atol=0)
 
 
+@pytest.mark.parametrize("start_pos", [0, 5])
+def test_row_subset_equals_full_computation_bitwise(start_pos):
+    """The largest parity cases may ask the oracle for some output rows only.
+    Each requested row, and every cache row up to the last requested position
+    of its sequence, must be bitwise the row of the full computation: the
+    subset runs the same per-row loops in the same order, it only skips rows.
+    Rows are taken at both ends of each sequence and inside it, including a
+    sequence with no requested row (its cache rows stay unwritten)."""
+    w = _small("smollm2_135m_prefill", B=3, S=37, start_pos=start_pos, max_seq=48, seed=12,
+               dtype="f32")
+    t = workloads.generate(w)
+    y_full, kc_full, vc_full, st_full = oracle.run_workload(w, t, stages=True)
+    rows = [0, 1, 17, 36, 2 * 37 + 20]          # sequence 1 asks for nothing
+    y_sub, kc_sub, vc_sub, st_sub = oracle.run_workload(w, t, rows=rows, stages=True)
+    yf, ys = y_full.reshape(w.M, w.d), y_sub.reshape(w.M, w.d)
+    np.testing.assert_array_equal(ys[rows], yf[rows])
+    for name in ("n1", "q", "o", "h", "n2", "z"):
+        np.testing.assert_array_equal(st_sub[name][rows], st_full[name][rows])
+    for b, last in ((0, 36), (2, 20)):
+        hi = start_pos + last + 1
+        np.testing.assert_array_equal(kc_sub[b, :, :hi], kc_full[b, :, :hi])
+        np.testing.assert_array_equal(vc_sub[b, :, :hi], vc_full[b, :, :hi])
+    assert not np.any(kc_sub[1, :, start_pos:start_pos + w.S])
+    # rows not asked for are left at zero, so the subset did skip work
+    others = sorted(set(range(w.M)) - set(rows))
+    assert not np.any(ys[others])
+
+
 def test_residual_wiring_zero_weights():
     """"Full Llama 3 transformer block", How it works: h = x + Attn(...),
     y = h + FFN(...).  With Wo = 0 and W_down = 0, y = x exactly; with
@@ -775,6 +803,8 @@ MUTANTS = [
      "swiglu(n, mw->w_gate + e * (size_t)f * d, mw->w_up + e * (size_t)f * d,",
      "swiglu(n, mw->w_up + e * (size_t)f * d, mw->w_gate + e * (size_t)f * d,",
      ["test_moe_ffn_row_closed_form", "test_moe_zero_router_takes_the_first_k_equally"]),
+    ("row subset: each sequence's cache one row short", "if (s + 1 > need[b]) need[b] = s + 1;",
+     "if (s > need[b]) need[b] = s;", ["test_row_subset_equals_full_computation_bitwise"]),
 ]
 
 
@@ -810,7 +840,8 @@ def test_planted_mistake_is_caught(tmp_path, label, old, new, pins):
         oracle._lib = mut
         for pin in pins:
             fn = globals()[pin]
-            args = {"test_block_matches_library_composition": ("tiny_f32", {"B": 3, "S": 9, "seed": 5})}
+            args = {"test_block_matches_library_composition": ("tiny_f32", {"B": 3, "S": 9, "seed": 5}),
+                    "test_row_subset_equals_full_computation_bitwise": (5,)}
             with pytest.raises(AssertionError):
                 if pin in args:
                     fn(*args[pin])
