@@ -29,7 +29,7 @@ EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_forward_ragge
            "llama_stack_graph_create", "llama_stack_graph_launch", "llama_stack_graph_destroy",
            "llama_stack_destroy", "llama_stack_num_layers", "llama_stack_last_error",
            "llama_moe_block_init", "llama_block_copy_routing", "llama_block_operand_type",
-           "llama_stack_operand_type")
+           "llama_stack_operand_type", "llama_block_forward_decode_static")
 MAX_STACK_LAYERS = 1024
 STAGE_NAMES = ("rmsnorm_1", "qkv_rope_append", "attention", "o_proj_residual", "rmsnorm_2",
                "gate_up_swiglu", "down_residual")
@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.llama_block_forward_ragged.argtypes = [vp, vp, i32, i32, ctypes.POINTER(ctypes.c_int32),
                                                  ctypes.POINTER(LbKVCache), vp, vp]
         L.llama_block_forward_ragged.restype = ctypes.c_int
+        L.llama_block_forward_decode_static.argtypes = [vp, vp, i32, i32, ctypes.POINTER(LbKVCache), vp, vp]
+        L.llama_block_forward_decode_static.restype = ctypes.c_int
         L.llama_block_destroy.argtypes = [vp]
         L.llama_block_destroy.restype = None
         L.llama_block_status_string.argtypes = [ctypes.c_int]
@@ -233,6 +235,19 @@ def llama_block_forward_ragged(handle: int, x, start_pos, kv: Tuple, out, stream
     st = lib().llama_block_forward_ragged(handle, _ptr(x), B, S, arr, ctypes.byref(c), _ptr(out),
                                           _stream(stream))
     _check(handle, st, "llama_block_forward_ragged")
+
+
+def llama_block_forward_decode_static(handle: int, x, start_pos: int, kv: Tuple, out, stream=None) -> None:
+    """One decode step (x, out: [B][1][d]) on the library's static scratch array
+    instead of the handle's workspace; allocates nothing."""
+    k, v = kv
+    B, S = int(x.shape[0]), int(x.shape[1])
+    if S != 1:
+        raise ValueError(f"a decode step takes one token per sequence, got seq_len {S}")
+    c = LbKVCache(_ptr(k), _ptr(v), int(k.shape[0]), int(k.shape[2]))
+    st = lib().llama_block_forward_decode_static(handle, _ptr(x), B, int(start_pos), ctypes.byref(c),
+                                                 _ptr(out), _stream(stream))
+    _check(handle, st, "llama_block_forward_decode_static")
 
 
 def llama_block_destroy(handle: int) -> None:

@@ -16,7 +16,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <atomic>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -96,8 +98,71 @@ struct lb_block {
     int64_t profiled_calls = 0;
 };
 
+// The scratch buffers one forward writes and reads: the handle's workspace,
+// or (llama_block_forward_decode_static) pieces of the library's static array.
+struct Workspace {
+    void* n1 = nullptr;
+    void* n2 = nullptr;
+    void* q = nullptr;
+    void* o = nullptr;
+    void* z = nullptr;
+    float* h = nullptr;
+    void* kws = nullptr;
+    void* vws = nullptr;
+    float* part = nullptr;
+    float* gpart = nullptr;
+    size_t gpart_cap = 0;
+    void* at_n1 = nullptr;
+    void* at_o = nullptr;
+    void* at_n2 = nullptr;
+    void* at_z = nullptr;
+};
+
+static Workspace handle_workspace(const lb_block* blk) {
+    Workspace w;
+    w.n1 = blk->n1;
+    w.n2 = blk->n2;
+    w.q = blk->q;
+    w.o = blk->o;
+    w.z = blk->z;
+    w.h = blk->h;
+    w.kws = blk->kws;
+    w.vws = blk->vws;
+    w.part = blk->part;
+    w.gpart = blk->gpart;
+    w.gpart_cap = blk->gpart_cap;
+    w.at_n1 = blk->at_n1;
+    w.at_o = blk->at_o;
+    w.at_n2 = blk->at_n2;
+    w.at_z = blk->at_z;
+    return w;
+}
+
 static constexpr int kProfileSlots = 256;
 static constexpr int kDecodeRows = 64;  // largest decode batch that runs on the tiled GEMMs
+
+// ---- static scratch of llama_block_forward_decode_static ---------------------------
+// One array per GPU in the library's device code; that entry point carves its
+// scratch buffers out of it and so allocates nothing.  Host code never uses
+// the array's name as an address: each device's copy sits at its own address,
+// looked up once per device (set up by init) and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[LB_STATIC_SCRATCH_BYTES];
+static constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch[kMaxDevices];
+static std::mutex g_scratch_lock;
+
+// Look up the current device's copy of `scratch` (dev must be current).
+static void setup_static_scratch(int dev) {
+    if (dev < 0 || dev >= kMaxDevices || g_scratch[dev].load(std::memory_order_acquire)) return;
+    std::lock_guard<std::mutex> guard(g_scratch_lock);
+    if (g_scratch[dev].load(std::memory_order_relaxed)) return;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess && p) {
+        g_scratch[dev].store(p, std::memory_order_release);
+    } else {
+        (void)hipGetLastError();
+    }
+}
 
 static void profile_release(lb_block* blk) {
     for (hipEvent_t e : blk->events) hipEventDestroy(e);
@@ -295,6 +360,7 @@ static lb_status create_core(const lb_config* cfg, Elem op_type, lb_block** out)
         delete blk;
         return fail(nullptr, LB_ERR_HIP, "hipGetDevice failed");
     }
+    setup_static_scratch(blk->dev);
     const int d = c.d_model, dh = c.d_head, dff = c.d_ff;
     blk->qd = c.n_heads * dh;
     blk->kvd = c.n_kv_heads * dh;
@@ -686,9 +752,12 @@ static lb_status run_moe_ffn(lb_block* blk, const LayerW& L, const void* n2, voi
     return LB_OK;
 }
 
-// sp: start position of every sequence (validated by the caller)
+// sp: start position of every sequence (validated by the caller).  wk: the
+// scratch buffers; stage_state: record the layout of this call's stage
+// buffers for llama_block_copy_stage (calls on the handle's own workspace).
 static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int B, int S,
-                             const lb::SeqPos& sp, const lb_kv_cache* kv, void* out, hipStream_t s) {
+                             const lb::SeqPos& sp, const lb_kv_cache* kv, void* out, hipStream_t s,
+                             const Workspace& wk, bool stage_state = true) {
     const lb_config& c = blk->cfg;
     const int M = B * S, d = c.d_model, dh = c.d_head, nkv = c.n_kv_heads, dff = c.d_ff;
     const int cap = kv->max_seq_len;
@@ -718,14 +787,14 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     // GEMMs on k-step tiled activations and weights
     const bool dec = dt == Elem::BF16 && S == 1 && M <= kDecodeRows;
     const int mt = dec ? lb::decode_row_tiles(M) : 0;
-    const lb::SplitWs ws{blk->gpart, blk->gpart_cap};
-    void* n1 = dec ? blk->at_n1 : blk->n1;
-    void* o = dec ? blk->at_o : blk->o;
+    const lb::SplitWs ws{wk.gpart, wk.gpart_cap};
+    void* n1 = dec ? wk.at_n1 : wk.n1;
+    void* o = dec ? wk.at_o : wk.o;
     const bool moe = blk->moe_E > 0;
     // MoE blocks keep n2 and z row-major: the router and the grouping read n2 by rows
     const bool dec_ffn = dec && !moe;
-    void* n2 = dec_ffn ? blk->at_n2 : blk->n2;
-    void* z = dec_ffn ? blk->at_z : blk->z;
+    void* n2 = dec_ffn ? wk.at_n2 : wk.n2;
+    void* z = dec_ffn ? wk.at_z : wk.z;
 
     mark(0);
     e = lb::launch_rmsnorm(dt, op, x, L.g1, n1, M, d, (float)c.norm_eps, mt, s);
@@ -745,9 +814,9 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     const bool ws_kv = (dt == Elem::BF16) && S > 1 && all_zero;
     const int s_stride = (S + 7) & ~7;
     lb::QkvEpi qe;
-    qe.q = blk->q;
-    qe.kws = ws_kv ? blk->kws : nullptr;
-    qe.vws = ws_kv ? blk->vws : nullptr;
+    qe.q = wk.q;
+    qe.kws = ws_kv ? wk.kws : nullptr;
+    qe.vws = ws_kv ? wk.vws : nullptr;
     qe.kc = kv->k;
     qe.vc = kv->v;
     qe.rope = blk->rope;
@@ -765,7 +834,7 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "qkv projection: %s", hipGetErrorString(e));
 
     lb::AttnArgs a;
-    a.q = blk->q;
+    a.q = wk.q;
     a.o = o;
     a.B = B;
     a.S = S;
@@ -775,8 +844,8 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     a.nkv = nkv;
     a.dh = dh;
     if (ws_kv) {
-        a.k = blk->kws;
-        a.v = blk->vws;
+        a.k = wk.kws;
+        a.v = wk.vws;
         a.kv_bg = (long)s_stride * dh;
     } else {
         a.k = kv->k;
@@ -785,20 +854,22 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     }
     mark(2);
     if (dt == Elem::F32) e = lb::attn_simple(a, s);
-    else if (S == 1) e = lb::attn_decode(op, dt, a, blk->part, mt, s);
+    else if (S == 1) e = lb::attn_decode(op, dt, a, wk.part, mt, s);
     else e = lb::attn_prefill(op, ws_kv ? op : dt, a, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "attention: %s", hipGetErrorString(e));
 
     mark(3);
-    if (dec) e = lb::decode_resid(op, dt, o, L.wt_o, M, d, blk->qd, x, blk->h, ws, s);
-    else e = lb::gemm_resid(op, dt, o, L.w_o, M, d, blk->qd, x, blk->h, ws, s);
+    if (dec) e = lb::decode_resid(op, dt, o, L.wt_o, M, d, blk->qd, x, wk.h, ws, s);
+    else e = lb::gemm_resid(op, dt, o, L.w_o, M, d, blk->qd, x, wk.h, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "o projection: %s", hipGetErrorString(e));
     mark(4);
-    e = lb::launch_rmsnorm(Elem::F32, op, blk->h, L.g2, n2, M, d, (float)c.norm_eps, dec_ffn ? mt : 0, s);
+    e = lb::launch_rmsnorm(Elem::F32, op, wk.h, L.g2, n2, M, d, (float)c.norm_eps, dec_ffn ? mt : 0, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "rmsnorm_2: %s", hipGetErrorString(e));
-    blk->last_mt = mt;
-    blk->last_ffn_mt = dec_ffn ? mt : 0;
-    blk->last_m = M;
+    if (stage_state) {
+        blk->last_mt = mt;
+        blk->last_ffn_mt = dec_ffn ? mt : 0;
+        blk->last_m = M;
+    }
     if (moe) {
         lb_status st = run_moe_ffn(blk, L, n2, z, B * S, out, ws, s, mark);
         if (st == LB_OK) mark(7);
@@ -809,8 +880,8 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     else e = lb::gemm_swiglu(op, n2, L.w_gu, M, 2 * dff, d, z, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "gate/up projection: %s", hipGetErrorString(e));
     mark(6);
-    if (dec) e = lb::decode_out(op, dt, z, L.wt_down, M, d, dff, blk->h, out, ws, s);
-    else e = lb::gemm_out(op, dt, z, L.w_down, M, d, dff, blk->h, out, ws, s);
+    if (dec) e = lb::decode_out(op, dt, z, L.wt_down, M, d, dff, wk.h, out, ws, s);
+    else e = lb::gemm_out(op, dt, z, L.w_down, M, d, dff, wk.h, out, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "down projection: %s", hipGetErrorString(e));
     mark(7);
     return LB_OK;
@@ -895,7 +966,7 @@ static lb_status forward_checked(lb_block* blk, const void* x, int32_t batch, in
     st = make_positions(blk, batch, seq_len, start_pos, starts, nullptr, kv->max_seq_len, &sp);
     if (st != LB_OK) return st;
     return on_device(blk, [&] {
-        return run_forward(blk, blk->lw, x, batch, seq_len, sp, kv, out, (hipStream_t)stream);
+        return run_forward(blk, blk->lw, x, batch, seq_len, sp, kv, out, (hipStream_t)stream, handle_workspace(blk));
     });
 }
 
@@ -913,6 +984,55 @@ extern "C" lb_status llama_block_forward_ragged(lb_block* blk, const void* x, in
         return fail(blk, LB_ERR_INVALID_ARG, "start_pos must be non-NULL");
     }
     return forward_checked(blk, x, batch, seq_len, 0, start_pos, kv, out, stream);
+}
+
+// Decode forward on the static scratch: the buffers of a decode step of at most
+// kDecodeRows tokens, each 256-byte aligned, then the split-K partials in what
+// is left.
+extern "C" lb_status llama_block_forward_decode_static(lb_block* blk, const void* x, int32_t batch,
+                                                       int32_t start_pos, const lb_kv_cache* kv, void* out,
+                                                       void* stream) {
+    if (!blk) return LB_ERR_INVALID_ARG;
+    blk->err.clear();
+    if (blk->dt != Elem::BF16 || blk->moe_E > 0)
+        return fail(blk, LB_ERR_UNSUPPORTED, "the static-scratch decode runs dense bf16 blocks only");
+    lb_status st = check_call(blk, x, batch, 1, kv, out);
+    if (st != LB_OK) return st;
+    if (batch > kDecodeRows)
+        return fail(blk, LB_ERR_UNSUPPORTED, "the static-scratch decode takes at most %d sequences (got %d)",
+                    kDecodeRows, batch);
+    lb::SeqPos sp;
+    st = make_positions(blk, batch, 1, start_pos, nullptr, nullptr, kv->max_seq_len, &sp);
+    if (st != LB_OK) return st;
+    const lb_config& c = blk->cfg;
+    const size_t eo = esz(blk->op), R = kDecodeRows;
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const size_t sz[7] = {al(R * c.d_model * eo), al(R * blk->qd * eo), al(R * blk->qd * eo),
+                          al(R * c.d_model * 4), al(R * c.d_model * eo), al(R * c.d_ff * eo),
+                          al(lb::decode_partials_floats(batch, c.n_heads, c.d_head, c.max_seq_len) * 4)};
+    size_t need = 0;
+    for (size_t b : sz) need += b;
+    if (need > (size_t)LB_STATIC_SCRATCH_BYTES)
+        return fail(blk, LB_ERR_UNSUPPORTED,
+                    "a decode step of this block needs %zu bytes of scratch, more than the static %zu", need,
+                    (size_t)LB_STATIC_SCRATCH_BYTES);
+    char* base = (char*)(blk->dev >= 0 && blk->dev < kMaxDevices ? g_scratch[blk->dev].load(std::memory_order_acquire)
+                                                                 : nullptr);
+    if (!base) return fail(blk, LB_ERR_HIP, "the static scratch of device %d is not available", blk->dev);
+    Workspace w;
+    char* p = base;
+    w.at_n1 = p, p += sz[0];
+    w.q = p, p += sz[1];
+    w.at_o = p, p += sz[2];
+    w.h = (float*)p, p += sz[3];
+    w.at_n2 = p, p += sz[4];
+    w.at_z = p, p += sz[5];
+    w.part = (float*)p, p += sz[6];
+    w.gpart = (float*)p;
+    w.gpart_cap = ((size_t)LB_STATIC_SCRATCH_BYTES - need) / sizeof(float);
+    return on_device(blk, [&] {
+        return run_forward(blk, blk->lw, x, batch, 1, sp, kv, out, (hipStream_t)stream, w, false);
+    });
 }
 
 // ---- stacks of blocks ------------------------------------------------------------
@@ -1012,7 +1132,7 @@ static lb_status stack_run(lb_stack* sk, const void* x, int B, int S, const lb::
     const void* in = x;
     for (size_t l = 0; l < sk->layers.size(); ++l) {
         void* o = hidden ? (char*)hidden + l * act : sk->act[l & 1];
-        lb_status st = run_forward(blk, sk->layers[l], in, B, S, sp, &kv[l], o, s);
+        lb_status st = run_forward(blk, sk->layers[l], in, B, S, sp, &kv[l], o, s, handle_workspace(blk));
         if (st != LB_OK) return st;
         in = o;
     }

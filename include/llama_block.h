@@ -189,6 +189,26 @@ lb_status llama_block_forward_ragged(lb_block* blk, const void* x, int32_t batch
                                      int32_t seq_len, const int32_t* start_pos,
                                      const lb_kv_cache* kv, void* out, void* stream);
 
+/* For callers that cannot allocate device memory while they run (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * llama_block_forward for one decode step (seq_len == 1) whose scratch
+ * buffers (normalised rows, q, the attention output and its split partials,
+ * the fp32 residual, SiLU(gate)*up, split-K partials) live in one static device
+ * array of LB_STATIC_SCRATCH_BYTES bytes per GPU, held by the library until
+ * the process ends, instead of the handle's workspace.  It calls no
+ * allocator.  Arguments as llama_block_forward with seq_len = 1; bf16 dense
+ * blocks only, batch <= 64, and a block whose decode buffers do not fit the
+ * array is refused with LB_ERR_UNSUPPORTED (the 70B width fits at 64
+ * sequences).  The result equals llama_block_forward's for the same call.
+ * Every call on one GPU shares that array, whatever the handle, and the array
+ * keeps the last call's contents: calls that overlap on one GPU (other
+ * streams, other threads) race, and the caller must serialise them.  The
+ * stage buffers that llama_block_copy_stage reads are not written. */
+#define LB_STATIC_SCRATCH_BYTES (32u << 20)
+lb_status llama_block_forward_decode_static(lb_block* blk, const void* x, int32_t batch,
+                                            int32_t start_pos, const lb_kv_cache* kv, void* out,
+                                            void* stream);
+
 /* ---- Mixture-of-experts blocks ----------------------------------------------
  * The FFN becomes a mixture of experts with a shared expert ("Llama 4 From
  * Scratch", The idea: N expert FFNs, a router that sends each token to its
