@@ -11,8 +11,11 @@ Default run (N = 1):
     headline `value` in tokens/s;
   * decode:  Llama-3-8B-width block, 32 sequences x 1 new token at position
     8191 over 8191 cached positions -> reported under "decode" (us/step);
-  * cpu_baseline: the fp64 oracle on the host cores over a bounded sample of
-    the prefill workload (the first tokens of one sequence).
+  * configs: the tiny fp32 block (latency), the SmolLM2-width prefill and the
+    70B-width prefill, each with its stage times and roofline;
+  * cpu_baseline: the fp64 oracle on the host cores on every row of the
+    prefill workload, and per workload under cpu_baselines (the 70B width on
+    its first 256 tokens).
 Per-stage GPU times come from the library's HIP-event profiler on the
 forward's stream: a first pass times every stage and finds the dominant one;
 the timed region of `value` then records events only around that stage, whose
@@ -85,21 +88,28 @@ def stage_work(w, positions=None, active_experts=None):
 PER_CALL = 50  # forwards timed one by one for the median / p10 / p90
 
 
-def run_gpu(w, steps, warmup, positions=None):
+def make_tensors(w, on_device=False):
+    """The workload's tensors: drawn on the host by workloads.generate (the
+    oracle's inputs), or on the device for model-sized blocks (same
+    distributions, other random streams) when on_device."""
+    import workloads
+    if w.n_experts > 0 or on_device:
+        g = workloads.generate_stack_on_device(w, 1)
+        return dict(g["layers"][0], x=g["x"])
+    return workloads.generate(w)
+
+
+def run_gpu(w, steps, warmup, positions=None, tensors=None, per_call=True):
     import torch
 
     import decoder_only_transformer_amd as lbmod
-    import workloads
 
     cap = (w.capacity + 7) // 8 * 8
     cfg = lbmod.make_config(w.d, w.H, w.n_kv, w.d_head, w.d_ff, w.M, cap, w.theta, w.eps, w.dtype)
+    t = tensors if tensors is not None else make_tensors(w)
     if w.n_experts > 0:
-        # billions of expert weights: drawn on the device
-        g = workloads.generate_stack_on_device(w, 1)
-        t = dict(g["layers"][0], x=g["x"])
         blk = lbmod.LlamaMoeBlock(cfg, t, w.moe)
     else:
-        t = workloads.generate(w)
         blk = lbmod.LlamaBlock(cfg, {n: t[n].to("cuda") for n in lbmod.WEIGHT_NAMES})
     k, v = lbmod.new_kv_cache(w.B, w.n_kv, cap, w.d_head, w.torch_dtype)
     if w.start_pos > 0:
@@ -108,6 +118,7 @@ def run_gpu(w, steps, warmup, positions=None):
     x = t["x"].to("cuda")
     out = torch.empty_like(x)
     del t
+    torch.cuda.empty_cache()
     sp = list(positions) if positions is not None else w.start_pos
     for _ in range(warmup):
         blk.forward(x, sp, (k, v), out)
@@ -143,9 +154,9 @@ def run_gpu(w, steps, warmup, positions=None):
     #    and after a 512 MB read that evicts the 256 MB MALL and the L2s (a
     #    read, so that no dirty lines are left to be written back during the
     #    timed call)
-    per_call = {"calls": PER_CALL}
+    calls = {"calls": PER_CALL}
     scratch = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    for tag, flush in (("", False), ("flushed_", True)):
+    for tag, flush in ((("", False), ("flushed_", True)) if per_call else ()):
         ev = []
         for _ in range(PER_CALL):
             if flush:
@@ -159,17 +170,17 @@ def run_gpu(w, steps, warmup, positions=None):
         torch.cuda.synchronize()
         d = sorted(a.elapsed_time(b) for a, b in ev)
         q = lambda f: d[min(len(d) - 1, int(round(f * (len(d) - 1))))]
-        per_call.update({tag + "median_ms": round(q(0.5), 4), tag + "p10_ms": round(q(0.1), 4),
-                         tag + "p90_ms": round(q(0.9), 4)})
+        calls.update({tag + "median_ms": round(q(0.5), 4), tag + "p10_ms": round(q(0.1), 4),
+                      tag + "p90_ms": round(q(0.9), 4)})
     del scratch
     active = None
     if w.n_experts > 0:
         active = int(torch.unique(blk.routing(w.M)[0]).numel())
-        per_call["active_experts"] = active
+        calls["active_experts"] = active
     blk.close()
     del k, v, x, out
     torch.cuda.empty_cache()
-    return ms, avg_all, dom, avg_dom[dom], ms_plain, ms_all, per_call
+    return ms, avg_all, dom, avg_dom[dom], ms_plain, ms_all, calls
 
 
 def run_stack(w, n_layers, steps, warmup):
@@ -326,24 +337,46 @@ def vendor_gemm(w, reps=20):
     return out
 
 
-def cpu_baseline(w, tokens):
-    """The fp64 oracle, as it stands, on the host: the first `tokens` tokens of
-    one sequence of workload w (full block weights)."""
-    import workloads
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, tensors, rows=None, repeats=1):
+    """The fp64 oracle, as it stands, on the host: one forward of workload w on
+    `tensors` (its own inputs, cache prefix included), every token row or the
+    flat token rows `rows` (the oracle then computes only what those rows
+    see), timed `repeats` times (median).  Tokens/s counts the rows computed."""
     import oracle
-    ws = workloads.with_overrides(w, B=1, S=tokens)
-    t = workloads.generate(ws)
-    cfg = oracle.cfg_of(ws)
-    xs = t["x"]
-    wts = {n: oracle._f64(t[n]) for n in oracle.WEIGHT_NAMES}
-    kc, vc = oracle.empty_cache(ws)
-    t0 = time.perf_counter()
-    oracle.block_forward(cfg, xs, wts, 0, kc, vc)
-    dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{w.name} weights, first {tokens} tokens of one sequence (B=1, S={tokens}), "
-                      f"fp64 naive loops"}
+    cfg = oracle.cfg_of(w)
+    wts = {n: oracle._f64(tensors[n]) for n in oracle.WEIGHT_NAMES}
+    x = oracle._f64(tensors["x"])
+    times = []
+    for _ in range(repeats):
+        kc, vc = oracle.empty_cache(w)
+        if w.start_pos > 0:
+            kc[:, :, :w.start_pos, :] = oracle._f64(tensors["k_prefix"])
+            vc[:, :, :w.start_pos, :] = oracle._f64(tensors["v_prefix"])
+        t0 = time.perf_counter()
+        oracle.block_forward(cfg, x, wts, w.start_pos, kc, vc, rows=rows)
+        times.append(time.perf_counter() - t0)
+        del kc, vc
+    times.sort()
+    dt = times[len(times) // 2]
+    n = w.M if rows is None else len(rows)
+    sample = (f"{w.name}: all {n} token rows (B={w.B}, S={w.S}, start_pos={w.start_pos})"
+              if rows is None else
+              f"{w.name}: the first {n} token rows of the {w.S}-token sequence (the oracle computes "
+              f"only what they see)")
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3), "runs": repeats,
+            "sample": sample + ", fp64 naive loops"}
 
 
 def main():
@@ -355,12 +388,13 @@ def main():
     ap.add_argument("--decode-workload", default="llama3_8b_decode")
     ap.add_argument("--decode-steps", type=int, default=0, help="default: 5 x --steps")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the model-level stack decode")
     ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts block")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged decode")
     ap.add_argument("--no-vendor", action="store_true", help="skip the vendor-library GEMM figures")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny fp32, SmolLM2-width and 70B-width entries")
     ap.add_argument("--copy-only", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -382,7 +416,8 @@ def main():
 
     w = workloads.get(args.workload)
     log(f"[bench] prefill {w.name}: warmup {args.warmup}, steps {args.steps}")
-    ms, avg, dom, dom_ms, ms_plain, ms_all, per_call = run_gpu(w, args.steps, args.warmup)
+    t_pre = make_tensors(w)
+    ms, avg, dom, dom_ms, ms_plain, ms_all, per_call = run_gpu(w, args.steps, args.warmup, tensors=t_pre)
     roof, stages = roofline(w, avg, dom, dom_ms, "mfma")
     roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     total_flops = sum(v["flops"] for v in stage_work(w).values())
@@ -421,7 +456,8 @@ def main():
         wd = workloads.get(args.decode_workload)
         dsteps = args.decode_steps or 5 * args.steps
         log(f"[bench] decode {wd.name}: warmup {args.warmup}, steps {dsteps}")
-        dms, davg, ddom, ddom_ms, dms_plain, dms_all, dper_call = run_gpu(wd, dsteps, args.warmup)
+        t_dec = make_tensors(wd)
+        dms, davg, ddom, ddom_ms, dms_plain, dms_all, dper_call = run_gpu(wd, dsteps, args.warmup, tensors=t_dec)
         droof, dstages = roofline(wd, davg, ddom, ddom_ms, "hbm")
         droof["traffic"] = measured_traffic(wd.name, droof["kernel"])
         total_bytes = sum(v["bytes"] for v in stage_work(wd).values())
@@ -457,7 +493,7 @@ def main():
         # batch): positions spread evenly from 1024 to the workload's last one
         pos = [1024 + (wd.start_pos - 1024) * b // max(wd.B - 1, 1) for b in range(wd.B)]
         log(f"[bench] ragged decode: positions {pos[0]}..{pos[-1]}")
-        rms, ravg, rdom, rdom_ms, rms_plain, rms_all, _ = run_gpu(wd, dsteps, args.warmup, pos)
+        rms, ravg, rdom, rdom_ms, rms_plain, rms_all, _ = run_gpu(wd, dsteps, args.warmup, pos, tensors=t_dec)
         rroof, rstages = roofline(wd, ravg, rdom, rdom_ms, "hbm", pos)
         rroof["traffic"] = None  # counters are taken for the uniform decode only
         rbytes = sum(v["bytes"] for v in stage_work(wd, pos).values())
@@ -516,10 +552,59 @@ def main():
                 "hbm_frac": round(sbytes / (min(se, sg) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
             log(f"[bench] stack decode {name}: eager {se:.3f} ms, graph {sg:.3f} ms")
 
+    # the other workloads of the benchmark suite: the tiny fp32 block (latency),
+    # the SmolLM2-width prefill and the 70B-width prefill (weights drawn on the
+    # device), each with its stage times and roofline
+    extra = {}
+    if not args.no_configs:
+        result["configs"] = []
+        for name, bound, steps, on_dev in (("tiny_f32", "latency", 5 * args.steps, False),
+                                           ("smollm2_135m_prefill", "mfma", 5 * args.steps, False),
+                                           ("llama3_70b_prefill", "mfma", max(args.steps // 2, 3), True)):
+            wc = workloads.get(name)
+            log(f"[bench] {name}: warmup {args.warmup}, steps {steps}")
+            tc = make_tensors(wc, on_device=on_dev)
+            cms, cavg, cdom, cdom_ms, cms_plain, _, _ = run_gpu(wc, steps, args.warmup, tensors=tc, per_call=False)
+            work = stage_work(wc)
+            fl = sum(v["flops"] for v in work.values())
+            entry = {"workload": name, "B": wc.B, "S": wc.S, "start_pos": wc.start_pos, "d": wc.d, "H": wc.H,
+                     "n_kv": wc.n_kv, "d_head": wc.d_head, "d_ff": wc.d_ff, "dtype": wc.dtype, "steps": steps,
+                     "ms_per_step": round(cms, 4), "us_per_step": round(cms * 1e3, 2),
+                     "ms_per_step_without_events": round(cms_plain, 4),
+                     "tokens_per_s": round(wc.M / (cms * 1e-3), 1)}
+            if bound == "mfma":
+                croof, cstages = roofline(wc, cavg, cdom, cdom_ms, "mfma")
+                entry.update({"block_tflops": round(fl / (cms * 1e-3) / 1e12, 2),
+                              "block_mfma_frac": round(fl / (cms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                              "roofline": croof, "stages": cstages})
+            else:
+                _, cstages = roofline(wc, cavg, cdom, cdom_ms, "mfma")
+                entry.update({"bound": "latency (1.5 MFLOP per call)", "stages": cstages})
+            result["configs"].append(entry)
+            extra[name] = tc
+            log(f"[bench] {name}: {cms * 1e3:.1f} us/step")
+
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        # the fp64 oracle on the host cores, per workload: the headline one on
+        # every row of the 8B-width prefill, the others beside their GPU entries
+        log("[bench] cpu baseline: oracle on every row of the 8B-width prefill")
+        result["cpu_baseline"] = cpu_baseline(w, t_pre)
         log(f"[bench] cpu baseline {result['cpu_baseline']['seconds']} s")
+        cb = {"llama3_8b_prefill": result["cpu_baseline"]}
+        if not args.no_decode:
+            log("[bench] cpu baseline: decode (median of 3)")
+            cb[wd.name] = cpu_baseline(wd, t_dec, repeats=3)
+        for name, tc in extra.items():
+            wc = workloads.get(name)
+            if wc.M <= 4096 and name != "llama3_70b_prefill":
+                log(f"[bench] cpu baseline: {name} (median of 3)")
+                cb[name] = cpu_baseline(wc, tc, repeats=3)
+            else:
+                log(f"[bench] cpu baseline: {name}, first 256 tokens")
+                cb[name] = cpu_baseline(wc, tc, rows=list(range(256)))
+        result["cpu_baselines"] = cb
+        for name, v in cb.items():
+            log(f"[bench] cpu baseline {name}: {v['seconds']} s, {v['value']} tokens/s")
 
     print(json.dumps(result), flush=True)
 

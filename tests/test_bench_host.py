@@ -87,3 +87,16 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_times_the_oracle_on_the_workload():
+    """The CPU baseline runs the oracle on the workload's own tensors: every row,
+    or a stated row sample whose tokens/s counts only those rows."""
+    import workloads
+    w = workloads.with_overrides(workloads.get("tiny_f32"), B=2, S=8, start_pos=4, max_seq=12)
+    t = workloads.generate(w)
+    full = bench.cpu_baseline(w, t, repeats=3)
+    assert full["kind"] == "oracle" and full["runs"] == 3 and full["cores"] >= 1
+    assert full["value"] > 0 and "all 16 token rows" in full["sample"] and full["cpu_model"]
+    part = bench.cpu_baseline(w, t, rows=[0, 1, 2])
+    assert "first 3 token rows" in part["sample"]
