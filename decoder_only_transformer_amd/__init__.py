@@ -29,7 +29,8 @@ EXPORTS = ("llama_block_init", "llama_block_forward", "llama_block_forward_ragge
            "llama_stack_graph_create", "llama_stack_graph_launch", "llama_stack_graph_destroy",
            "llama_stack_destroy", "llama_stack_num_layers", "llama_stack_last_error",
            "llama_moe_block_init", "llama_block_copy_routing", "llama_block_operand_type",
-           "llama_stack_operand_type", "llama_block_forward_decode_static")
+           "llama_stack_operand_type", "llama_block_forward_decode_static", "llama_block_footprint",
+           "llama_block_device_bytes", "llama_stack_device_bytes")
 MAX_STACK_LAYERS = 1024
 STAGE_NAMES = ("rmsnorm_1", "qkv_rope_append", "attention", "o_proj_residual", "rmsnorm_2",
                "gate_up_swiglu", "down_residual")
@@ -58,6 +59,11 @@ class LbKVCache(ctypes.Structure):
 
 
 WEIGHT_NAMES = [f[0] for f in LbWeights._fields_]
+
+
+class LbFootprint(ctypes.Structure):
+    _fields_ = [("weights", ctypes.c_uint64), ("workspace", ctypes.c_uint64),
+                ("init_staging", ctypes.c_uint64)]
 
 
 class LbMoeConfig(ctypes.Structure):
@@ -146,6 +152,12 @@ def lib() -> ctypes.CDLL:
         L.llama_block_operand_type.restype = ctypes.c_int
         L.llama_stack_operand_type.argtypes = [vp]
         L.llama_stack_operand_type.restype = ctypes.c_int
+        L.llama_block_footprint.argtypes = [ctypes.POINTER(LbConfig), i32, ctypes.POINTER(LbFootprint)]
+        L.llama_block_footprint.restype = ctypes.c_int
+        L.llama_block_device_bytes.argtypes = [vp]
+        L.llama_block_device_bytes.restype = ctypes.c_uint64
+        L.llama_stack_device_bytes.argtypes = [vp]
+        L.llama_stack_device_bytes.restype = ctypes.c_uint64
         L.llama_stack_last_error.argtypes = [vp]
         L.llama_stack_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -262,6 +274,23 @@ def llama_block_operand_type(handle: int) -> str:
 
 def llama_stack_operand_type(handle: int) -> str:
     return ELEM_NAMES[lib().llama_stack_operand_type(handle)]
+
+
+def llama_block_footprint(cfg: LbConfig, n_layers: int = 0) -> dict:
+    """Device bytes of a block (n_layers 0) or a stack of n_layers blocks,
+    from the config alone: {"weights", "workspace", "init_staging"}."""
+    fp = LbFootprint()
+    st = lib().llama_block_footprint(ctypes.byref(cfg), int(n_layers), ctypes.byref(fp))
+    _check(None, st, "llama_block_footprint")
+    return {"weights": fp.weights, "workspace": fp.workspace, "init_staging": fp.init_staging}
+
+
+def llama_block_device_bytes(handle: int) -> int:
+    return int(lib().llama_block_device_bytes(handle))
+
+
+def llama_stack_device_bytes(handle: int) -> int:
+    return int(lib().llama_stack_device_bytes(handle))
 
 
 def llama_block_stage_info(handle: int, stage: str) -> Tuple[str, int]:
@@ -430,6 +459,10 @@ class LlamaBlock:
     def operand_type(self) -> str:
         return llama_block_operand_type(self.handle)
 
+    @property
+    def device_bytes(self) -> int:
+        return llama_block_device_bytes(self.handle)
+
     def stage(self, name: str, rows: int):
         import torch
         elem, cols = llama_block_stage_info(self.handle, name)
@@ -461,6 +494,10 @@ class LlamaStack:
     @property
     def n_layers(self) -> int:
         return llama_stack_num_layers(self.handle)
+
+    @property
+    def device_bytes(self) -> int:
+        return llama_stack_device_bytes(self.handle)
 
     def forward(self, x, start_pos, kv_list, out, hidden=None, stream=None):
         llama_stack_forward(self.handle, x, start_pos, kv_list, out, hidden, stream)

@@ -1,8 +1,11 @@
 // GEMM kernels: C[M][N] = A[M][K] . W[N][K]^T with fp32 accumulation, results
 // handed to an epilogue (epilogues.h) in 8-column chunks.
 //
-//  gemm_big_kernel    prefill, large: 256 x 256 tiles, 16x16x32 MFMA,
-//                     four-stage LDS ring of direct-to-LDS loads
+//  gemm_big2_kernel   prefill, large: 256 x 256 tiles, 64-deep k-steps,
+//                     16x16x32 MFMA, two 64 KB LDS stages, weights in the
+//                     k-step tiled layout
+//  gemm_big_kernel    grouped expert GEMMs (row-major expert weights):
+//                     256 x 256 tiles, four-stage LDS ring
 //  gemm_mfma_kernel   prefill, small: 32x32x16 MFMA tiles, direct-to-LDS
 //                     loads, LDS double buffering
 //  gemm_skinny_kernel decode (M <= 64): 16x16x32 MFMA, split-K over waves
@@ -100,7 +103,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // elements.
 // NTW: the W loads carry the non-temporal hint (weights read by one row
 // tile only).
-template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi, bool NTW = false, int STAGES = 2>
+// WT: W is in the k-step tiled layout (lb_device.h; N % 16 == 0): the W
+// stage is BN/16 row tiles x 2 pieces of 1 KB, each one direct-to-LDS load,
+// kept in LDS in piece order (piece rt * 2 + h), whose 16-lane groups read 256
+// contiguous bytes for the MFMA operand.
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi, bool NTW = false, int STAGES = 2,
+          bool WT = false>
 __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T* __restrict__ W, int M,
                                                int N, int K, Epi epi, int m0, int n0, T* lds) {
     typedef typename vec8<T>::type V8;
@@ -130,13 +138,21 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
         const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
         aoff[i] = (unsigned)(((size_t)(min(m0 + row, M - 1) - m0) * K + c * 8) * sizeof(T));
     }
+    const int nks32 = K / 32;
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-        const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
-        boff[i] = (unsigned)(((size_t)(min(n0 + row, N - 1) - n0) * K + c * 8) * sizeof(T));
+        if constexpr (WT) {
+            // piece q = i*NW + wave of the stage: row tile q/2, k half q%2
+            const int q = i * NW + wave, rt = min((n0 >> 4) + (q >> 1), (N >> 4) - 1) - (n0 >> 4);
+            boff[i] = (unsigned)((((size_t)rt * nks32 + (q & 1)) * 512 + lane * 8) * sizeof(T));
+        } else {
+            const int p = (i * NW + wave) * 64 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+            boff[i] = (unsigned)(((size_t)(min(n0 + row, N - 1) - n0) * K + c * 8) * sizeof(T));
+        }
     }
     const T* a0 = A + (size_t)m0 * K;
-    const T* w0 = W + (size_t)n0 * K;
+    const T* w0 = WT ? W + (size_t)(n0 >> 4) * nks32 * 512 : W + (size_t)n0 * K;
+    constexpr int WSTEP = WT ? 2 * 512 : BK;  // elements from one k-step of W to the next
     const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)lds;
     const int nk = K / BK;
     // k-steps past the end reload the last one into a stage nobody reads
@@ -149,7 +165,7 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
             lds_dma16_s(a0 + ks * BK, aoff[i], la + (unsigned)((i * NW + wave) * 64 * 8 * (int)sizeof(T)));
 #pragma unroll
         for (int i = 0; i < BCH; ++i)
-            lds_dma16_s<NTW>(w0 + ks * BK, boff[i], lb + (unsigned)((i * NW + wave) * 64 * 8 * (int)sizeof(T)));
+            lds_dma16_s<NTW>(w0 + (size_t)ks * WSTEP, boff[i], lb + (unsigned)((i * NW + wave) * 64 * 8 * (int)sizeof(T)));
     };
 
     f32x16 acc[TM][TN];
@@ -183,7 +199,11 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = wn * WN + j * 32 + (lane & 31);
-                bfr[j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
+                if constexpr (WT)
+                    bfr[j] = *reinterpret_cast<const V8*>(lb + ((row >> 4) * 2 + (kc >> 2)) * 512 +
+                                                          ((kc & 3) * 16 + (row & 15)) * 8);
+                else
+                    bfr[j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
@@ -226,7 +246,7 @@ __device__ __forceinline__ void gemm_mfma_tile(const T* __restrict__ A, const T*
     }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi>
+template <typename T, int BM, int BN, int WM, int WN, int NW, class Epi, bool WT = false>
 __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict__ A,
                                                             const T* __restrict__ W, int M, int N,
                                                             int K, Epi epi) {
@@ -245,7 +265,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_mfma_kernel(const T* __restrict_
     const int in_group = bid % per_group;
     const int tm = first_m + in_group % gsize;
     const int tn = in_group / gsize;
-    gemm_mfma_tile<T, BM, BN, WM, WN, NW, Epi>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
+    gemm_mfma_tile<T, BM, BN, WM, WN, NW, Epi, false, 2, WT>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
 }
 
 // Any epilogue applied to rows counted from m_off (the tile sees row m, the
@@ -501,6 +521,179 @@ __global__ void __launch_bounds__(256) gemm_big_grouped_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------------------------------
+// Large prefill GEMM with 64-deep k-steps: 256 x 256 tiles, four wavefronts in
+// a 2 x 2 grid (128 x 128 each, 16x16x32 MFMAs, accumulators in AGPRs), two
+// LDS stages of 64 KB.  A stage of A is 256 rows x 128 bytes, loaded by
+// direct-to-LDS loads of whole cache lines (eight 128-byte rows per wavefront
+// instruction; chunk index XORed by (row / 2) & 7 in LDS, free of bank
+// conflicts for the operand read).  With WT, W is in the k-step tiled layout
+// (lb_device.h; N % 16 == 0): a stage is 16 row tiles x 2 pieces of 1 KB, one
+// load each, kept in piece order, whose operand reads are 1 KB contiguous.
+// Each k-step is two sub-steps of 64 MFMAs.  Operands are double-buffered in
+// registers: during one sub-step the wavefront reads the next sub-step's
+// operands (groups 0..6 of its 8 MFMA groups) into the other buffer.  One
+// barrier per k-step, between its sub-steps: every wavefront's reads of stage
+// kt are complete (sub-step 1's operands are in registers) and stage kt+1 has
+// landed; sub-step 1 then reads stage kt+1 and its first four groups issue
+// the loads of stage kt+2 into stage kt's buffer.  Rows beyond M / N are
+// clamped to the last valid row.  K % 64 == 0.
+// ------------------------------------------------------------------------------------
+template <typename T>
+constexpr int big2_tile_lds() { return 2 * 512 * 64; }
+
+template <typename T, class Epi, bool WT>
+__device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T* __restrict__ W, int M, int N,
+                                               int K, Epi epi, int m0, int n0, T* lds) {
+    typedef typename vec8<T>::type V8;
+    constexpr int BM = 256, BN = 256, BK = 64, NW = 4, NT = 256, WM = 128, WN = 128;
+    constexpr int TI = 8, TJ = 8;
+    constexpr int SA = BM * BK, SB = BN * BK, STG = SA + SB;   // elements per stage
+    constexpr int NA = SA / 8 / NT, NB = SB / 8 / NT;          // loads per thread per stage (8 + 8)
+    constexpr int ND = NA + NB;
+    constexpr int EPR = 64, CPAD = BN + 4;
+    static_assert(2 * STG == big2_tile_lds<T>(), "LDS size");
+    static_assert(EPR * CPAD * 4 <= 2 * STG * (int)sizeof(T), "epilogue stage fits");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nks32 = K / 32;
+    // load d: the wavefront's instruction d of a stage fills 64 consecutive
+    // 16-byte slots ((d % NA) * NW + wave) * 64 of its operand, lane l the slot l
+    unsigned voff[ND], ldst[ND];
+    const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)lds;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+        const bool isa = d < NA;
+        const int slot0 = ((isa ? d : d - NA) * NW + wave) * 64;
+        if (isa || !WT) {
+            const int p = slot0 + lane, row = p >> 3, c = (p & 7) ^ ((row >> 1) & 7);
+            const int r = isa ? min(m0 + row, M - 1) - m0 : min(n0 + row, N - 1) - n0;
+            voff[d] = (unsigned)(((size_t)r * K + c * 8) * sizeof(T));
+        } else {
+            // piece q = slot0 / 64 of the stage: row tile q / 2, k half q % 2
+            const int q = slot0 >> 6, rt = min((n0 >> 4) + (q >> 1), (N >> 4) - 1) - (n0 >> 4);
+            voff[d] = (unsigned)((((size_t)rt * nks32 + (q & 1)) * 512 + lane * 8) * sizeof(T));
+        }
+        ldst[d] = lds0 + (unsigned)(((isa ? 0 : SA) + slot0 * 8) * (int)sizeof(T));
+    }
+    const T* abase = A + (size_t)m0 * K;
+    const T* wbase = WT ? W + (size_t)(n0 >> 4) * nks32 * 512 : W + (size_t)n0 * K;
+    constexpr int WSTEP = WT ? 2 * 512 : BK;  // elements from one k-step of W to the next
+    const int nk = K / BK;
+    // k-steps past the end reload the last one into a stage nobody reads
+    auto dma = [&](int kstep, int d) {
+        const size_t ks = (size_t)(kstep < nk ? kstep : nk - 1);
+        lds_dma16_s(d < NA ? abase + ks * BK : wbase + ks * WSTEP, voff[d],
+                    ldst[d] + (unsigned)((kstep & 1) * STG * (int)sizeof(T)));
+    };
+    f32x4 acc[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    V8 af[2][TI], bf[2][TJ];
+    // operand item it (0..7: A row tile, 8..15: W column tile) of sub-step s
+    // (0/1) of stage kstep, into register buffer fb
+    auto rd = [&](int kstep, int s, int fb, int it) {
+        const T* st = lds + (kstep & 1) * STG;
+        const int f = it < TI ? it : it - TI;
+        const int kc = s * 4 + (lane >> 4);
+        if (it < TI) {
+            const int row = wm * WM + f * 16 + (lane & 15);
+            af[fb][f] = *reinterpret_cast<const V8*>(st + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
+        } else if constexpr (WT) {
+            bf[fb][f] = *reinterpret_cast<const V8*>(st + SA + ((wn * 8 + f) * 2 + s) * 512 + lane * 8);
+        } else {
+            const int row = wn * WN + f * 16 + (lane & 15);
+            bf[fb][f] = *reinterpret_cast<const V8*>(st + SA + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
+        }
+    };
+    // prologue: stages 0 and 1 in flight, stage 0 landed
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dma(0, d);
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dma(1, d);
+    wait_vm<ND>();
+    lds_barrier();
+#pragma unroll
+    for (int it = 0; it < TI + TJ; ++it) rd(0, 0, 0, it);
+    // one sub-step: 64 MFMAs on buffer fb in 8 groups; groups 0..6 read the
+    // next sub-step's operands (stage nstage, sub-step ns) into buffer fb^1;
+    // with loads, groups 0..3 issue the loads of stage kd
+    auto sub = [&](const int fb, const int nstage, const int ns, const bool loads, const int kd) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[fb][i], bf[fb][j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (loads && i < 4) {
+#pragma unroll
+                for (int d = 4 * i; d < 4 * i + 4; ++d) dma(kd, d);
+            }
+            if (i < TI - 1) {
+#pragma unroll
+                for (int it = i * 16 / 7; it < (i + 1) * 16 / 7; ++it) rd(nstage, ns, fb ^ 1, it);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int kt = 0; kt < nk; ++kt) {
+        sub(0, kt, 1, false, 0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wait_vm<0>();
+        lds_barrier();
+        sub(1, kt + 1, 0, true, kt + 2);
+    }
+    wait_vm<0>();
+    __syncthreads();
+
+    // Epilogue: stage EPR rows of the fp32 tile through LDS, then hand
+    // contiguous 8-column chunks to the epilogue.
+    float* cst = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int p = 0; p < BM / EPR; ++p) {
+        EpiPass<Epi, EPR, BN, NT, CPAD> pass;
+        pass.fetch(epi, tid, m0 + p * EPR, n0, M, N);
+        if (wm == (p * EPR) / WM) {
+#pragma unroll
+            for (int ii = 0; ii < EPR / 16; ++ii) {
+                const int i = ((p * EPR) % WM) / 16 + ii;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        cst[(ii * 16 + 4 * (lane >> 4) + r) * CPAD + wn * WN + j * 16 + (lane & 15)] = acc[i][j][r];
+            }
+        }
+        __syncthreads();
+        pass.finish(epi, cst, tid, m0 + p * EPR, n0, M, N);
+        __syncthreads();
+    }
+}
+
+template <typename T, class Epi, bool WT>
+__global__ void __launch_bounds__(256) gemm_big2_kernel(const T* __restrict__ A, const T* __restrict__ W, int M,
+                                                       int N, int K, Epi epi) {
+    constexpr int BM = 256, BN = 256;
+    __shared__ __attribute__((aligned(16))) T lds[big2_tile_lds<T>()];
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    // workgroups are dealt round-robin to the 8 XCDs: renumber so that each
+    // XCD runs a contiguous range of tiles, walked in groups of 8 tile-rows
+    // (column-major inside a group) so that neighbours share A and W panels
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (bid / per_group) * GM;
+    const int gsize = min(tiles_m - first_m, GM);
+    const int in_group = bid % per_group;
+    const int tm = first_m + in_group % gsize;
+    const int tn = in_group / gsize;
+    gemm_big2_tile<T, Epi, WT>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
+}
+
+// ------------------------------------------------------------------------------------
 // Decode GEMM for M <= 16*MT token rows: a weight-streaming kernel.  Grid
 // (N / (16*CT), KS), KW wavefronts per block.  Every wavefront owns the block's
 // 16*CT output columns (CT 16x16x32 MFMA column tiles); the KS blocks of a
@@ -515,7 +708,7 @@ __global__ void __launch_bounds__(256) gemm_big_grouped_kernel(const T* __restri
 // reduce_epilogue_kernel adds the KS partials in order (deterministic).
 // K % 32 == 0.
 // ------------------------------------------------------------------------------------
-template <typename T, int MT, int KW, int U, int CT, bool PARTIAL, class Epi, bool NT = false>
+template <typename T, int MT, int KW, int U, int CT, bool PARTIAL, class Epi, bool NT = false, bool WT = false>
 __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restrict__ A,
                                                               const T* __restrict__ W, int M,
                                                               int N, int K, int KS,
@@ -534,10 +727,15 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
     const int kcount = (int)((long)(ks + 1) * nks / KS) - kfirst;
     const int n_my = wave < kcount ? (kcount - wave + KW - 1) / KW : 0;
     const int nchunk = (n_my + U - 1) / U;
+    // WT: W in the k-step tiled layout (N % 16 == 0), lane l's 16 bytes of a
+    // k-step are l * 8 elements into the row tile's 1 KB piece
     const T* wp[CT];
+    constexpr int WSTEP = WT ? 512 : 32;  // elements from one k-step of a lane's weights to the next
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
-        wp[c] = W + (size_t)min(n0 + 16 * c + (lane & 15), N - 1) * K + 8 * (lane >> 4);
+    for (int c = 0; c < CT; ++c) {
+        if constexpr (WT) wp[c] = W + (size_t)min((n0 >> 4) + c, (N >> 4) - 1) * nks * 512 + lane * 8;
+        else wp[c] = W + (size_t)min(n0 + 16 * c + (lane & 15), N - 1) * K + 8 * (lane >> 4);
+    }
     const T* ap[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) ap[t] = A + (size_t)min(t * 16 + (lane & 15), M - 1) * K + 8 * (lane >> 4);
@@ -554,7 +752,7 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
         for (int u = 0; u < U; ++u) {
             const int kstep = min(kfirst + wave + (chunk * U + u) * KW, nks - 1);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) bw[s][u][c] = load_w<NT>(reinterpret_cast<const V8*>(wp[c] + kstep * 32));
+            for (int c = 0; c < CT; ++c) bw[s][u][c] = load_w<NT>(reinterpret_cast<const V8*>(wp[c] + (size_t)kstep * WSTEP));
 #pragma unroll
             for (int t = 0; t < MT; ++t) aa[s][u][t] = *reinterpret_cast<const V8*>(ap[t] + kstep * 32);
         }

@@ -19,13 +19,14 @@ size_t skinny_partials_floats(int max_m, int max_n) { return (size_t)kSkinnyMaxS
 // fits in the 256 MB MALL, where plain loads let it stay between calls.
 constexpr size_t kStreamMinBytes = size_t(40) << 20;
 
+// W is in the k-step tiled layout (N % 16 == 0, K % 32 == 0).
 template <typename T, int MT, bool NT, class Epi>
 static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const Epi& epi,
                              float* part, size_t part_cap, hipStream_t s) {
     if constexpr (MT <= 2) {
         if (N >= 128 * 192) {  // wide outputs: 128 columns per wavefront, no split
             const dim3 grid((N + 127) / 128, 1);
-            gemm_skinny_kernel<T, MT, 8, 1, 8, false, Epi, NT><<<grid, 512, 0, s>>>(A, W, M, N, K, 1, part, epi);
+            gemm_skinny_kernel<T, MT, 8, 1, 8, false, Epi, NT, true><<<grid, 512, 0, s>>>(A, W, M, N, K, 1, part, epi);
             return hipGetLastError();
         }
     }
@@ -37,10 +38,10 @@ static hipError_t run_skinny(const T* A, const T* W, int M, int N, int K, const 
     while (ks > 1 && (size_t)ks * M * N > part_cap) --ks;
     const dim3 grid(tiles, ks);
     if (ks == 1) {
-        gemm_skinny_kernel<T, MT, 4, 2, 4, false, Epi, NT><<<grid, 256, 0, s>>>(A, W, M, N, K, 1, part, epi);
+        gemm_skinny_kernel<T, MT, 4, 2, 4, false, Epi, NT, true><<<grid, 256, 0, s>>>(A, W, M, N, K, 1, part, epi);
         return hipGetLastError();
     }
-    gemm_skinny_kernel<T, MT, 4, 2, 4, true, Epi, NT><<<grid, 256, 0, s>>>(A, W, M, N, K, ks, part, epi);
+    gemm_skinny_kernel<T, MT, 4, 2, 4, true, Epi, NT, true><<<grid, 256, 0, s>>>(A, W, M, N, K, ks, part, epi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     reduce_epilogue_kernel<Epi><<<(M * (N / 8) + 255) / 256, 256, 0, s>>>(part, M, N, ks, epi);
@@ -137,10 +138,12 @@ static int device_cus() {
     return n;
 }
 
+// Prefill GEMM: A [M][K] row-major, W in the k-step tiled layout.
 template <typename T, class Epi>
 static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Epi& epi,
                            const SplitWs& ws, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
+    if (N % 16 != 0 || K % 64 != 0) return hipErrorInvalidValue;
     if (M <= 64) {
         const bool nt = (size_t)N * K * sizeof(T) >= kStreamMinBytes;
         if (M <= 16) return nt ? run_skinny<T, 1, true>(A, W, M, N, K, epi, ws.part, ws.cap, s)
@@ -151,7 +154,7 @@ static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Ep
                   : run_skinny<T, 4, false>(A, W, M, N, K, epi, ws.part, ws.cap, s);
     }
     const long tm = (M + 255) / 256, tn = (N + 255) / 256, t256 = tm * tn;
-    if (K % 64 == 0 && t256 >= 192) {
+    if (t256 >= 192) {
         // A CU runs one 256 x 256 tile at a time, so a launch takes
         // ceil(tiles / CUs) rounds.  When the last round would be at most
         // half full and made of whole tile columns (the 8B q/k/v product:
@@ -161,16 +164,17 @@ static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Ep
         const long rem = t256 % cus;
         if (rem > 0 && 2 * rem <= cus && rem % tm == 0 && rem / tm < tn) {
             const int n1 = (int)(tn - rem / tm) * 256, nt = N - n1;
-            gemm_big_kernel<T, 256, 256, Epi><<<(unsigned)(tm * (tn - rem / tm)), 256, 0, s>>>(A, W, M, n1, K, epi);
+            gemm_big2_kernel<T, Epi, true><<<(unsigned)(tm * (tn - rem / tm)), 256, 0, s>>>(A, W, M, n1, K, epi);
             const long t = (long)((M + 127) / 128) * ((nt + 127) / 128);
-            gemm_mfma_kernel<T, 128, 128, 64, 64, 4, EpiShift<Epi>><<<(unsigned)t, 256, 0, s>>>(
-                A, W + (size_t)n1 * K, M, nt, K, EpiShift<Epi>{epi, n1});
+            // the tiled weight rows from n1 on: row tile n1 / 16 onward
+            gemm_mfma_kernel<T, 128, 128, 64, 64, 4, EpiShift<Epi>, true><<<(unsigned)t, 256, 0, s>>>(
+                A, W + (size_t)(n1 / 16) * (K / 32) * 512, M, nt, K, EpiShift<Epi>{epi, n1});
         } else {
-            gemm_big_kernel<T, 256, 256, Epi><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
+            gemm_big2_kernel<T, Epi, true><<<(unsigned)t256, 256, 0, s>>>(A, W, M, N, K, epi);
         }
     } else {
         const long t = (long)((M + 127) / 128) * ((N + 127) / 128);
-        gemm_mfma_kernel<T, 128, 128, 64, 64, 4, Epi><<<(unsigned)t, 256, 0, s>>>(A, W, M, N, K, epi);
+        gemm_mfma_kernel<T, 128, 128, 64, 64, 4, Epi, true><<<(unsigned)t, 256, 0, s>>>(A, W, M, N, K, epi);
     }
     return hipGetLastError();
 }

@@ -42,6 +42,8 @@ hipError_t launch_pack_gate_up(Elem src_t, Elem dst_t, const void* gate, const v
                                int dff, int d, hipStream_t s);
 
 // ---- GEMMs: C[M][N] = A[M][K] . W[N][K]^T, fp32 accumulation ---------------------
+// For 16-bit operands W is in the k-step tiled layout (lb_device.h) in every
+// GEMM below, prefill and decode; for fp32 blocks it is row-major [N][K].
 struct QkvEpi {
     void* q;          // [M][qd]           operand type
     void* kws;        // [B][nkv][s_stride][dh] operand type, or nullptr

@@ -26,17 +26,14 @@
 
 using lb::Elem;
 
-// Packed weights of one block.
+// Packed weights of one block: for bf16 blocks one copy, in the operand type
+// and the k-step tiled layout (lb_device.h) that both the prefill and the
+// decode GEMMs read; for fp32 blocks row-major fp32.
 struct LayerW {
-    void* w_qkv = nullptr;
+    void* w_qkv = nullptr;   // [Wq; Wk; Wv]
     void* w_o = nullptr;
-    void* w_gu = nullptr;
+    void* w_gu = nullptr;    // gate/up interleaved in groups of four rows
     void* w_down = nullptr;
-    // the same weights in the decode (k-step tiled) layout, bf16 blocks only
-    void* wt_qkv = nullptr;
-    void* wt_o = nullptr;
-    void* wt_gu = nullptr;
-    void* wt_down = nullptr;
     float* g1 = nullptr;
     float* g2 = nullptr;
 };
@@ -87,6 +84,7 @@ struct lb_block {
     float* m_r = nullptr;        // [T*K][d] expert outputs
     float* m_hs = nullptr;       // [T][d] h plus the shared expert
     std::vector<void*> allocs;
+    uint64_t device_bytes = 0;   // sum of the sizes in allocs
     std::string err;
     // per-stage timing: a ring of event sets, LB_NUM_STAGES + 1 events each
     bool profiling = false;
@@ -221,6 +219,7 @@ static bool dalloc(lb_block* blk, P** out, size_t bytes) {
         return false;
     }
     blk->allocs.push_back(p);
+    blk->device_bytes += bytes;
     *out = static_cast<P*>(p);
     return true;
 }
@@ -287,22 +286,64 @@ static lb_status validate_config(const lb_config* c) {
     return LB_OK;
 }
 
+// Bytes of every device buffer of a dense block, from its (validated) config
+// alone: create_core, alloc_layer and llama_stack_init allocate exactly these,
+// and llama_block_footprint adds them up.  Operands take 2 bytes in bf16
+// blocks (fp16 or bf16) and 4 in fp32 blocks.
+struct Sizes {
+    size_t rope, n1, n2, q, o, z, h;                         // every block
+    size_t kws, vws, part, gpart, at_n1, at_o, at_n2, at_z;  // bf16 blocks only (else 0)
+    size_t ws_rows, gpart_floats;
+    size_t w_qkv, w_o, w_gu, w_down, g1, g2;                 // the weights of one block
+    size_t staging;                                          // held while init packs (bf16)
+    size_t g_final, act;                                     // a stack's final gain, activations
+
+    uint64_t workspace() const {
+        return (uint64_t)rope + n1 + n2 + q + o + z + h + kws + vws + part + gpart + at_n1 + at_o + at_n2 + at_z;
+    }
+    uint64_t layer() const { return (uint64_t)w_qkv + w_o + w_gu + w_down + g1 + g2; }
+};
+
+static Sizes sizes_of(const lb_config& c) {
+    Sizes z = {};
+    const bool bf = c.dtype == LB_BF16;
+    const size_t eo = bf ? 2 : 4, eio = bf ? 2 : 4;
+    const size_t T = (size_t)c.max_tokens, d = (size_t)c.d_model, dh = (size_t)c.d_head, dff = (size_t)c.d_ff;
+    const size_t qd = (size_t)c.n_heads * dh, kvd = (size_t)c.n_kv_heads * dh, nqkv = qd + 2 * kvd;
+    z.rope = (size_t)c.max_seq_len * (dh / 2) * sizeof(float2);
+    z.n1 = z.n2 = T * d * eo;
+    z.q = z.o = T * qd * eo;
+    z.z = T * dff * eo;
+    z.h = T * d * 4;
+    if (bf) {
+        // prefill from position 0 keeps k and v^T in the operand type with the
+        // sequence stride rounded up to 8: B * round8(S) <= T + 7 * T / 2 rows.
+        z.ws_rows = T + 7 * (T / 2) + 8;
+        z.kws = z.vws = z.ws_rows * kvd * eo;
+        z.part = lb::decode_partials_floats(c.max_tokens, c.n_heads, c.d_head, c.max_seq_len) * sizeof(float);
+        z.gpart_floats = lb::skinny_partials_floats(c.max_tokens < 64 ? c.max_tokens : 64,
+                                                    (int)std::max(std::max(nqkv, d), 2 * dff));
+        z.gpart = z.gpart_floats * sizeof(float);
+        z.at_n1 = z.at_n2 = (size_t)kDecodeRows * d * eo;
+        z.at_o = (size_t)kDecodeRows * qd * eo;
+        z.at_z = (size_t)kDecodeRows * dff * eo;
+        z.staging = std::max(std::max(nqkv * d, d * qd), 2 * dff * d) * eo;
+    }
+    z.w_qkv = nqkv * d * eo;
+    z.w_o = d * qd * eo;
+    z.w_gu = 2 * dff * d * eo;
+    z.w_down = d * dff * eo;
+    z.g1 = z.g2 = d * 4;
+    z.g_final = d * 4;
+    z.act = T * d * eio;
+    return z;
+}
+
 // Allocate one block's packed weights (owned by blk's allocation list).
 static bool alloc_layer(lb_block* blk, LayerW* L) {
-    const lb_config& c = blk->cfg;
-    const int d = c.d_model, dff = c.d_ff;
-    const size_t eo = esz(blk->op);
-    bool ok = dalloc(blk, &L->w_qkv, (size_t)blk->nqkv * d * eo) &&
-              dalloc(blk, &L->w_o, (size_t)d * blk->qd * eo) &&
-              dalloc(blk, &L->w_gu, (size_t)2 * dff * d * eo) &&
-              dalloc(blk, &L->w_down, (size_t)d * dff * eo) && dalloc(blk, &L->g1, (size_t)d * 4) &&
-              dalloc(blk, &L->g2, (size_t)d * 4);
-    if (ok && blk->dt == Elem::BF16)
-        ok = dalloc(blk, &L->wt_qkv, (size_t)blk->nqkv * d * eo) &&
-             dalloc(blk, &L->wt_o, (size_t)d * blk->qd * eo) &&
-             dalloc(blk, &L->wt_gu, (size_t)2 * dff * d * eo) &&
-             dalloc(blk, &L->wt_down, (size_t)d * dff * eo);
-    return ok;
+    const Sizes z = sizes_of(blk->cfg);
+    return dalloc(blk, &L->w_qkv, z.w_qkv) && dalloc(blk, &L->w_o, z.w_o) && dalloc(blk, &L->w_gu, z.w_gu) &&
+           dalloc(blk, &L->w_down, z.w_down) && dalloc(blk, &L->g1, z.g1) && dalloc(blk, &L->g2, z.g2);
 }
 
 static bool weights_complete(const lb_weights* w) {
@@ -312,32 +353,39 @@ static bool weights_complete(const lb_weights* w) {
     return true;
 }
 
-// Enqueue the packing of one block's weights from the caller's tensors.
-static hipError_t pack_layer(const lb_block* blk, const lb_weights* w, const LayerW& L, hipStream_t s) {
+// Enqueue the packing of one block's weights from the caller's tensors.  For
+// bf16 blocks each matrix is converted row-major into `stage` (device scratch
+// of Sizes::staging bytes) and then tiled into its place.
+static hipError_t pack_layer(const lb_block* blk, const lb_weights* w, const LayerW& L, void* stage,
+                             hipStream_t s) {
     const lb_config& c = blk->cfg;
     const int d = c.d_model, dh = c.d_head, dff = c.d_ff;
     const Elem op = blk->op, dt = blk->dt;
+    const bool tiled = dt == Elem::BF16;
     const size_t eo_row = (size_t)d * esz(op);
+    // row-major destination of a matrix: its final place (fp32) or the stage
+    auto dst = [&](void* final_place) { return tiled ? stage : final_place; };
+    auto tile = [&](void* final_place, int rows, int K) {
+        return tiled ? lb::launch_tile_weights(op, stage, final_place, rows, K, s) : hipSuccess;
+    };
     // rotate_half layout: the rows of each q and k head are reordered so that
     // the projection puts dimensions i and i + d_head/2 side by side, where the
     // epilogue turns adjacent pairs; it stores them back in natural order
     const int perm_dh = c.rope_layout == LB_ROPE_HALF ? dh : 0;
-    hipError_t e = lb::launch_convert_rows(dt, op, w->wq, L.w_qkv, blk->qd, d, perm_dh, s);
+    void* qkv = dst(L.w_qkv);
+    hipError_t e = lb::launch_convert_rows(dt, op, w->wq, qkv, blk->qd, d, perm_dh, s);
     if (e == hipSuccess)
-        e = lb::launch_convert_rows(dt, op, w->wk, (char*)L.w_qkv + (size_t)blk->qd * eo_row, blk->kvd, d,
-                                    perm_dh, s);
+        e = lb::launch_convert_rows(dt, op, w->wk, (char*)qkv + (size_t)blk->qd * eo_row, blk->kvd, d, perm_dh, s);
     if (e == hipSuccess)
-        e = lb::launch_convert(dt, op, w->wv, (char*)L.w_qkv + (size_t)(blk->qd + blk->kvd) * eo_row,
+        e = lb::launch_convert(dt, op, w->wv, (char*)qkv + (size_t)(blk->qd + blk->kvd) * eo_row,
                                (size_t)blk->kvd * d, s);
-    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wo, L.w_o, (size_t)d * blk->qd, s);
-    if (e == hipSuccess) e = lb::launch_pack_gate_up(dt, op, w->w_gate, w->w_up, L.w_gu, dff, d, s);
-    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->w_down, L.w_down, (size_t)d * dff, s);
-    if (e == hipSuccess && dt == Elem::BF16) {
-        e = lb::launch_tile_weights(op, L.w_qkv, L.wt_qkv, blk->nqkv, d, s);
-        if (e == hipSuccess) e = lb::launch_tile_weights(op, L.w_o, L.wt_o, d, blk->qd, s);
-        if (e == hipSuccess) e = lb::launch_tile_weights(op, L.w_gu, L.wt_gu, 2 * dff, d, s);
-        if (e == hipSuccess) e = lb::launch_tile_weights(op, L.w_down, L.wt_down, d, dff, s);
-    }
+    if (e == hipSuccess) e = tile(L.w_qkv, blk->nqkv, d);
+    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->wo, dst(L.w_o), (size_t)d * blk->qd, s);
+    if (e == hipSuccess) e = tile(L.w_o, d, blk->qd);
+    if (e == hipSuccess) e = lb::launch_pack_gate_up(dt, op, w->w_gate, w->w_up, dst(L.w_gu), dff, d, s);
+    if (e == hipSuccess) e = tile(L.w_gu, 2 * dff, d);
+    if (e == hipSuccess) e = lb::launch_convert(dt, op, w->w_down, dst(L.w_down), (size_t)d * dff, s);
+    if (e == hipSuccess) e = tile(L.w_down, d, dff);
     if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->attn_norm, L.g1, (size_t)d, s);
     if (e == hipSuccess) e = lb::launch_convert(dt, Elem::F32, w->ffn_norm, L.g2, (size_t)d, s);
     return e;
@@ -365,29 +413,19 @@ static lb_status create_core(const lb_config* cfg, Elem op_type, lb_block** out)
     blk->qd = c.n_heads * dh;
     blk->kvd = c.n_kv_heads * dh;
     blk->nqkv = blk->qd + 2 * blk->kvd;
-    const size_t T = (size_t)c.max_tokens;
     const Elem op = blk->op, dt = blk->dt;
     const size_t eo = esz(op);
+    const Sizes z = sizes_of(c);
 
-    bool ok = dalloc(blk, &blk->rope, (size_t)c.max_seq_len * (dh / 2) * sizeof(float2)) &&
-              dalloc(blk, &blk->n1, T * d * eo) && dalloc(blk, &blk->n2, T * d * eo) &&
-              dalloc(blk, &blk->q, T * blk->qd * eo) && dalloc(blk, &blk->o, T * blk->qd * eo) &&
-              dalloc(blk, &blk->z, T * dff * eo) && dalloc(blk, &blk->h, T * d * 4);
+    bool ok = dalloc(blk, &blk->rope, z.rope) && dalloc(blk, &blk->n1, z.n1) && dalloc(blk, &blk->n2, z.n2) &&
+              dalloc(blk, &blk->q, z.q) && dalloc(blk, &blk->o, z.o) && dalloc(blk, &blk->z, z.z) &&
+              dalloc(blk, &blk->h, z.h);
     if (ok && dt == Elem::BF16) {
-        // prefill from position 0 keeps k and v^T in the operand type with the
-        // sequence stride rounded up to 8: B * round8(S) <= T + 7 * T / 2 rows.
-        blk->ws_rows = T + 7 * (T / 2) + 8;
-        ok = dalloc(blk, &blk->kws, blk->ws_rows * blk->kvd * eo) &&
-             dalloc(blk, &blk->vws, blk->ws_rows * blk->kvd * eo) &&
-             dalloc(blk, &blk->part,
-                    lb::decode_partials_floats(c.max_tokens, c.n_heads, dh, c.max_seq_len) * sizeof(float)) &&
-             dalloc(blk, &blk->gpart, (blk->gpart_cap = lb::skinny_partials_floats(
-                                           c.max_tokens < 64 ? c.max_tokens : 64,
-                                           std::max(std::max(blk->nqkv, d), 2 * dff))) * sizeof(float)) &&
-             dalloc(blk, &blk->at_n1, (size_t)kDecodeRows * d * eo) &&
-             dalloc(blk, &blk->at_o, (size_t)kDecodeRows * blk->qd * eo) &&
-             dalloc(blk, &blk->at_n2, (size_t)kDecodeRows * d * eo) &&
-             dalloc(blk, &blk->at_z, (size_t)kDecodeRows * dff * eo);
+        blk->ws_rows = z.ws_rows;
+        blk->gpart_cap = z.gpart_floats;
+        ok = dalloc(blk, &blk->kws, z.kws) && dalloc(blk, &blk->vws, z.vws) && dalloc(blk, &blk->part, z.part) &&
+             dalloc(blk, &blk->gpart, z.gpart) && dalloc(blk, &blk->at_n1, z.at_n1) &&
+             dalloc(blk, &blk->at_o, z.at_o) && dalloc(blk, &blk->at_n2, z.at_n2) && dalloc(blk, &blk->at_z, z.at_z);
     }
     if (!ok) {
         free_all(blk);
@@ -589,11 +627,18 @@ static lb_status choose_operands(const lb_config* cfg, const lb_weights* ws, int
 static lb_status load_layers(lb_block* blk, const lb_weights* w, int n, LayerW* ls) {
     for (int l = 0; l < n; ++l)
         if (!alloc_layer(blk, &ls[l])) return fail(nullptr, LB_ERR_OOM, "device allocation failed (weights of block %d)", l);
+    // staging buffer of the tiling (bf16 blocks), freed before returning
+    void* stage = nullptr;
+    if (blk->dt == Elem::BF16 && hipMalloc(&stage, sizes_of(blk->cfg).staging) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(nullptr, LB_ERR_OOM, "device allocation failed (weight staging)");
+    }
     hipStream_t s = nullptr;
     hipError_t e = hipStreamCreate(&s);
-    for (int l = 0; l < n && e == hipSuccess; ++l) e = pack_layer(blk, &w[l], ls[l], s);
+    for (int l = 0; l < n && e == hipSuccess; ++l) e = pack_layer(blk, &w[l], ls[l], stage, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (s) hipStreamDestroy(s);
+    if (stage) hipFree(stage);
     if (e != hipSuccess) return fail(nullptr, LB_ERR_HIP, "weight packing failed: %s", hipGetErrorString(e));
     return LB_OK;
 }
@@ -829,7 +874,7 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     qe.qd = blk->qd;
     qe.rope_half = c.rope_layout == LB_ROPE_HALF;
     mark(1);
-    if (dec) e = lb::decode_qkv(op, dt, n1, L.wt_qkv, M, blk->nqkv, d, qe, ws, s);
+    if (dec) e = lb::decode_qkv(op, dt, n1, L.w_qkv, M, blk->nqkv, d, qe, ws, s);
     else e = lb::gemm_qkv(op, dt, n1, L.w_qkv, M, blk->nqkv, d, qe, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "qkv projection: %s", hipGetErrorString(e));
 
@@ -859,7 +904,7 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "attention: %s", hipGetErrorString(e));
 
     mark(3);
-    if (dec) e = lb::decode_resid(op, dt, o, L.wt_o, M, d, blk->qd, x, wk.h, ws, s);
+    if (dec) e = lb::decode_resid(op, dt, o, L.w_o, M, d, blk->qd, x, wk.h, ws, s);
     else e = lb::gemm_resid(op, dt, o, L.w_o, M, d, blk->qd, x, wk.h, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "o projection: %s", hipGetErrorString(e));
     mark(4);
@@ -876,11 +921,11 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
         return st;
     }
     mark(5);
-    if (dec) e = lb::decode_swiglu(op, n2, L.wt_gu, M, 2 * dff, d, z, ws, s);
+    if (dec) e = lb::decode_swiglu(op, n2, L.w_gu, M, 2 * dff, d, z, ws, s);
     else e = lb::gemm_swiglu(op, n2, L.w_gu, M, 2 * dff, d, z, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "gate/up projection: %s", hipGetErrorString(e));
     mark(6);
-    if (dec) e = lb::decode_out(op, dt, z, L.wt_down, M, d, dff, wk.h, out, ws, s);
+    if (dec) e = lb::decode_out(op, dt, z, L.w_down, M, d, dff, wk.h, out, ws, s);
     else e = lb::gemm_out(op, dt, z, L.w_down, M, d, dff, wk.h, out, ws, s);
     if (e != hipSuccess) return fail(blk, LB_ERR_HIP, "down projection: %s", hipGetErrorString(e));
     mark(7);
@@ -1073,9 +1118,9 @@ extern "C" lb_status llama_stack_init(const lb_config* cfg, int32_t n_layers, co
     lb_stack* sk = new lb_stack();
     sk->core = blk;
     sk->layers.resize((size_t)n_layers);
-    const size_t act = (size_t)blk->cfg.max_tokens * blk->cfg.d_model * esz(blk->dt);
-    bool ok = dalloc(blk, &sk->g_final, (size_t)blk->cfg.d_model * 4) && dalloc(blk, &sk->act[0], act) &&
-              dalloc(blk, &sk->act[1], act);
+    const Sizes z = sizes_of(blk->cfg);
+    bool ok = dalloc(blk, &sk->g_final, z.g_final) && dalloc(blk, &sk->act[0], z.act) &&
+              dalloc(blk, &sk->act[1], z.act);
     st = ok ? load_layers(blk, layers, n_layers, sk->layers.data())
             : fail(nullptr, LB_ERR_OOM, "device allocation failed");
     if (st == LB_OK) {
@@ -1283,6 +1328,23 @@ extern "C" lb_elem llama_block_operand_type(const lb_block* blk) {
 extern "C" lb_elem llama_stack_operand_type(const lb_stack* sk) {
     return sk ? to_abi(sk->core->op) : LB_ELEM_F32;
 }
+
+extern "C" lb_status llama_block_footprint(const lb_config* cfg, int32_t n_layers, lb_footprint* out) {
+    if (!cfg || !out) return fail(nullptr, LB_ERR_INVALID_ARG, "cfg or out is NULL");
+    if (n_layers < 0 || n_layers > LB_MAX_STACK_LAYERS)
+        return fail(nullptr, LB_ERR_INVALID_ARG, "n_layers (%d) must be in [0, %d]", n_layers, LB_MAX_STACK_LAYERS);
+    lb_status st = validate_config(cfg);
+    if (st != LB_OK) return st;
+    const Sizes z = sizes_of(*cfg);
+    out->weights = z.layer() * (uint64_t)(n_layers > 0 ? n_layers : 1);
+    out->workspace = z.workspace() + (n_layers > 0 ? (uint64_t)z.g_final + 2 * (uint64_t)z.act : 0);
+    out->init_staging = z.staging;
+    return LB_OK;
+}
+
+extern "C" uint64_t llama_block_device_bytes(const lb_block* blk) { return blk ? blk->device_bytes : 0; }
+
+extern "C" uint64_t llama_stack_device_bytes(const lb_stack* sk) { return sk ? sk->core->device_bytes : 0; }
 
 extern "C" lb_status llama_block_stage_info(const lb_block* blk, lb_stage which, lb_elem* elem, int64_t* cols) {
     if (!blk || !elem || !cols) return LB_ERR_INVALID_ARG;

@@ -356,6 +356,32 @@ typedef enum { LB_ELEM_F32 = 0, LB_ELEM_BF16 = 1, LB_ELEM_F16 = 2 } lb_elem;
 lb_elem llama_block_operand_type(const lb_block* blk);
 lb_elem llama_stack_operand_type(const lb_stack* st);
 
+/* Device memory of a dense block or stack, in bytes as requested from the
+ * allocator (it may round each allocation up), computed from the config alone
+ * on the host: no GPU call, so a deployment can be sized before any weight
+ * exists ("The Evolving Transformer 04 LLaMA", 07 ASSEMBLE LLAMA: a model is
+ * N such blocks).  A block holds one copy of its weights, in the operand type
+ * (2 bytes an element for bf16 blocks, 4 for fp32), plus its gains in fp32.
+ *   n_layers   0: one block handle (llama_block_init); 1..LB_MAX_STACK_LAYERS:
+ *              a stack of that many blocks (llama_stack_init)
+ *   weights    the packed weights and gains of every block
+ *   workspace  the RoPE table, activations and scratch one handle shares
+ *              across its blocks (for a stack also the final gain and two
+ *              activation buffers)
+ *   init_staging  device memory init also holds while it packs (0 for fp32)
+ * KV caches are the caller's and not counted.  MoE blocks are not covered.
+ * Errors: NULL cfg or out, n_layers out of range, or any config that init
+ * rejects (the same status and message as init). */
+typedef struct lb_footprint {
+    uint64_t weights;
+    uint64_t workspace;
+    uint64_t init_staging;
+} lb_footprint;
+lb_status llama_block_footprint(const lb_config* cfg, int32_t n_layers, lb_footprint* out);
+/* Bytes a live handle holds (weights + workspace as above); 0 for NULL. */
+uint64_t llama_block_device_bytes(const lb_block* blk);
+uint64_t llama_stack_device_bytes(const lb_stack* st);
+
 /* Describe a stage buffer: element type and columns per token row. */
 lb_status llama_block_stage_info(const lb_block* blk, lb_stage which, lb_elem* elem,
                                  int64_t* cols);

@@ -45,18 +45,21 @@ int main(void) {
          offsetof(lb_config, norm_eps), offsetof(lb_config, dtype), offsetof(lb_config, operands),
          sizeof(lb_weights));
   printf("%zu %zu %zu\\n", sizeof(lb_kv_cache), offsetof(lb_kv_cache, batch), offsetof(lb_kv_cache, max_seq_len));
+  printf("%zu %zu\\n", sizeof(lb_footprint), offsetof(lb_footprint, init_staging));
   return 0;
 }
 """)
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
-    a, b = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")[:2]
+    a, b, c = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")[:3]
     C = lbmod.LbConfig
     want_a = [ctypes.sizeof(C), C.rope_theta.offset, C.norm_eps.offset, C.dtype.offset,
               C.operands.offset, ctypes.sizeof(lbmod.LbWeights)]
     assert [int(v) for v in a.split()] == want_a
     K = lbmod.LbKVCache
     assert [int(v) for v in b.split()] == [ctypes.sizeof(K), K.batch.offset, K.max_seq_len.offset]
+    F = lbmod.LbFootprint
+    assert [int(v) for v in c.split()] == [ctypes.sizeof(F), F.init_staging.offset]
 
 
 def _fake_weights():
@@ -161,3 +164,65 @@ def test_moe_init_rejects_bad_arguments_before_any_device_call():
     assert L.llama_moe_block_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(mc), ctypes.byref(ew),
                                   ctypes.byref(h)) == lbmod.LB_ERR_INVALID_ARG
     assert L.llama_block_copy_routing(None, None, None, None, None) == lbmod.LB_ERR_INVALID_ARG
+
+
+def _bytes_of_weights(d, H, n_kv, dh, dff, elem):
+    """Bytes of one block's weights as the pages size them: Wq [H dh x d],
+    Wk and Wv [n_kv dh x d], Wo [d x H dh], gate and up [d_ff x d], down
+    [d x d_ff] ("Full Llama 3 transformer block", How it works), one copy in
+    the operand type, plus the two gains in fp32."""
+    mats = H * dh * d + 2 * n_kv * dh * d + d * H * dh + 3 * dff * d
+    return mats * elem + 2 * d * 4
+
+
+def test_footprint_holds_one_weight_copy_per_block():
+    """8B width (d 4096, 32/8 heads of 128, d_ff 14336): one packed copy of
+    the weights, 436,207,616 bytes of matrices, not two; an fp32 block holds
+    4 bytes an element."""
+    cfg = lbmod.make_config(4096, 32, 8, 128, 14336, 4096, 4096, 5e5, 1e-5, "bf16")
+    fp = lbmod.llama_block_footprint(cfg)
+    assert fp["weights"] == _bytes_of_weights(4096, 32, 8, 128, 14336, 2)
+    assert fp["weights"] - 2 * 4096 * 4 == 436_207_616
+    # staging of init: the largest matrix, gate/up [2 d_ff x d]
+    assert fp["init_staging"] == 2 * 14336 * 4096 * 2
+    small = lbmod.make_config(64, 4, 2, 16, 176, 16, 16, 1e4, 1e-5, "f32")
+    fp32 = lbmod.llama_block_footprint(small)
+    assert fp32["weights"] == _bytes_of_weights(64, 4, 2, 16, 176, 4)
+    assert fp32["init_staging"] == 0
+
+
+def test_footprint_of_a_70b_width_stack_fits_one_gpu():
+    """80 blocks of the 70B width (d 8192, 64/8 heads of 128, d_ff 28672),
+    "Full Llama 3 transformer block", How it works, with a workspace for 8192
+    token rows and the KV caches of 8 sequences of 8192 positions: the whole
+    model's blocks fit in one MI355X's 288 GB, and a stack's weights are
+    exactly n_layers blocks' worth."""
+    cfg = lbmod.make_config(8192, 64, 8, 128, 28672, 8192, 8192, 5e5, 1e-5, "bf16")
+    one = lbmod.llama_block_footprint(cfg, 1)
+    fp = lbmod.llama_block_footprint(cfg, 80)
+    per_block = _bytes_of_weights(8192, 64, 8, 128, 28672, 2)
+    assert fp["weights"] == 80 * per_block == 80 * one["weights"]
+    assert fp["workspace"] == one["workspace"]
+    # a stack adds the final gain and two activation buffers to a block's workspace
+    blk = lbmod.llama_block_footprint(cfg, 0)
+    assert fp["workspace"] == blk["workspace"] + 8192 * 4 + 2 * 8192 * 8192 * 2
+    kv = 80 * 2 * 8 * 8192 * 8 * 128 * 2
+    total = fp["weights"] + fp["workspace"] + fp["init_staging"] + kv
+    assert total < 288e9, total / 1e9
+    # two copies of the weights would not have fit beside the same caches
+    assert 2 * fp["weights"] + fp["workspace"] + kv > 288e9
+
+
+def test_footprint_rejects_what_init_rejects():
+    L = lbmod.lib()
+    bad = lbmod.make_config(65, 4, 2, 16, 176, 16, 16, 1e4, 1e-5, "f32")
+    out = lbmod.LbFootprint()
+    assert L.llama_block_footprint(ctypes.byref(bad), 0, ctypes.byref(out)) == lbmod.LB_ERR_INVALID_ARG
+    assert "d_model" in lbmod.llama_block_last_error(None)
+    ok = lbmod.make_config(64, 4, 2, 16, 176, 16, 16, 1e4, 1e-5, "f32")
+    for n in (-1, lbmod.MAX_STACK_LAYERS + 1):
+        assert L.llama_block_footprint(ctypes.byref(ok), n, ctypes.byref(out)) == lbmod.LB_ERR_INVALID_ARG
+    assert L.llama_block_footprint(None, 0, ctypes.byref(out)) == lbmod.LB_ERR_INVALID_ARG
+    assert L.llama_block_footprint(ctypes.byref(ok), 0, None) == lbmod.LB_ERR_INVALID_ARG
+    assert L.llama_block_device_bytes(None) == 0
+    assert L.llama_stack_device_bytes(None) == 0
