@@ -529,9 +529,10 @@ __global__ void __launch_bounds__(256) gemm_big_grouped_kernel(const T* __restri
 // conflicts for the operand read).  With WT, W is in the k-step tiled layout
 // (lb_device.h; N % 16 == 0): a stage is 16 row tiles x 2 pieces of 1 KB, one
 // load each, kept in piece order, whose operand reads are 1 KB contiguous.
-// Each k-step is two sub-steps of 64 MFMAs.  Operands are double-buffered in
-// registers: during one sub-step the wavefront reads the next sub-step's
-// operands (groups 0..6 of its 8 MFMA groups) into the other buffer.  One
+// Each k-step is two sub-steps of 64 MFMAs, accumulating in place (AGPRs).
+// Operands are double-buffered in registers: during one sub-step the
+// wavefront reads the next sub-step's operands (groups 0..6 of its 8 MFMA
+// groups) into the other buffer.  One
 // barrier per k-step, between its sub-steps: every wavefront's reads of stage
 // kt are complete (sub-step 1's operands are in registers) and stage kt+1 has
 // landed; sub-step 1 then reads stage kt+1 and its first four groups issue
@@ -624,7 +625,7 @@ __device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T*
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[fb][i], bf[fb][j], acc[i][j]);
+            for (int j = 0; j < TJ; ++j) mfma16_tied(acc[i][j], af[fb][i], bf[fb][j]);
             __builtin_amdgcn_sched_barrier(0);
             if (loads && i < 4) {
 #pragma unroll
@@ -645,6 +646,7 @@ __device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T*
         sub(1, kt + 1, 0, true, kt + 2);
     }
     wait_vm<0>();
+    mfma_drain();
     __syncthreads();
 
     // Epilogue: stage EPR rows of the fp32 tile through LDS, then hand

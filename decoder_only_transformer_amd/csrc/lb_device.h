@@ -158,6 +158,23 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same products accumulating in place: the accumulator is one AGPR tuple
+// that the instruction reads and writes (the builtins above may get a
+// destination apart from the accumulator, which makes the register allocator
+// shuffle accumulators through other registers when every AGPR holds one).
+// The compiler does not see these as matrix instructions and inserts no wait
+// states after them: after the last one, call mfma_drain() before any other
+// instruction reads the accumulators.  Operand registers loaded from memory
+// are waited for as for any inline-asm input.
+__device__ __forceinline__ void mfma16_tied(f32x4& c, const f16x8& a, const f16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_tied(f32x4& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// 24 wait states: more than the result latency of a 16x16x32 product
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // ---- decode operand layout -------------------------------------------------------
 // Token-batch GEMMs of the decode path read their operands in "k-step tiles":
 // for an operand with rows r (tokens or weight rows) and K columns, the 16
