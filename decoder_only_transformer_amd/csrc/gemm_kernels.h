@@ -521,38 +521,39 @@ __global__ void __launch_bounds__(256) gemm_big_grouped_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------------------------------
-// Large prefill GEMM with 64-deep k-steps: 256 x 256 tiles, four wavefronts in
-// a 2 x 2 grid (128 x 128 each, 16x16x32 MFMAs, accumulators in AGPRs), two
-// LDS stages of 64 KB.  A stage of A is 256 rows x 128 bytes, loaded by
-// direct-to-LDS loads of whole cache lines (eight 128-byte rows per wavefront
-// instruction; chunk index XORed by (row / 2) & 7 in LDS, free of bank
-// conflicts for the operand read).  With WT, W is in the k-step tiled layout
-// (lb_device.h; N % 16 == 0): a stage is 16 row tiles x 2 pieces of 1 KB, one
-// load each, kept in piece order, whose operand reads are 1 KB contiguous.
-// Each k-step is two sub-steps of 64 MFMAs, accumulating in place (AGPRs).
-// Operands are double-buffered in registers: during one sub-step the
-// wavefront reads the next sub-step's operands (groups 0..6 of its 8 MFMA
-// groups) into the other buffer.  One
-// barrier per k-step, between its sub-steps: every wavefront's reads of stage
-// kt are complete (sub-step 1's operands are in registers) and stage kt+1 has
-// landed; sub-step 1 then reads stage kt+1 and its first four groups issue
-// the loads of stage kt+2 into stage kt's buffer.  Rows beyond M / N are
-// clamped to the last valid row.  K % 64 == 0.
+// Large prefill GEMM with 64-deep k-steps: 256 x BN tiles (BN 256 or 192),
+// four wavefronts in a 2 x 2 grid (128 x BN/2 each, 16x16x32 MFMAs,
+// accumulators in AGPRs), two LDS stages of (256 + BN) x 128 bytes.  A stage
+// of A is 256 rows x 128 bytes, loaded by direct-to-LDS loads of whole cache
+// lines (eight 128-byte rows per wavefront instruction; chunk index XORed by
+// (row / 2) & 7 in LDS, free of bank conflicts for the operand read).  With
+// WT, W is in the k-step tiled layout (lb_device.h; N % 16 == 0): a stage is
+// BN / 16 row tiles x 2 pieces of 1 KB, one load each, kept in piece order,
+// whose operand reads are 1 KB contiguous.  Each k-step is two sub-steps of
+// TI x TJ MFMAs, accumulating in place (AGPRs).  Operands are double-buffered
+// in registers: during one sub-step the wavefront reads the next sub-step's
+// operands (spread over groups 0..6 of its 8 MFMA groups) into the other
+// buffer.  One barrier per k-step, between its sub-steps: every wavefront's
+// reads of stage kt are complete (sub-step 1's operands are in registers) and
+// stage kt+1 has landed; sub-step 1 then reads stage kt+1 and its first four
+// groups issue the loads of stage kt+2 into stage kt's buffer.  Rows beyond
+// M / N are clamped to the last valid row.  K % 64 == 0.
 // ------------------------------------------------------------------------------------
-template <typename T>
-constexpr int big2_tile_lds() { return 2 * 512 * 64; }
+template <typename T, int BN>
+constexpr int big2_tile_lds() { return 2 * (256 + BN) * 64; }
 
-template <typename T, class Epi, bool WT>
+template <typename T, class Epi, bool WT, int BN>
 __device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T* __restrict__ W, int M, int N,
                                                int K, Epi epi, int m0, int n0, T* lds) {
     typedef typename vec8<T>::type V8;
-    constexpr int BM = 256, BN = 256, BK = 64, NW = 4, NT = 256, WM = 128, WN = 128;
-    constexpr int TI = 8, TJ = 8;
+    static_assert(BN == 256 || BN == 192, "tile width");
+    constexpr int BM = 256, BK = 64, NW = 4, NT = 256, WM = 128, WN = BN / 2;
+    constexpr int TI = WM / 16, TJ = WN / 16, NIT = TI + TJ;
     constexpr int SA = BM * BK, SB = BN * BK, STG = SA + SB;   // elements per stage
-    constexpr int NA = SA / 8 / NT, NB = SB / 8 / NT;          // loads per thread per stage (8 + 8)
+    constexpr int NA = SA / 8 / NT, NB = SB / 8 / NT;          // loads per thread per stage (8 + BN / 32)
     constexpr int ND = NA + NB;
     constexpr int EPR = 64, CPAD = BN + 4;
-    static_assert(2 * STG == big2_tile_lds<T>(), "LDS size");
+    static_assert(2 * STG == big2_tile_lds<T, BN>(), "LDS size");
     static_assert(EPR * CPAD * 4 <= 2 * STG * (int)sizeof(T), "epilogue stage fits");
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -603,7 +604,7 @@ __device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T*
             const int row = wm * WM + f * 16 + (lane & 15);
             af[fb][f] = *reinterpret_cast<const V8*>(st + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
         } else if constexpr (WT) {
-            bf[fb][f] = *reinterpret_cast<const V8*>(st + SA + ((wn * 8 + f) * 2 + s) * 512 + lane * 8);
+            bf[fb][f] = *reinterpret_cast<const V8*>(st + SA + ((wn * TJ + f) * 2 + s) * 512 + lane * 8);
         } else {
             const int row = wn * WN + f * 16 + (lane & 15);
             bf[fb][f] = *reinterpret_cast<const V8*>(st + SA + row * BK + ((kc ^ ((row >> 1) & 7)) << 3));
@@ -617,7 +618,7 @@ __device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T*
     wait_vm<ND>();
     lds_barrier();
 #pragma unroll
-    for (int it = 0; it < TI + TJ; ++it) rd(0, 0, 0, it);
+    for (int it = 0; it < NIT; ++it) rd(0, 0, 0, it);
     // one sub-step: 64 MFMAs on buffer fb in 8 groups; groups 0..6 read the
     // next sub-step's operands (stage nstage, sub-step ns) into buffer fb^1;
     // with loads, groups 0..3 issue the loads of stage kd
@@ -629,11 +630,11 @@ __device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T*
             __builtin_amdgcn_sched_barrier(0);
             if (loads && i < 4) {
 #pragma unroll
-                for (int d = 4 * i; d < 4 * i + 4; ++d) dma(kd, d);
+                for (int d = 4 * i; d < 4 * i + 4 && d < ND; ++d) dma(kd, d);
             }
             if (i < TI - 1) {
 #pragma unroll
-                for (int it = i * 16 / 7; it < (i + 1) * 16 / 7; ++it) rd(nstage, ns, fb ^ 1, it);
+                for (int it = i * NIT / 7; it < (i + 1) * NIT / 7; ++it) rd(nstage, ns, fb ^ 1, it);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -673,11 +674,11 @@ __device__ __forceinline__ void gemm_big2_tile(const T* __restrict__ A, const T*
     }
 }
 
-template <typename T, class Epi, bool WT>
+template <typename T, class Epi, bool WT, int BN = 256>
 __global__ void __launch_bounds__(256) gemm_big2_kernel(const T* __restrict__ A, const T* __restrict__ W, int M,
                                                        int N, int K, Epi epi) {
-    constexpr int BM = 256, BN = 256;
-    __shared__ __attribute__((aligned(16))) T lds[big2_tile_lds<T>()];
+    constexpr int BM = 256;
+    __shared__ __attribute__((aligned(16))) T lds[big2_tile_lds<T, BN>()];
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     // workgroups are dealt round-robin to the 8 XCDs: renumber so that each
     // XCD runs a contiguous range of tiles, walked in groups of 8 tile-rows
@@ -692,7 +693,7 @@ __global__ void __launch_bounds__(256) gemm_big2_kernel(const T* __restrict__ A,
     const int in_group = bid % per_group;
     const int tm = first_m + in_group % gsize;
     const int tn = in_group / gsize;
-    gemm_big2_tile<T, Epi, WT>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
+    gemm_big2_tile<T, Epi, WT, BN>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
 }
 
 // ------------------------------------------------------------------------------------

@@ -154,9 +154,21 @@ static hipError_t run_gemm(const T* A, const T* W, int M, int N, int K, const Ep
                   : run_skinny<T, 4, false>(A, W, M, N, K, epi, ws.part, ws.cap, s);
     }
     const long tm = (M + 255) / 256, tn = (N + 255) / 256, t256 = tm * tn;
+    if (t256 >= 192 && N % 192 == 0) {
+        // A CU runs one tile at a time, so a launch takes ceil(tiles / CUs)
+        // rounds of tile time ~ BN.  256 x 192 tiles when their rounds cost
+        // less (the 8B q/k/v product: 512 tiles in 2 rounds of 192 columns
+        // against 384 in 2 of 256), the 192-wide tile taken 5 % slower per
+        // column.
+        const long cus = device_cus();
+        const long t192 = tm * (N / 192);
+        if ((t192 + cus - 1) / cus * 192 * 105 < (t256 + cus - 1) / cus * 256 * 100) {
+            gemm_big2_kernel<T, Epi, true, 192><<<(unsigned)t192, 256, 0, s>>>(A, W, M, N, K, epi);
+            return hipGetLastError();
+        }
+    }
     if (t256 >= 192) {
-        // A CU runs one 256 x 256 tile at a time, so a launch takes
-        // ceil(tiles / CUs) rounds.  When the last round would be at most
+        // When the last round of 256 x 256 tiles would be at most
         // half full and made of whole tile columns (the 8B q/k/v product:
         // 384 tiles), those columns go to the 128 x 128 kernel instead, two
         // blocks per CU: measured 82 us for them there against a 113 us round.
