@@ -1,11 +1,11 @@
 // GEMM kernels: C[M][N] = A[M][K] . W[N][K]^T with fp32 accumulation, results
 // handed to an epilogue (epilogues.h) in 8-column chunks.
 //
-//  gemm_big2_kernel   prefill, large: 256 x 256 tiles, 64-deep k-steps,
-//                     16x16x32 MFMA, two 64 KB LDS stages, weights in the
-//                     k-step tiled layout
-//  gemm_big_kernel    grouped expert GEMMs (row-major expert weights):
-//                     256 x 256 tiles, four-stage LDS ring
+//  gemm_big2_kernel   prefill, large: 256 x 256 (or 256 x 192) tiles,
+//                     64-deep k-steps, 16x16x32 MFMA, two LDS stages,
+//                     weights in the k-step tiled layout
+//  gemm_big_grouped_kernel  grouped expert GEMMs (row-major expert weights):
+//                     256 x 256 tiles, 32-deep k-steps, four-stage LDS ring
 //  gemm_mfma_kernel   prefill, small: 32x32x16 MFMA tiles, direct-to-LDS
 //                     loads, LDS double buffering
 //  gemm_skinny_kernel decode (M <= 64): 16x16x32 MFMA, split-K over waves
@@ -325,10 +325,10 @@ __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------------------------------
-// Large prefill GEMM.  Block tile BM x BN (256 x 256 in use; 128-row tiles
-// measured slower), BK = 32, four wavefronts in a 2 x 2 grid, each
-// BM/2 x BN/2 with 16x16x32 MFMAs (accumulators in AGPRs; one wavefront per
-// SIMD).  A four-stage
+// 256 x 256 tile body of the grouped expert GEMM (row-major weights).  Block
+// tile BM x BN (256 x 256 in use), BK = 32, four wavefronts in a 2 x 2 grid,
+// each BM/2 x BN/2 with 16x16x32 MFMAs (accumulators in AGPRs; one wavefront
+// per SIMD).  A four-stage
 // LDS ring is filled by direct-to-LDS loads issued from inline assembly (so
 // the compiler's counters for LDS reads stay exact; the kernel waits for
 // the loads itself).  One barrier opens each k-step: after it, stage k+1 is
@@ -474,25 +474,6 @@ __device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* 
         pass.finish(epi, cst, tid, m0 + p * EPR, n0, M, N);
         __syncthreads();
     }
-}
-
-template <typename T, int BM, int BN, class Epi>
-__global__ void __launch_bounds__(256) gemm_big_kernel(const T* __restrict__ A,
-                                                      const T* __restrict__ W, int M, int N,
-                                                      int K, Epi epi) {
-    __shared__ __attribute__((aligned(16))) T lds[big_tile_lds<T, BM, BN>()];
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int bid = blockIdx.x;
-    const int nb = gridDim.x;
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-    constexpr int GM = 8;
-    const int per_group = GM * tiles_n;
-    const int first_m = (bid / per_group) * GM;
-    const int gsize = min(tiles_m - first_m, GM);
-    const int in_group = bid % per_group;
-    const int tm = first_m + in_group % gsize;
-    const int tn = in_group / gsize;
-    gemm_big_tile<T, BM, BN, Epi>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
 }
 
 // Grouped GEMM over experts with the 256 x 256 tile body: as

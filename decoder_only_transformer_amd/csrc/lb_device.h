@@ -162,10 +162,12 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 // that the instruction reads and writes (the builtins above may get a
 // destination apart from the accumulator, which makes the register allocator
 // shuffle accumulators through other registers when every AGPR holds one).
-// The compiler does not see these as matrix instructions and inserts no wait
-// states after them: after the last one, call mfma_drain() before any other
-// instruction reads the accumulators.  Operand registers loaded from memory
-// are waited for as for any inline-asm input.
+// The compiler does not see these as matrix instructions and inserts none of
+// the wait states they need: after the last one, call mfma_drain() before
+// any other instruction reads the accumulators, and feed them only operands
+// that come straight from memory loads (which the compiler waits for as for
+// any inline-asm input) -- an operand written by a vector ALU instruction
+// just before (a select, a move) can be read stale.
 __device__ __forceinline__ void mfma16_tied(f32x4& c, const f16x8& a, const f16x8& b) {
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
