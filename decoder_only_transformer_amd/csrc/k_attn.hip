@@ -307,6 +307,13 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
         const T* qp = q + (size_t)(b * S + qrow) * qd + h * DH + 8 * (lane >> 5);
 #pragma unroll
         for (int kk = 0; kk < DH / 16; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qp + 16 * kk);
+        // consume q here: the compiler then waits for these loads once, before
+        // the tile loop.  Left to itself it waits for them at the first use in
+        // every tile, with counters that also cover the next tile's
+        // direct-to-LDS loads (invisible to it), so every tile would wait for
+        // the next one to land before its fifth product.
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk) asm volatile("" ::"v"(qf[kk]));
     }
     // keys the block loads: up to its last query; keys this wavefront uses:
     // up to its own last query (none past S)
