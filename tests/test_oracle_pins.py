@@ -209,6 +209,15 @@ def test_rope_llama31_blend_meets_both_classes():
         prev = sc
 
 
+def test_rope_llama31_speeds_keep_their_order():
+    """Slowing the slow pairs and blending the six between keeps the pairs in
+    order: every scaled speed is below the one before it (pair i + 1 turns
+    slower than pair i, as without scaling), across both class boundaries."""
+    for dh, theta in ((128, 5e5), (64, 1e5), (128, 1e4)):
+        scaled = np.array([oracle.rope_freq(_cfg(dh, theta, scaling=_L31), i) for i in range(dh // 2)])
+        assert np.all(np.diff(scaled) < 0), (dh, theta)
+
+
 def test_rope_variants_keep_relative_invariance():
     """Every layout / scaling variant still depends only on the distance m - n."""
     r = rng(23)
