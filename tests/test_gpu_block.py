@@ -63,6 +63,19 @@ def test_llama3_8b_width_ragged_rows_sampled():
     run.close()
 
 
+@pytest.mark.timeout(900)
+def test_llama3_8b_width_long_sequence_sampled():
+    """8B width, one sequence of 16384 tokens (four times the benchmark's):
+    128 query blocks per head in the prefill attention and 256 key tiles for
+    the last ones, 64 row tiles in every prefill GEMM.  Rows at both ends and
+    at tile edges against the oracle (which computes every row's K and V); a
+    narrow FFN keeps it quick."""
+    w = workloads.with_overrides(workloads.get("llama3_8b_prefill"), B=1, S=16384, d_ff=1024, seed=41)
+    rows = sample_rows(w, [0, 1, 255, 256, 8191, 8192, 16127, 16128, 16383])
+    run, *_ = check_block(w, rows=rows)
+    run.close()
+
+
 def test_llama3_8b_decode_full():
     run, *_ = check_block(workloads.get("llama3_8b_decode"))
     run.close()
@@ -330,6 +343,13 @@ def test_forward_rejects_bad_arguments_without_writing():
     assert ei.value.status == lbmod.LB_ERR_INVALID_ARG
     with pytest.raises(lbmod.LlamaBlockError):
         run.block.forward(run.x, 0, run.kv, run.x)  # out aliases x
+    # empty calls: no sequence, or no token per sequence
+    L = lbmod.lib()
+    kv = lbmod.LbKVCache(run.kv[0].data_ptr(), run.kv[1].data_ptr(), run.kv[0].shape[0], run.kv[0].shape[2])
+    for batch, seq_len in ((0, 8), (1, 0)):
+        st = L.llama_block_forward(run.block.handle, run.x.data_ptr(), batch, seq_len, 0, kv,
+                                   sentinel.data_ptr(), None)
+        assert st == lbmod.LB_ERR_INVALID_ARG, (batch, seq_len, st)
     torch.cuda.synchronize()
     assert torch.all(sentinel == 7.0)
     run.close()
