@@ -163,6 +163,19 @@ def test_decode_llama3_width_batches(B):
     run.close()
 
 
+@pytest.mark.parametrize("B", [5, 20, 40])
+def test_decode_wide_gate_up_blocks_of_eight(B):
+    """Decode with a gate/up width whose column tiles 7 does not divide
+    (d_ff 12288: 1536 tiles), so the LDS-shared gate/up GEMM runs blocks of 8
+    tiles rather than the 7 of the Llama widths; one, two and four 16-row
+    token tiles."""
+    w = workloads.BlockWorkload("decode_wide8", "bf16", B=B, S=1, start_pos=90, d=1024, H=8,
+                                n_kv=2, d_head=128, d_ff=12288, theta=5e5, eps=1e-5, w_std=0.02,
+                                g_mean=1.0, g_std=0.05, max_seq=128, seed=30 + B)
+    run, *_ = check_block(w)
+    run.close()
+
+
 def test_decode_split_k_narrow_outputs():
     """Decode at d 2048: the o and down products have fewer than 192 column
     tiles and weights of several MB, so their K is split over several blocks
