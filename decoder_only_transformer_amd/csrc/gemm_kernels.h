@@ -8,9 +8,17 @@
 //                     256 x 256 tiles, 32-deep k-steps, four-stage LDS ring
 //  gemm_mfma_kernel   prefill, small: 32x32x16 MFMA tiles, direct-to-LDS
 //                     loads, LDS double buffering
-//  gemm_skinny_kernel decode (M <= 64): 16x16x32 MFMA, split-K over waves
-//                     and blocks, weights streamed from HBM straight into
-//                     MFMA operands (+ reduce_epilogue_kernel)
+//  gemm_skinny_kernel row-major activations of M <= 64 rows (prefill-path
+//                     calls with few tokens): 16x16x32 MFMA, split-K over
+//                     waves and blocks, weights streamed from HBM straight
+//                     into MFMA operands (+ reduce_epilogue_kernel)
+//  gemm_decode_kernel decode (one token per sequence, <= 64 sequences):
+//                     activations and weights both k-step tiled, every
+//                     operand load one contiguous 1 KB piece, K split over
+//                     waves and, for long K, blocks (+ reduce_epilogue_kernel)
+//  gemm_decode_wide_kernel  decode, very wide outputs (gate/up): the 7 or 8
+//                     column tiles of a block share the activations through LDS
+//  gemm_simple_kernel fp32 blocks: plain LDS-tiled fp32 FMA
 //
 // The M <= 64 kernels read each weight byte once per call.  With NT their
 // weight loads carry the non-temporal hint (streamed reads of hundreds of MB
@@ -18,7 +26,6 @@
 // for matrices of 40 MB and more, so that the weights of a small model can
 // stay in the 256 MB MALL from one call to the next.  Activations, shared by
 // every block, are read plainly.
-//  gemm_simple_kernel fp32 blocks: plain LDS-tiled fp32 FMA
 #pragma once
 
 #include <type_traits>
@@ -678,7 +685,8 @@ __global__ void __launch_bounds__(256) gemm_big2_kernel(const T* __restrict__ A,
 }
 
 // ------------------------------------------------------------------------------------
-// Decode GEMM for M <= 16*MT token rows: a weight-streaming kernel.  Grid
+// GEMM for M <= 16*MT rows of row-major activations (calls through the
+// prefill path with few tokens): a weight-streaming kernel.  Grid
 // (N / (16*CT), KS), KW wavefronts per block.  Every wavefront owns the block's
 // 16*CT output columns (CT 16x16x32 MFMA column tiles); the KS blocks of a
 // column tile split K into contiguous ranges and a block deals its k-steps of
