@@ -120,6 +120,28 @@ def test_ragged_fp32_block():
     _check_ragged(w, pos)
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_ragged_random_shapes(i):
+    """Seeded random ragged calls: heads per group 1 to 8, d_head 64 and 128,
+    1 to 40 sequences, one token (decode) or chunks of up to 48, each
+    sequence at its own position (0 included) and both RoPE layouts."""
+    import random
+    rng = random.Random(8675309 + 104729 * i)
+    dh = rng.choice([64, 128])
+    n_kv = rng.choice([1, 2])
+    n_rep = rng.choice([1, 2, 3, 4, 8])
+    H = n_kv * n_rep
+    S = 1 if rng.random() < 0.5 else rng.randint(2, 48)
+    B = rng.randint(2, 40) if S == 1 else rng.randint(2, 5)
+    pos = [rng.randint(0, 260) for _ in range(B)]
+    pos[rng.randrange(B)] = 0
+    w = workloads.BlockWorkload(f"ragged_rand{i}", "bf16", B=B, S=S, start_pos=max(pos), d=H * dh, H=H,
+                                n_kv=n_kv, d_head=dh, d_ff=64 * rng.randint(2, 32), theta=5e5, eps=1e-5,
+                                w_std=0.02, g_mean=1.0, g_std=0.05, max_seq=max(pos) + S + rng.randint(0, 9),
+                                seed=500 + i, rope_half=rng.random() < 0.4)
+    _check_ragged(w, pos)
+
+
 @pytest.mark.parametrize("S", [1, 24])
 def test_ragged_with_equal_positions_is_the_uniform_forward(S):
     """Every sequence at one position: the ragged call computes bitwise what
