@@ -4,8 +4,8 @@
 //  gemm_big2_kernel   prefill, large: 256 x 256 (or 256 x 192) tiles,
 //                     64-deep k-steps, 16x16x32 MFMA, two LDS stages,
 //                     weights in the k-step tiled layout
-//  gemm_big_grouped_kernel  grouped expert GEMMs (row-major expert weights):
-//                     256 x 256 tiles, 32-deep k-steps, four-stage LDS ring
+//  gemm_big_grouped_kernel  grouped expert GEMMs: the same tile body on
+//                     row-major expert weights
 //  gemm_mfma_kernel   prefill, small: 32x32x16 MFMA tiles, direct-to-LDS
 //                     loads, LDS double buffering
 //  gemm_skinny_kernel row-major activations of M <= 64 rows (prefill-path
@@ -332,183 +332,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_grouped_kernel(const T* __restri
 }
 
 // ------------------------------------------------------------------------------------
-// 256 x 256 tile body of the grouped expert GEMM (row-major weights).  Block
-// tile BM x BN (256 x 256 in use), BK = 32, four wavefronts in a 2 x 2 grid,
-// each BM/2 x BN/2 with 16x16x32 MFMAs (accumulators in AGPRs; one wavefront
-// per SIMD).  A four-stage
-// LDS ring is filled by direct-to-LDS loads issued from inline assembly (so
-// the compiler's counters for LDS reads stay exact; the kernel waits for
-// the loads itself).  One barrier opens each k-step: after it, stage k+1 is
-// complete for every wavefront, and the step's eight MFMA groups each take
-// one A row and about one B fragment of stage k+1 and one load of stage k+3
-// (A single-buffered in registers, B double-buffered).  LDS rows
-// are 64 bytes (4 chunks) with chunk index XORed by (row / 2) & 3, the
-// pattern measured free of bank conflicts for this operand read (16 rows at
-// each of the 4 chunks of a 64-byte row per instruction).
-// Rows beyond M / N are clamped to the last valid row.  K % 64 == 0.
-// ------------------------------------------------------------------------------------
-
-// Elements of LDS one gemm_big_tile needs.
-template <typename T, int BM, int BN>
-constexpr int big_tile_lds() { return 4 * (BM + BN) * 32; }
-
-// One BM x BN output tile at (m0, n0); lds holds big_tile_lds<T, BM, BN>().
-template <typename T, int BM, int BN, class Epi>
-__device__ __forceinline__ void gemm_big_tile(const T* __restrict__ A, const T* __restrict__ W, int M, int N,
-                                              int K, Epi epi, int m0, int n0, T* lds) {
-    typedef typename vec8<T>::type V8;
-    constexpr int STAGES = 4, BK = 32, NW = 4, NT = 256, WM = BM / 2, WN = BN / 2;
-    constexpr int TI = WM / 16, TJ = WN / 16;
-    constexpr int SA = BM * BK, SB = BN * BK, STG = SA + SB;  // elements per stage
-    constexpr int NA = BM * BK / 8 / NT, NB = BN * BK / 8 / NT; // loads per thread per stage
-    constexpr int ND = NA + NB;
-    constexpr int EPR = 64, CPAD = BN + 4;  // rows r, r+4, r+8, r+12 of a store on distinct banks
-    static_assert(NA * NT * 8 == SA && NB * NT * 8 == SB, "whole load instructions");
-    static_assert(EPR * CPAD * 4 <= STAGES * STG * (int)sizeof(T), "epilogue stage fits");
-    static_assert(STAGES * STG == big_tile_lds<T, BM, BN>(), "LDS size");
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    // load d of a stage: instruction (d % NA or d - NA) of this wavefront fills
-    // 64 consecutive 16-byte slots; lane l the slot l.  Addresses are the
-    // tile's first A (or W) row, wave-uniform, plus a per-lane byte offset
-    // (below 256 rows x K elements, far inside 32 bits for any K taken)
-    unsigned voff[ND], ldst[ND];
-    const unsigned lds0 = (unsigned)(size_t)(lds_ptr_t)lds;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-        const bool isa = d < NA;
-        const int slot0 = ((isa ? d : d - NA) * NW + wave) * 64;
-        const int p = slot0 + lane, row = p >> 2, c = (p & 3) ^ ((row >> 1) & 3);
-        const int r = isa ? min(m0 + row, M - 1) - m0 : min(n0 + row, N - 1) - n0;
-        voff[d] = (unsigned)(((size_t)r * K + c * 8) * sizeof(T));
-        ldst[d] = lds0 + (unsigned)(((isa ? 0 : SA) + slot0 * 8) * (int)sizeof(T));
-    }
-    const T* abase = A + (size_t)m0 * K;
-    const T* wbase = W + (size_t)n0 * K;
-    const int nk = K / BK;
-    // k-steps past the end reload the last one into a stage nobody reads
-    auto dma = [&](int kstep, int d) {
-        const int ks = kstep < nk ? kstep : nk - 1;
-        lds_dma16_s((d < NA ? abase : wbase) + ks * BK, voff[d],
-                    ldst[d] + (unsigned)((kstep % STAGES) * STG * (int)sizeof(T)));
-    };
-    f32x4 acc[TI][TJ];
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    V8 af[1][TI], bf[2][TJ];
-    // 16x16x32 operand: lane l holds row l % 16 and logical chunk l / 16
-    auto rd_a = [&](int kstep, int fb, int i) {
-        const T* la = lds + (kstep % STAGES) * STG;
-        const int row = wm * WM + i * 16 + (lane & 15), kc = lane >> 4;
-        af[fb][i] = *reinterpret_cast<const V8*>(la + row * BK + ((kc ^ ((row >> 1) & 3)) << 3));
-    };
-    auto rd_b = [&](int kstep, int fb, int j) {
-        const T* lb = lds + (kstep % STAGES) * STG + SA;
-        const int row = wn * WN + j * 16 + (lane & 15), kc = lane >> 4;
-        bf[fb][j] = *reinterpret_cast<const V8*>(lb + row * BK + ((kc ^ ((row >> 1) & 3)) << 3));
-    };
-
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-#pragma unroll
-        for (int d = 0; d < ND; ++d) dma(st, d);
-    wait_vm<(STAGES - 2) * ND>();  // stage 0 has landed
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < TI - 1; ++i) rd_a(0, 0, i);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) rd_b(0, 0, j);
-
-    // one k-step; fb (the B operand buffer) is a constant after inlining.
-    // The barrier opens the step: stage kt+1 has landed everywhere and every
-    // wavefront is done with stage kt-1, which the step's loads refill.
-    // After MFMA group i, A row i of the next step is read into the same
-    // registers (their last use has issued) and the next step's B fragments
-    // go to the other buffer, spread over the groups with the loads, so the
-    // LDS sees a steady stream of reads rather than a burst after a barrier.
-    // The last group reads nothing (its A row for the next step is read in
-    // that step's first group), so the step's end waits on no fresh read.
-    auto step = [&](const int kt, const int fb) {
-        const int kd = kt + STAGES - 1;
-        wait_vm<(STAGES - 3) * ND>();  // only stage kt+2 may still fly
-        lds_barrier();
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(af[0][i], bf[fb][j], acc[i][j]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int d = i; d < ND; d += TI) dma(kd, d);
-            if (i == 0) rd_a(kt, 0, TI - 1);
-            if (i < TI - 1) {
-                rd_a(kt + 1, 0, i);
-#pragma unroll
-                for (int j = i * TJ / (TI - 1); j < (i + 1) * TJ / (TI - 1); ++j) rd_b(kt + 1, fb ^ 1, j);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    for (int kt = 0; kt < nk; kt += 2) {
-        step(kt, 0);
-        step(kt + 1, 1);
-    }
-    wait_vm<0>();
-    __syncthreads();
-
-    // Epilogue: stage EPR rows of the fp32 tile through LDS, then hand
-    // contiguous 8-column chunks to the epilogue.
-    float* cst = reinterpret_cast<float*>(lds);
-#pragma unroll
-    for (int p = 0; p < BM / EPR; ++p) {
-        EpiPass<Epi, EPR, BN, NT, CPAD> pass;
-        pass.fetch(epi, tid, m0 + p * EPR, n0, M, N);
-        if (wm == (p * EPR) / WM) {
-#pragma unroll
-            for (int ii = 0; ii < EPR / 16; ++ii) {
-                const int i = ((p * EPR) % WM) / 16 + ii;
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        cst[(ii * 16 + 4 * (lane >> 4) + r) * CPAD + wn * WN + j * 16 + (lane & 15)] = acc[i][j][r];
-            }
-        }
-        __syncthreads();
-        pass.finish(epi, cst, tid, m0 + p * EPR, n0, M, N);
-        __syncthreads();
-    }
-}
-
-// Grouped GEMM over experts with the 256 x 256 tile body: as
-// gemm_grouped_kernel (row tiles of height BM numbered per group by
-// tile_off, a host-side bound tiles_m_max, idle blocks return at once).
-template <typename T, int BM, int BN, class Epi>
-__global__ void __launch_bounds__(256) gemm_big_grouped_kernel(const T* __restrict__ A, const T* __restrict__ W,
-                                                              const int* __restrict__ row_off,
-                                                              const int* __restrict__ tile_off, int E, int N,
-                                                              int K, int tiles_m_max, Epi epi) {
-    __shared__ __attribute__((aligned(16))) T lds[big_tile_lds<T, BM, BN>()];
-    int bid = blockIdx.x;
-    const int nb = gridDim.x;
-    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-    const int tn = bid / tiles_m_max, tmg = bid - tn * tiles_m_max;
-    if (tmg >= tile_off[E]) return;
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tile_off[mid] <= tmg) lo = mid;
-        else hi = mid - 1;
-    }
-    const int r0 = row_off[lo], rows = row_off[lo + 1] - r0;
-    gemm_big_tile<T, BM, BN, EpiRowOff<Epi>>(A + (size_t)r0 * K, W + (size_t)lo * N * K, rows, N, K,
-                                             EpiRowOff<Epi>{epi, r0}, (tmg - tile_off[lo]) * BM, tn * BN, lds);
-}
-
-// ------------------------------------------------------------------------------------
 // Large prefill GEMM with 64-deep k-steps: 256 x BN tiles (BN 256 or 192),
 // four wavefronts in a 2 x 2 grid (128 x BN/2 each, 16x16x32 MFMAs,
 // accumulators in AGPRs), two LDS stages of (256 + BN) x 128 bytes.  A stage
@@ -691,6 +514,33 @@ __global__ void __launch_bounds__(256) gemm_big2_kernel(const T* __restrict__ A,
     const int tm = first_m + in_group % gsize;
     const int tn = in_group / gsize;
     gemm_big2_tile<T, Epi, WT, BN>(A, W, M, N, K, epi, tm * BM, tn * BN, lds);
+}
+
+// Grouped GEMM over experts with the 256 x 256 tile body of gemm_big2_tile
+// on row-major expert weights: as gemm_grouped_kernel (row tiles of height
+// 256 numbered per group by tile_off, a host-side bound tiles_m_max, idle
+// blocks return at once).  The 64-deep body measured 2.29 ms per MoE prefill
+// step against 2.32 ms with a 32-deep four-stage one (A/B on one box).
+template <typename T, class Epi>
+__global__ void __launch_bounds__(256) gemm_big_grouped_kernel(const T* __restrict__ A, const T* __restrict__ W,
+                                                              const int* __restrict__ row_off,
+                                                              const int* __restrict__ tile_off, int E, int N,
+                                                              int K, int tiles_m_max, Epi epi) {
+    __shared__ __attribute__((aligned(16))) T lds[big2_tile_lds<T, 256>()];
+    int bid = blockIdx.x;
+    const int nb = gridDim.x;
+    if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+    const int tn = bid / tiles_m_max, tmg = bid - tn * tiles_m_max;
+    if (tmg >= tile_off[E]) return;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_off[mid] <= tmg) lo = mid;
+        else hi = mid - 1;
+    }
+    const int r0 = row_off[lo], rows = row_off[lo + 1] - r0;
+    gemm_big2_tile<T, EpiRowOff<Epi>, false, 256>(A + (size_t)r0 * K, W + (size_t)lo * N * K, rows, N, K,
+                                                  EpiRowOff<Epi>{epi, r0}, (tmg - tile_off[lo]) * 256, tn * 256, lds);
 }
 
 // ------------------------------------------------------------------------------------

@@ -252,7 +252,7 @@ static hipError_t grouped_swiglu_t(const void* A, const void* W, const int* row_
     const EpiSwiGLU<T> epi{(T*)z, N / 2, 0};
     if (moe_tile_m(MK, E) == 256) {
         const int tm = grouped_tiles_m(MK, E, 256), tn = (N + 255) / 256;
-        gemm_big_grouped_kernel<T, 256, 256, EpiSwiGLU<T>><<<(unsigned)tm * tn, 256, 0, s>>>(
+        gemm_big_grouped_kernel<T, EpiSwiGLU<T>><<<(unsigned)tm * tn, 256, 0, s>>>(
             (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, epi);
         return hipGetLastError();
     }
@@ -286,7 +286,7 @@ static hipError_t grouped_down_t(const void* A, const void* W, const int* row_of
                                  int MK, int N, int K, float* r, hipStream_t s) {
     if (moe_tile_m(MK, E) == 256) {
         const int tm = grouped_tiles_m(MK, E, 256), tn = (N + 255) / 256;
-        gemm_big_grouped_kernel<T, 256, 256, EpiStoreF32><<<(unsigned)tm * tn, 256, 0, s>>>(
+        gemm_big_grouped_kernel<T, EpiStoreF32><<<(unsigned)tm * tn, 256, 0, s>>>(
             (const T*)A, (const T*)W, row_off, tile_off, E, N, K, tm, EpiStoreF32{r, N});
         return hipGetLastError();
     }

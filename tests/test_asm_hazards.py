@@ -73,10 +73,13 @@ def _violations(asm_text):
     return loops, bad
 
 
-@pytest.mark.timeout(600)
-def test_inline_mfma_operands_come_from_loads(tmp_path):
-    out = tmp_path / "k_gemm.s"
-    cmd = [lib_build.HIPCC] + lib_build.FLAGS + ["-x", "hip", os.path.join(lib_build.CSRC, "k_gemm.hip"),
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("src", ["k_gemm.hip", "k_moe.hip"])
+def test_inline_mfma_operands_come_from_loads(tmp_path, src):
+    """The dense prefill GEMMs (k_gemm.hip) and the grouped expert GEMMs
+    (k_moe.hip) share the tile body with the inline-assembly MFMAs."""
+    out = tmp_path / (src + ".s")
+    cmd = [lib_build.HIPCC] + lib_build.FLAGS + ["-x", "hip", os.path.join(lib_build.CSRC, src),
                                                  "-S", "--cuda-device-only", "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     text = out.read_text()
