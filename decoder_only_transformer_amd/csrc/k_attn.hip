@@ -375,18 +375,30 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
         // one runs its softmax
         __builtin_amdgcn_s_setprio(1);
         f32x16 sacc[2];
+        // K fragments: the first key block's eight go out together, then
+        // each product of the first block is followed by the read of the
+        // second block's fragment for the same registers
+        auto kread = [&](int kb, int kk) -> V8 {
+            const int row = kb * 32 + prow;
+            const int ch = 2 * kk + (lane >> 5);
+            return *reinterpret_cast<const V8*>(ks + row * DH + ((ch ^ kswz128(row)) << 3));
+        };
+        V8 kf[DH / 16];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kk = 0; kk < DH / 16; ++kk) kf[kk] = kread(0, kk);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.0f;
-            const int row = kb * 32 + prow;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kk = 0; kk < DH / 16; ++kk) {
-                const int ch = 2 * kk + (lane >> 5);
-                const V8 kf = *reinterpret_cast<const V8*>(ks + row * DH + ((ch ^ kswz128(row)) << 3));
-                sacc[kb] = mfma32(kf, qf[kk], sacc[kb]);
-            }
+        for (int kk = 0; kk < DH / 16; ++kk) {
+            sacc[0] = mfma32(kf[kk], qf[kk], sacc[0]);
+            kf[kk] = kread(1, kk);
+            __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int kk = 0; kk < DH / 16; ++kk) sacc[1] = mfma32(kf[kk], qf[kk], sacc[1]);
         __builtin_amdgcn_s_setprio(0);
         const int t0 = tile * KT;
         float mx = -INFINITY;
