@@ -441,8 +441,9 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
                     pf[kb][cc][e] = from_f32<T>(p);
                 }
         __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int dt = 0; dt < DH / 32; ++dt) {
+        // V^T fragments of column block dt (four, from two transpose reads
+        // each), read one column block ahead of its products
+        auto vread = [&](int dt, V8 (&vf)[4]) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -456,11 +457,21 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
                     const T* pb = vs + kb2 * DH + ((((dcol >> 3) ^ vswz128(kb2)) << 3) | (dcol & 7));
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)pa);
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)pb);
-                    V8 vf;
-                    __builtin_memcpy(&vf, &lo, 8);
-                    __builtin_memcpy(reinterpret_cast<char*>(&vf) + 8, &hi, 8);
-                    oacc[dt] = mfma32(vf, pf[kb][cc], oacc[dt]);
+                    __builtin_memcpy(&vf[kb * 2 + cc], &lo, 8);
+                    __builtin_memcpy(reinterpret_cast<char*>(&vf[kb * 2 + cc]) + 8, &hi, 8);
                 }
+        };
+        V8 vfb[2][4];
+        vread(0, vfb[0]);
+#pragma unroll
+        for (int dt = 0; dt < DH / 32; ++dt) {
+            if (dt + 1 < DH / 32) vread(dt + 1, vfb[(dt + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) oacc[dt] = mfma32(vfb[dt & 1][kb * 2 + cc], pf[kb][cc], oacc[dt]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
     }
