@@ -417,7 +417,12 @@ __global__ void __launch_bounds__(NWH * QB * 64, 8 / (NWH * QB)) attn_prefill_fa
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+        {
+            // the other half of the wavefront holds the same queries' other
+            // keys: swap halves in registers (no LDS round trip)
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+        }
         const bool raise = mx > m_used + 8.0f;
         if (__builtin_amdgcn_ballot_w64(raise)) {
             const float m_new = raise ? mx : m_used;
