@@ -128,15 +128,29 @@ __device__ __forceinline__ V load_w(const V* p) {
 }
 
 // ---- wavefront reductions (64 lanes, fixed butterfly order) ----------------
+// Each step combines a lane with its partner in a group twice the size of the
+// last: quad permutes (groups of 2 and 4), the row half-mirror (8) and row
+// mirror (16) of DPP, then the 16- and 32-lane half swaps.  Every step runs in
+// the vector ALU (no LDS round trip), and partners add the same two values,
+// so every lane ends with the same, deterministic result.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <class Op> __device__ __forceinline__ float wave_reduce(float v, Op op) {
+    v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+    v = op(v, dpp_mov<0x140>(v));  // row_mirror
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // ---- MFMA wrappers -------------------------------------------------------------
