@@ -15,7 +15,8 @@
 //  gemm_decode_kernel decode (one token per sequence, <= 64 sequences):
 //                     activations and weights both k-step tiled, every
 //                     operand load one contiguous 1 KB piece, K split over
-//                     waves and, for long K, blocks (+ reduce_epilogue_kernel)
+//                     waves and, for long K, two blocks that finish the tile
+//                     themselves (or + reduce_epilogue_kernel)
 //  gemm_decode_wide_kernel  decode, very wide outputs (gate/up): the 7 or 8
 //                     column tiles of a block share the activations through LDS
 //  gemm_simple_kernel fp32 blocks: plain LDS-tiled fp32 FMA
@@ -666,13 +667,20 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(const T* __restric
 // Loads past the end of a run repeat a valid k-step and are discarded.  The
 // block sums its wavefronts in LDS in a fixed order; with KS == 1 it runs the
 // epilogue on rows < M, otherwise it stores an fp32 partial [ks][M][N] for
-// reduce_epilogue_kernel.  N % (16*CT) == 0, K % 32 == 0.
+// reduce_epilogue_kernel.  With `cnt` (KS == 2, one zeroed word per block
+// column) the pair finishes itself instead: both blocks store their partial,
+// each then counts itself in cnt[blockIdx.x], and the one that counts second
+// adds the other's partial, runs the epilogue and clears the word.  Nobody
+// waits; the partials and the count move with agent-coherent accesses
+// (sc1), and the sum part0 + part1 has the same bits as the reduction
+// kernel's.  N % (16*CT) == 0, K % 32 == 0.
 // ------------------------------------------------------------------------------------
 template <typename T, int MT, int CT, int U, int NW, bool PARTIAL, class Epi, bool NT = false>
 __global__ void __launch_bounds__(NW * 64) gemm_decode_kernel(const T* __restrict__ At,
                                                               const T* __restrict__ Wt, int M,
                                                               int N, int K, int KS,
-                                                              float* __restrict__ part, Epi epi) {
+                                                              float* __restrict__ part, Epi epi,
+                                                              unsigned* cnt = nullptr) {
     typedef typename vec8<T>::type V8;
     constexpr int COLS = 16 * CT;
     __shared__ float red[NW][MT * 16][COLS + 1];
@@ -736,17 +744,55 @@ __global__ void __launch_bounds__(NW * 64) gemm_decode_kernel(const T* __restric
                 red[wave][t * 16 + 4 * (lane >> 4) + r][cc * 16 + (lane & 15)] = acc[t][cc][r];
     __syncthreads();
     const int n0 = nt0 * 16;
+    // this block's sum of chunk q (8 columns of one row), waves in order
+    auto block_sum = [&](int row, int c8, float (&v)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float sacc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) sacc += red[w][row][c8 * 8 + e];
+            v[e] = sacc;
+        }
+    };
+    if (PARTIAL && cnt) {
+        __shared__ unsigned arrived;
+        const __amdgpu_buffer_rsrc_t r = agent_rsrc(part);
+        auto off = [&](int ks, int row, int c8) { return (unsigned)((((size_t)ks * M + row) * N + n0 + c8 * 8) * 4); };
+        for (int q = threadIdx.x; q < MT * 16 * (COLS / 8); q += NW * 64) {
+            const int row = q / (COLS / 8), c8 = q % (COLS / 8);
+            if (row < M) {
+                float v[8];
+                block_sum(row, c8, v);
+                store16_agent(r, off(ksp, row, c8), f32x4{v[0], v[1], v[2], v[3]});
+                store16_agent(r, off(ksp, row, c8) + 16, f32x4{v[4], v[5], v[6], v[7]});
+            }
+        }
+        wait_vm<0>();  // the partial is stored before the block counts itself
+        __syncthreads();
+        if (threadIdx.x == 0)
+            arrived = __hip_atomic_fetch_add(cnt + blockIdx.x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (arrived == 0) return;  // the other block finishes the tile
+        if (threadIdx.x == 0) __hip_atomic_store(cnt + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = threadIdx.x; q < MT * 16 * (COLS / 8); q += NW * 64) {
+            const int row = q / (COLS / 8), c8 = q % (COLS / 8);
+            if (row < M) {
+                float v[8];
+                block_sum(row, c8, v);
+                const f32x4 a = load16_agent(r, off(ksp ^ 1, row, c8)), b = load16_agent(r, off(ksp ^ 1, row, c8) + 16);
+                const float o[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = ksp == 0 ? v[e] + o[e] : o[e] + v[e];
+                epi.row8(row, n0 + c8 * 8, v);
+            }
+        }
+        return;
+    }
     for (int q = threadIdx.x; q < MT * 16 * (COLS / 8); q += NW * 64) {
         const int row = q / (COLS / 8), c8 = q % (COLS / 8);
         if (row < M) {
             float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float sacc = 0.0f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) sacc += red[w][row][c8 * 8 + e];
-                v[e] = sacc;
-            }
+            block_sum(row, c8, v);
             if (PARTIAL) store8(part + ((size_t)ksp * M + row) * N + n0 + c8 * 8, v);
             else epi.row8(row, n0 + c8 * 8, v);
         }

@@ -90,6 +90,12 @@ static hipError_t run_decode_mt(const T* At, const T* Wt, int M, int N, int K, c
     // split keeps one block per CU (measured faster than one split, despite
     // the extra reduction launch, from K = 8192 up)
     if (tiles >= 192 && tiles % 2 == 0 && nks >= 256 && (size_t)2 * M * N <= ws.cap) {
+        if (ws.cnt && ws.ncnt >= tiles / 2) {
+            // the pair of blocks of a column tile adds its halves itself
+            gemm_decode_kernel<T, MT, 2, 2, 4, true, Epi, NT><<<dim3(tiles / 2, 2), 256, 0, s>>>(
+                At, Wt, M, N, K, 2, ws.part, epi, ws.cnt);
+            return hipGetLastError();
+        }
         gemm_decode_kernel<T, MT, 2, 2, 4, true, Epi, NT><<<dim3(tiles / 2, 2), 256, 0, s>>>(At, Wt, M, N, K, 2, ws.part, epi);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

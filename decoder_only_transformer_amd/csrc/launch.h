@@ -63,8 +63,13 @@ constexpr int kSkinnyMaxSplit = 8;
 size_t skinny_partials_floats(int max_m, int max_n);
 struct SplitWs {
     float* part;
-    size_t cap;
+    size_t cap;                // floats at part
+    unsigned* cnt = nullptr;   // zeroed words: a two-way split decode GEMM finishes itself
+    int ncnt = 0;
 };
+// words of SplitWs::cnt a block's workspace holds (one per block column of a
+// split decode GEMM)
+constexpr int kSplitCounters = 4096;
 hipError_t gemm_qkv(Elem op, Elem cache, const void* A, const void* W, int M, int N, int K,
                     const QkvEpi& e, const SplitWs& part, hipStream_t s);
 // out(fp32) = resid + A W^T

@@ -235,6 +235,21 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, un
                      "s"(lds_byte_addr)
                      : "memory", "m0");
 }
+// 16-byte accesses through a buffer resource with the agent-scope coherence
+// bit (sc1), the cache policy of relaxed device-scope atomics: a store is
+// visible to a later sc1 load from any XCD once it has completed (vmcnt), with
+// no cache-wide write-back or invalidate.  Offsets in bytes; accesses beyond
+// 2 GiB from the base are dropped by the range check.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t agent_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void store16_agent(__amdgpu_buffer_rsrc_t r, unsigned off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 16);
+}
+__device__ __forceinline__ f32x4 load16_agent(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+}
+
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 

@@ -59,6 +59,7 @@ struct lb_block {
     float* part = nullptr;       // decode attention partials
     float* gpart = nullptr;      // split-K decode GEMM partials
     size_t gpart_cap = 0;        // floats
+    unsigned* gcnt = nullptr;    // arrival counts of the two-way split decode GEMM (zeroed at init)
     // decode activations (<= kDecodeRows token rows) in the k-step tiled layout
     void* at_n1 = nullptr;
     void* at_o = nullptr;
@@ -110,6 +111,7 @@ struct Workspace {
     float* part = nullptr;
     float* gpart = nullptr;
     size_t gpart_cap = 0;
+    unsigned* gcnt = nullptr;
     void* at_n1 = nullptr;
     void* at_o = nullptr;
     void* at_n2 = nullptr;
@@ -129,6 +131,7 @@ static Workspace handle_workspace(const lb_block* blk) {
     w.part = blk->part;
     w.gpart = blk->gpart;
     w.gpart_cap = blk->gpart_cap;
+    w.gcnt = blk->gcnt;
     w.at_n1 = blk->at_n1;
     w.at_o = blk->at_o;
     w.at_n2 = blk->at_n2;
@@ -292,14 +295,15 @@ static lb_status validate_config(const lb_config* c) {
 // blocks (fp16 or bf16) and 4 in fp32 blocks.
 struct Sizes {
     size_t rope, n1, n2, q, o, z, h;                         // every block
-    size_t kws, vws, part, gpart, at_n1, at_o, at_n2, at_z;  // bf16 blocks only (else 0)
+    size_t kws, vws, part, gpart, gcnt, at_n1, at_o, at_n2, at_z;  // bf16 blocks only (else 0)
     size_t ws_rows, gpart_floats;
     size_t w_qkv, w_o, w_gu, w_down, g1, g2;                 // the weights of one block
     size_t staging;                                          // held while init packs (bf16)
     size_t g_final, act;                                     // a stack's final gain, activations
 
     uint64_t workspace() const {
-        return (uint64_t)rope + n1 + n2 + q + o + z + h + kws + vws + part + gpart + at_n1 + at_o + at_n2 + at_z;
+        return (uint64_t)rope + n1 + n2 + q + o + z + h + kws + vws + part + gpart + gcnt + at_n1 + at_o + at_n2 +
+               at_z;
     }
     uint64_t layer() const { return (uint64_t)w_qkv + w_o + w_gu + w_down + g1 + g2; }
 };
@@ -324,6 +328,7 @@ static Sizes sizes_of(const lb_config& c) {
         z.gpart_floats = lb::skinny_partials_floats(c.max_tokens < 64 ? c.max_tokens : 64,
                                                     (int)std::max(std::max(nqkv, d), 2 * dff));
         z.gpart = z.gpart_floats * sizeof(float);
+        z.gcnt = (size_t)lb::kSplitCounters * sizeof(unsigned);
         z.at_n1 = z.at_n2 = (size_t)kDecodeRows * d * eo;
         z.at_o = (size_t)kDecodeRows * qd * eo;
         z.at_z = (size_t)kDecodeRows * dff * eo;
@@ -424,8 +429,10 @@ static lb_status create_core(const lb_config* cfg, Elem op_type, lb_block** out)
         blk->ws_rows = z.ws_rows;
         blk->gpart_cap = z.gpart_floats;
         ok = dalloc(blk, &blk->kws, z.kws) && dalloc(blk, &blk->vws, z.vws) && dalloc(blk, &blk->part, z.part) &&
-             dalloc(blk, &blk->gpart, z.gpart) && dalloc(blk, &blk->at_n1, z.at_n1) &&
-             dalloc(blk, &blk->at_o, z.at_o) && dalloc(blk, &blk->at_n2, z.at_n2) && dalloc(blk, &blk->at_z, z.at_z);
+             dalloc(blk, &blk->gpart, z.gpart) && dalloc(blk, &blk->gcnt, z.gcnt) &&
+             dalloc(blk, &blk->at_n1, z.at_n1) && dalloc(blk, &blk->at_o, z.at_o) && dalloc(blk, &blk->at_n2, z.at_n2) &&
+             dalloc(blk, &blk->at_z, z.at_z);
+        ok = ok && hipMemset(blk->gcnt, 0, z.gcnt) == hipSuccess;
     }
     if (!ok) {
         free_all(blk);
@@ -832,7 +839,7 @@ static lb_status run_forward(lb_block* blk, const LayerW& L, const void* x, int 
     // GEMMs on k-step tiled activations and weights
     const bool dec = dt == Elem::BF16 && S == 1 && M <= kDecodeRows;
     const int mt = dec ? lb::decode_row_tiles(M) : 0;
-    const lb::SplitWs ws{wk.gpart, wk.gpart_cap};
+    const lb::SplitWs ws{wk.gpart, wk.gpart_cap, wk.gcnt, wk.gcnt ? lb::kSplitCounters : 0};
     void* n1 = dec ? wk.at_n1 : wk.n1;
     void* o = dec ? wk.at_o : wk.o;
     const bool moe = blk->moe_E > 0;
