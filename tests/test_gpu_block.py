@@ -163,6 +163,36 @@ def test_decode_llama3_width_batches(B):
     run.close()
 
 
+def test_decode_steps_reuse_the_split_down_product():
+    """Three decode steps on one handle at the Llama-3-8B width: the down
+    product (K = 14336) runs as two-way K splits whose blocks finish the tile
+    themselves through per-tile arrival words kept in the workspace, which
+    every step must leave cleared for the next.  Each step is held to the bar
+    against the oracle fed the cache as the GPU left it ("Full Llama 3
+    transformer block", How it works: decode appends at start_pos and attends
+    to every cached position before it)."""
+    w = workloads.with_overrides(workloads.get("llama3_8b_decode"), B=4, start_pos=100, max_seq=128, seed=77)
+    t = workloads.generate(w)
+    run = BlockOnGpu(w, t)
+    try:
+        for step in range(3):
+            sp = w.start_pos + step
+            ws = workloads.with_overrides(w, start_pos=sp)
+            ts = dict(t)
+            if step > 0:
+                ts["x"] = workloads.generate(workloads.with_overrides(w, seed=77 + step), with_cache=False)["x"]
+                k, v = run.kv
+                ts["k_prefix"] = k[:, :, :sp, :].cpu()
+                ts["v_prefix"] = v[:, :, :sp, :].cpu()
+            y = run.forward(x=ts["x"].to("cuda"), start_pos=sp).double().cpu().numpy().reshape(w.M, w.d)
+            y_orc = oracle_rows(ws, ts)[0].reshape(w.M, w.d)
+            err = rel_err(y, y_orc)
+            log(f"    step {step} (start_pos {sp}): max|err|/rms = {err:.3e}")
+            assert err <= tol_of(ws, "auto"), (step, err)
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("B", [5, 20, 40])
 def test_decode_wide_gate_up_blocks_of_eight(B):
     """Decode with a gate/up width whose column tiles 7 does not divide
