@@ -1,7 +1,8 @@
 // Mixture-of-experts FFN ("Llama 4 From Scratch", The idea: N expert FFNs, a
 // router that sends each token to its top k, one always-on shared expert).
 //
-//   router      moe_router_kernel: logits = n2 . router^T (fp32), the top k
+//   router      moe_router_kernel: logits = n2 . router^T (fp32 sums of exact
+//               fp16 or bf16 products, 16 tokens per block), the top k
 //               (larger first, the lower index among equal logits) and the
 //               softmax of their logits
 //   grouping    moe_route_kernel: a counting sort of the (token, choice)
@@ -22,93 +23,125 @@
 namespace lb {
 
 // ---- router and top k ------------------------------------------------------------
-// One block per token: the row goes to LDS as fp32; wavefront w scores experts
-// w, w+4, ... (each lane a strided slice of the dot product, then the
-// wavefront's fixed butterfly), then wavefront 0 picks the top k.
-template <typename T>
-__global__ void __launch_bounds__(256) moe_router_kernel(const T* __restrict__ n, const T* __restrict__ wr,
+// One block per 16 tokens: the logits of the 16 tokens and 16*NE16 experts
+// come from 16x16x32 MFMAs (tokens x experts tiles; products exact, fp32
+// sums), d split over the four wavefronts in contiguous k ranges and their
+// partial sums added in LDS in wavefront order, so the result is fixed.  The
+// router matrix is read once per 16 tokens (one block per token read it once
+// per token: 67 us of an 8B-width MoE prefill step for 16 experts).  Then
+// each wavefront picks the top k of four tokens: k rounds of a wavefront
+// argmax over the experts not yet taken (lane l holds experts l, l+64,
+// l+128, l+192); NaN counts as -inf so that every comparison is a total order
+// and every lane agrees; the lower index wins among equal logits.
+template <typename T, int NE16>
+__global__ void __launch_bounds__(256) moe_router_kernel(const T* __restrict__ n, const T* __restrict__ wr, int M,
                                                          int d, int E, int K, float* __restrict__ logits,
                                                          int* __restrict__ sel, float* __restrict__ wts) {
-    __shared__ __attribute__((aligned(16))) float row[kMoeMaxWidth];
-    __shared__ float lg[kMoeMaxExperts];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const T* nr = n + (size_t)t * d;
-    for (int i = tid * 8; i < d; i += 256 * 8) {
-        float v[8];
-        load8(nr + i, v);
+    typedef typename vec8<T>::type V8;
+    __shared__ float part[4][16][NE16 * 16 + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * 16;
+    // operand fragments: lane -> row lane % 16 (token, or expert), 8
+    // consecutive k at 8 * (lane / 16) of each 32-wide k step
+    const int nks = (d + 31) / 32;
+    const int kb = wave * nks / 4, ke = (wave + 1) * nks / 4;
+    const int kl = 8 * (lane >> 4);
+    const T* arow = n + (size_t)min(t0 + (lane & 15), M - 1) * d + kl;
+    const T* brow[NE16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) row[i + e] = v[e];
-    }
-    __syncthreads();
-    for (int e = wave; e < E; e += 4) {
-        const T* w = wr + (size_t)e * d;
-        float acc = 0.0f;
-        for (int i = lane * 8; i < d; i += 64 * 8) {
-            float v[8];
-            load8(w + i, v);
+    for (int c = 0; c < NE16; ++c) brow[c] = wr + (size_t)min(c * 16 + (lane & 15), E - 1) * d + kl;
+    f32x4 acc[NE16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc += row[i + j] * v[j];
+    for (int c = 0; c < NE16; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // U k steps per group, all their loads issued before their products
+    // (about 16 loads in flight per lane at any NE16)
+    constexpr int U = NE16 >= 8 ? 1 : 8 / NE16;
+    for (int k0 = kb; k0 < ke; k0 += U) {
+        V8 a[U], b[U][NE16];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (k0 + u) * 32;
+            // d % 8 == 0: a lane's 8 values are all inside or all past d
+            const bool in = k0 + u < ke && k + kl < d;
+            a[u] = in ? *reinterpret_cast<const V8*>(arow + k) : V8{};
+#pragma unroll
+            for (int c = 0; c < NE16; ++c) b[u][c] = in ? *reinterpret_cast<const V8*>(brow[c] + k) : V8{};
         }
-        acc = wave_sum(acc);
-        if (lane == 0) lg[e] = acc;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < NE16; ++c) acc[c] = mfma16(a[u], b[u][c], acc[c]);
     }
+    // lane holds token 4 * (lane / 16) + r, expert c * 16 + lane % 16
+#pragma unroll
+    for (int c = 0; c < NE16; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[wave][4 * (lane >> 4) + r][c * 16 + (lane & 15)] = acc[c][r];
     __syncthreads();
-    if (wave != 0) return;
-    for (int e = lane; e < E; e += 64) logits[(size_t)t * E + e] = lg[e];
-
-    // k rounds of a wavefront argmax over the experts not yet taken (lane l
-    // holds experts l, l+64, l+128, l+192); NaN counts as -inf so that every
-    // comparison is a total order and every lane agrees
-    float top[kMoeMaxTopK];
-    int idx[kMoeMaxTopK];
-    unsigned taken = 0;
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const int tl = wave * 4 + q4, t = t0 + tl;
+        if (t >= M) break;  // whole wavefronts leave together
+        float lv[kMoeMaxExperts / 64];
 #pragma unroll
-    for (int j = 0; j < kMoeMaxTopK; ++j) {
-        top[j] = -INFINITY;
-        idx[j] = 0;
-        if (j < K) {
-            float bv = -INFINITY;
-            int bi = INT_MAX;
+        for (int q = 0; q < kMoeMaxExperts / 64; ++q) {
+            const int e = lane + 64 * q;
+            lv[q] = -INFINITY;
+            if (e < E) {
+                lv[q] = (part[0][tl][e] + part[1][tl][e]) + (part[2][tl][e] + part[3][tl][e]);
+                logits[(size_t)t * E + e] = lv[q];
+            }
+        }
+        float top[kMoeMaxTopK];
+        int idx[kMoeMaxTopK];
+        unsigned taken = 0;
 #pragma unroll
-            for (int q = 0; q < kMoeMaxExperts / 64; ++q) {
-                const int e = lane + 64 * q;
-                if (e < E && !((taken >> q) & 1u)) {
-                    float v = lg[e];
-                    v = v != v ? -INFINITY : v;
-                    if (bi == INT_MAX || v > bv) {
-                        bv = v;
-                        bi = e;
+        for (int j = 0; j < kMoeMaxTopK; ++j) {
+            top[j] = -INFINITY;
+            idx[j] = 0;
+            if (j < K) {
+                float bv = -INFINITY;
+                int bi = INT_MAX;
+#pragma unroll
+                for (int q = 0; q < kMoeMaxExperts / 64; ++q) {
+                    const int e = lane + 64 * q;
+                    if (e < E && !((taken >> q) & 1u)) {
+                        float v = lv[q];
+                        v = v != v ? -INFINITY : v;
+                        if (bi == INT_MAX || v > bv) {
+                            bv = v;
+                            bi = e;
+                        }
                     }
                 }
-            }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
+                for (int o = 32; o >= 1; o >>= 1) {
+                    const float ov = __shfl_xor(bv, o, 64);
+                    const int oi = __shfl_xor(bi, o, 64);
+                    if (ov > bv || (ov == bv && oi < bi)) {
+                        bv = ov;
+                        bi = oi;
+                    }
                 }
+                top[j] = bv;
+                idx[j] = bi;
+                if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
             }
-            top[j] = bv;
-            idx[j] = bi;
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
         }
-    }
-    if (lane == 0) {
-        // softmax over the chosen logits; top[0] is the largest
-        float p[kMoeMaxTopK], s = 0.0f;
+        if (lane == 0) {
+            // softmax over the chosen logits; top[0] is the largest
+            float p[kMoeMaxTopK], sum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kMoeMaxTopK; ++j) {
-            p[j] = j < K ? exp2_hw((top[j] - top[0]) * kLog2e) : 0.0f;
-            s += p[j];
-        }
-        const float inv = 1.0f / s;
+            for (int j = 0; j < kMoeMaxTopK; ++j) {
+                p[j] = j < K ? exp2_hw((top[j] - top[0]) * kLog2e) : 0.0f;
+                sum += p[j];
+            }
+            const float inv = 1.0f / sum;
 #pragma unroll
-        for (int j = 0; j < kMoeMaxTopK; ++j) {
-            if (j < K) {
-                sel[(size_t)t * K + j] = idx[j];
-                wts[(size_t)t * K + j] = p[j] * inv;
+            for (int j = 0; j < kMoeMaxTopK; ++j) {
+                if (j < K) {
+                    sel[(size_t)t * K + j] = idx[j];
+                    wts[(size_t)t * K + j] = p[j] * inv;
+                }
             }
         }
     }
@@ -198,18 +231,28 @@ struct EpiStoreF32 {
 
 // ---- launchers -------------------------------------------------------------------------
 
+// experts in tiles of 16: 1, 2, 4, 8 or 16 of them (E <= 256)
+template <typename T>
+static hipError_t router_t(const T* n, const T* wr, int M, int d, int E, int K, float* logits, int* sel, float* wts,
+                           hipStream_t s) {
+    const unsigned grid = (unsigned)((M + 15) / 16);
+    const int ne = (E + 15) / 16;
+    if (ne <= 1) moe_router_kernel<T, 1><<<grid, 256, 0, s>>>(n, wr, M, d, E, K, logits, sel, wts);
+    else if (ne <= 2) moe_router_kernel<T, 2><<<grid, 256, 0, s>>>(n, wr, M, d, E, K, logits, sel, wts);
+    else if (ne <= 4) moe_router_kernel<T, 4><<<grid, 256, 0, s>>>(n, wr, M, d, E, K, logits, sel, wts);
+    else if (ne <= 8) moe_router_kernel<T, 8><<<grid, 256, 0, s>>>(n, wr, M, d, E, K, logits, sel, wts);
+    else moe_router_kernel<T, 16><<<grid, 256, 0, s>>>(n, wr, M, d, E, K, logits, sel, wts);
+    return hipGetLastError();
+}
+
 hipError_t launch_moe_router(Elem op, const void* n, const void* wr, int M, int d, int E, int K,
                              float* logits, int* sel, float* wts, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     if (d % 8 != 0 || d > kMoeMaxWidth || E < 1 || E > kMoeMaxExperts || K < 1 || K > kMoeMaxTopK || K > E)
         return hipErrorInvalidValue;
-    if (op == Elem::F16)
-        moe_router_kernel<f16><<<M, 256, 0, s>>>((const f16*)n, (const f16*)wr, d, E, K, logits, sel, wts);
-    else if (op == Elem::BF16)
-        moe_router_kernel<bf16><<<M, 256, 0, s>>>((const bf16*)n, (const bf16*)wr, d, E, K, logits, sel, wts);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+    if (op == Elem::F16) return router_t<f16>((const f16*)n, (const f16*)wr, M, d, E, K, logits, sel, wts, s);
+    if (op == Elem::BF16) return router_t<bf16>((const bf16*)n, (const bf16*)wr, M, d, E, K, logits, sel, wts, s);
+    return hipErrorInvalidValue;
 }
 
 // Row-tile height of the grouped GEMMs: 256-row tiles of the large kernel
