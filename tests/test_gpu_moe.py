@@ -163,6 +163,14 @@ def test_moe_256_row_tiles(E, k):
                      seed=20 + E))
 
 
+@pytest.mark.parametrize("E,k,seed", [(20, 2, 31), (40, 2, 32), (100, 3, 33), (256, 8, 34)])
+def test_moe_router_expert_tiles(E, k, seed):
+    """Routers over 2, 4, 8 and 16 tiles of 16 experts (the last tile partial
+    where E is not a multiple of 16), up to the largest expert count and top k
+    the library takes; 200 tokens, so the last block of 16 tokens is partial."""
+    check_moe(_small(name=f"moe_router_{E}_{k}", B=2, S=100, n_experts=E, top_k=k, d_ff_expert=128, seed=seed))
+
+
 def test_moe_llama3_width_sampled():
     """The 8B-width attention with a MoE FFN (8 experts of width 4096, top 2,
     shared expert 4096) over 2 x 256 tokens; rows sampled at the ends of each
