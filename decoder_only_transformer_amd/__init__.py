@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libllama_block.so")
 LB_F32, LB_BF16 = 0, 1
 LB_OPERANDS_AUTO, LB_OPERANDS_F16, LB_OPERANDS_BF16 = 0, 1, 2
 LB_OK, LB_ERR_INVALID_ARG, LB_ERR_UNSUPPORTED, LB_ERR_OOM, LB_ERR_HIP = 0, 1, 2, 3, 4
-STAGES = {"n1": 0, "q": 1, "o": 2, "h": 3, "n2": 4, "z": 5}
+STAGES = {"n1": 0, "q": 1, "o": 2, "h": 3, "n2": 4, "z": 5, "routed": 6}
 ELEM_NAMES = {0: "f32", 1: "bf16", 2: "f16"}
 
 MAX_RAGGED_BATCH = 64

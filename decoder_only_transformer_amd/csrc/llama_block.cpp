@@ -1320,6 +1320,9 @@ static bool stage_buffer(const lb_block* blk, lb_stage which, const void** ptr, 
         case LB_STAGE_H: *ptr = blk->h; *elem = Elem::F32; *cols = c.d_model; return true;
         case LB_STAGE_N2: *ptr = blk->n2; *elem = blk->op; *cols = c.d_model; return true;
         case LB_STAGE_Z: *ptr = blk->z; *elem = blk->op; *cols = c.d_ff; return true;
+        case LB_STAGE_ROUTED:
+            if (blk->moe_E == 0) return false;
+            *ptr = blk->m_r; *elem = Elem::F32; *cols = c.d_model; return true;
     }
     return false;
 }
@@ -1369,8 +1372,26 @@ extern "C" lb_status llama_block_copy_stage(lb_block* blk, lb_stage which, void*
     int64_t cols;
     if (!dst || !stage_buffer(blk, which, &p, &e, &cols))
         return fail(blk, LB_ERR_INVALID_ARG, "bad stage or NULL destination");
-    const size_t cap = (size_t)blk->cfg.max_tokens * (size_t)cols * esz(e);
+    const size_t rows_per_token = which == LB_STAGE_ROUTED ? (size_t)blk->moe_K : 1;
+    const size_t cap = (size_t)blk->cfg.max_tokens * rows_per_token * (size_t)cols * esz(e);
     if (bytes > cap) return fail(blk, LB_ERR_INVALID_ARG, "%zu bytes exceed the stage buffer (%zu)", bytes, cap);
+    if (which == LB_STAGE_ROUTED) {
+        // expert rows are stored grouped by expert: row slot[t*K + j] holds
+        // pair (t, j); gather whole rows (16-byte pieces) into pair order
+        hipPointerAttribute_t attr{};
+        if (hipPointerGetAttributes(&attr, dst) != hipSuccess || attr.type != hipMemoryTypeDevice) {
+            (void)hipGetLastError();
+            return fail(blk, LB_ERR_INVALID_ARG, "the routed stage is copied to device memory only");
+        }
+        const size_t row_bytes = (size_t)cols * 4;
+        if (bytes % row_bytes != 0 || bytes / row_bytes > (size_t)blk->last_m * rows_per_token)
+            return fail(blk, LB_ERR_INVALID_ARG, "copy_stage: the routed stage copies whole rows of the last forward");
+        const int rows = (int)(bytes / row_bytes);
+        hipError_t err = lb::launch_moe_gather(Elem::F16, blk->m_r, blk->m_slot, rows, 1, (int)cols * 2, dst,
+                                               (hipStream_t)stream);
+        if (err != hipSuccess) return fail(blk, LB_ERR_HIP, "copy_stage: %s", hipGetErrorString(err));
+        return LB_OK;
+    }
     const int tiled_mt = (which == LB_STAGE_N2 || which == LB_STAGE_Z) ? blk->last_ffn_mt : blk->last_mt;
     if (tiled_mt > 0 && which != LB_STAGE_Q && which != LB_STAGE_H) {
         // the last forward was a decode: this stage lives in the tiled layout;

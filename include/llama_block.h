@@ -345,9 +345,15 @@ const char* llama_block_last_error(const lb_block* blk);
  *   N1 RMSNorm_1(x) [d_model]     Q q after RoPE [n_heads*d_head]
  *   O attention output [n_heads*d_head]   H residual h, always fp32 [d_model]
  *   N2 RMSNorm_2(h) [d_model]     Z SiLU(gate)*up [d_ff]
- * Element type: fp32 for fp32 blocks and for H; otherwise the operand type. */
+ * Element type: fp32 for fp32 blocks and for H; otherwise the operand type.
+ * MoE blocks add ROUTED: each routed expert's output for its token before
+ * the routing weight ("Llama 4 From Scratch", The idea: the chosen expert
+ * FFNs of a token), fp32 [batch*seq_len*top_k][d_model], row t*top_k + j for
+ * choice j of token row t; its buffer holds top_k rows per token row, and it
+ * is copied only to device memory (LB_ERR_INVALID_ARG for host memory or a
+ * dense block). */
 typedef enum { LB_STAGE_N1 = 0, LB_STAGE_Q = 1, LB_STAGE_O = 2, LB_STAGE_H = 3,
-               LB_STAGE_N2 = 4, LB_STAGE_Z = 5 } lb_stage;
+               LB_STAGE_N2 = 4, LB_STAGE_Z = 5, LB_STAGE_ROUTED = 6 } lb_stage;
 typedef enum { LB_ELEM_F32 = 0, LB_ELEM_BF16 = 1, LB_ELEM_F16 = 2 } lb_elem;
 
 /* Operand type the handle's matrix products run in: LB_ELEM_F32 for fp32

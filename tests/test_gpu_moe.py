@@ -14,7 +14,9 @@ the oracle in fp64.  So the tests check, per token:
     order), so only near-ties may be resolved differently;
   * y, and the written cache rows, against the oracle run with the library's
     choice, at the block bar (2e-2 rms), and the weights against the
-    oracle's softmax of the chosen logits within 4 d_t.
+    oracle's softmax of the chosen logits within 4 d_t;
+  * every routed expert's output row (before its weight) against that
+    expert's FFN of the library's n2 row, at 2e-2 of those rows' own rms.
 """
 import numpy as np
 import pytest
@@ -99,6 +101,23 @@ def check_moe(w, rows=None, start_pos=None):
         f"weights within {werr:.2f} of their bound")
     assert err <= tol, err
     assert werr <= 1.0, werr
+    # every routed expert's output at its own scale (a few % of y's rms at
+    # these weights, so y alone would hide errors in it): the oracle's FFN of
+    # that expert alone (top 1 forced to it, shared expert zeroed) on the
+    # library's n2 row
+    r_gpu = run.block.stage("routed", w.M * K).double().cpu().numpy().reshape(w.M, K, w.d)
+    one = dict(moe, n_experts=1, top_k=1)
+    solo = {n: np.zeros(tuple(t[n].shape)) for n in ("w_gate", "w_up", "w_down")}
+    r_o = np.zeros((len(rows), K, w.d))
+    for e in sorted({int(sel[r][j]) for r in rows for j in range(K)}):
+        solo.update({n: t[n][e:e + 1].double().numpy() for n in oracle.MOE_WEIGHT_NAMES})
+        for i, r in enumerate(rows):
+            for j in range(K):
+                if int(sel[r][j]) == e:
+                    r_o[i, j] = oracle.moe_ffn(cfg, one, n2[r], solo, force_sel=[0])[0]
+    rerr = rel_err(r_gpu[rows], r_o)
+    log(f"    routed expert rows {rerr:.3e} (tol {tol:g})")
+    assert rerr <= tol, rerr
     seqs = sorted({r // w.S for r in rows})
     for b in seqs:
         hi = max(r % w.S for r in rows if r // w.S == b) + 1
