@@ -58,6 +58,15 @@ def _logit_bound(n2, router):
     return 2.0 ** -10 * np.max(np.abs(n2) @ np.abs(router).T, axis=1)
 
 
+def _worst(got, want, rows, sel, k=1):
+    """Where the largest error of got against want sits: flat row (and, for
+    routed rows, its token and choice), column, both values, expert(s)."""
+    i, c = np.unravel_index(np.argmax(np.abs(got - want)), got.shape)
+    r = rows[i]
+    where = f"token {r // k} choice {r % k}" if k > 1 else f"row {r}"
+    return f"worst at {where} col {c}: {got[i, c]:.6g} vs {want[i, c]:.6g}, expert(s) {list(sel[r])}"
+
+
 def check_moe(w, rows=None, start_pos=None):
     """Run w on the GPU and check it as the module docstring says; rows:
     optional flat rows to check (all when None)."""
@@ -98,7 +107,7 @@ def check_moe(w, rows=None, start_pos=None):
     werr = np.max(np.abs(wts[rows] - wts_o[rows]) / (4 * bound[rows, None] + 1e-7))
     tol = tol_of(w)
     log(f"    y {err:.3e} (tol {tol:g}); choices differing from the exact top k: {differ} of {len(rows)}; "
-        f"weights within {werr:.2f} of their bound")
+        f"weights within {werr:.2f} of their bound; {_worst(y[rows], y_o[rows], rows, sel)}")
     assert err <= tol, err
     assert werr <= 1.0, werr
     # every routed expert's output at its own scale (a few % of y's rms at
@@ -116,7 +125,8 @@ def check_moe(w, rows=None, start_pos=None):
                 if int(sel[r][j]) == e:
                     r_o[i, j] = oracle.moe_ffn(cfg, one, n2[r], solo, force_sel=[0])[0]
     rerr = rel_err(r_gpu[rows], r_o)
-    log(f"    routed expert rows {rerr:.3e} (tol {tol:g})")
+    log(f"    routed expert rows {rerr:.3e} (tol {tol:g}); "
+        f"{_worst(r_gpu[rows].reshape(len(rows) * K, w.d), r_o.reshape(len(rows) * K, w.d), [r * K + j for r in rows for j in range(K)], sel.reshape(-1, 1), K)}")
     assert rerr <= tol, rerr
     seqs = sorted({r // w.S for r in rows})
     for b in seqs:
