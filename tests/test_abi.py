@@ -226,3 +226,11 @@ def test_footprint_rejects_what_init_rejects():
     assert L.llama_block_footprint(ctypes.byref(ok), 0, None) == lbmod.LB_ERR_INVALID_ARG
     assert L.llama_block_device_bytes(None) == 0
     assert L.llama_stack_device_bytes(None) == 0
+
+
+def test_stage_numbers_match_header():
+    """The binding's stage names carry the header's lb_stage values."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef enum \{([^}]*)\} lb_stage;", text).group(1)
+    header = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"LB_STAGE_(\w+)\s*=\s*(\d+)", body)}
+    assert header == lbmod.STAGES
